@@ -1,0 +1,181 @@
+/*
+ * hisa.h - C ABI of libhisa: hierarchical (block-then-token) sparse
+ * retrieval and sparse attention on AMD Instinct MI355X (gfx950).
+ *
+ * The method: keys are cut into fixed blocks of B tokens and each block is
+ * summarised by the mean of its indexer keys; each query scores the block
+ * summaries with the indexer's dot product, keeps m blocks (the first block
+ * and the query's own block always among them), scores every token of the
+ * kept blocks, keeps the best k tokens, and attends over those k tokens
+ * only. Sources: "PKU HISA sparse attention mechanism: 3x long-text
+ * efficiency" (intelliparadigm.com), sections 1.1, 1.2.1, 1.2.2, 1.3; the
+ * QbitAI news article on HISA (m.digipub.cc), parts "block-level coarse
+ * filter", "fine token selection" and "complexity". The two-level decode
+ * follows "Tencent Hunyuan HiLS-Attention" (ai-engineering pages, Ch01.911),
+ * section "hierarchical softmax decomposition".
+ *
+ * Conventions shared by every entry point
+ *  - Every tensor pointer is a device pointer owned by the caller. The
+ *    library never allocates, frees or synchronises; scratch memory comes
+ *    in through a caller-provided workspace whose size a *_workspace_bytes
+ *    query returns.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL means the
+ *    default stream). Device faults surface at the caller's next
+ *    synchronisation.
+ *  - Arguments are validated on the host before anything is launched. A
+ *    non-OK status means nothing was launched and no output was written;
+ *    hisa_last_error() then returns a thread-local description.
+ *  - bf16 tensors have a contiguous last dimension; the other dimensions are
+ *    addressed through hisa_strides_t (in elements). Base pointers must be
+ *    16-byte aligned and the strides multiples of 8 elements.
+ *  - Token and block indices are relative to their own sequence. Index
+ *    outputs are int32, ascending, and padded with -1 when fewer than the
+ *    requested number of candidates exist.
+ *  - Ties between equal scores go to the lowest index; -0.0 equals +0.0.
+ *    Scores must be finite (NaN or infinite inputs give an unspecified but
+ *    memory-safe selection).
+ *  - Supported sizes: indexer dim d in {64, 128}; block size B in
+ *    {64, 128, 256}; m >= 2; m*B <= 16384; 1 <= k <= 16384; attention
+ *    (Dk, Dv) in {(64, 64), (128, 128), (576, 512)}; Hq % Hkv == 0 with
+ *    Hq / Hkv <= 64. Anything else returns HISA_ERR_UNSUPPORTED.
+ */
+#ifndef HISA_H
+#define HISA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HISA_OK = 0,
+  HISA_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  HISA_ERR_SHAPE = 2,       /* inconsistent sizes, strides or alignment       */
+  HISA_ERR_UNSUPPORTED = 3, /* valid but unsupported size                     */
+  HISA_ERR_HIP = 4,         /* the HIP runtime reported a launch error        */
+  HISA_ERR_WORKSPACE = 5    /* workspace missing or smaller than required     */
+} hisa_status_t;
+
+typedef void* hisa_stream_t; /* hipStream_t */
+
+/* Strides in elements. Element (b, t, h, i) of a tensor lives at
+ * base + b*batch + t*token + h*head + i. Unused members are ignored. */
+typedef struct {
+  int64_t batch;
+  int64_t token;
+  int64_t head;
+} hisa_strides_t;
+
+/* Thread-local text describing the last non-OK status (empty if none). */
+const char* hisa_last_error(void);
+
+/* ABI version of this header (incremented on incompatible changes). */
+int hisa_abi_version(void);
+
+/* Step 1: block summaries (HISA explainer 1.2.1: fixed blocks, mean pooling;
+ * HISA news article: one feature vector per block).
+ *   kidx     bf16 [batch][L][d], element (b, j, i) at b*ks.batch + j*ks.token + i.
+ *   proj     optional bf16 [d][d] row-major; when given, every row becomes
+ *            proj @ row (the two-level decode's chunk key, HiLS chapter,
+ *            "learnable chunk-mass proxy", stood in by a fixed projection).
+ *   summary  optional fp32 [batch][n_rows][d], n_rows = ceil(L / B): row c is
+ *            the mean of tokens c*B .. min(L, (c+1)*B) - 1 (projected if proj).
+ *   split    optional bf16 [batch][n_rows][3][d]: three bf16 terms hi, mid, lo
+ *            whose exact sum is the fp32 row SUM (projected if proj), the
+ *            operand of hisa_block_score's bf16 matrix-core product.
+ * At least one of summary and split must be non-NULL. */
+hisa_status_t hisa_block_summary(const void* kidx, hisa_strides_t ks, int batch, int L, int d,
+                                 int B, const void* proj, float* summary, void* split,
+                                 hisa_stream_t stream);
+
+/* Step 2: block scores (HISA explainer 1.2.1 item 2; HISA news article,
+ * block-level coarse filter: the indexer's own dot product against the
+ * block features only).
+ *   qidx         bf16 [batch][nq][d], element (b, i, :) at b*qs.batch + i*qs.token.
+ *   q_pos        int32 [batch][nq]: absolute position t of each query, 0 <= t < n_rows*B.
+ *   split        the split output of hisa_block_summary for the same batch.
+ *   block_scores fp32 [batch][nq][n_rows]: entry c is qidx . summary[c] for
+ *                complete blocks c < t / B, and -inf for c >= t / B. */
+hisa_status_t hisa_block_score(const void* qidx, hisa_strides_t qs, const int32_t* q_pos,
+                               int batch, int nq, const void* split, int n_rows, int d, int B,
+                               float* block_scores, hisa_stream_t stream);
+
+/* Step 3: top-m blocks (HISA explainer 1.2.1 item 3; HISA news article: keep
+ * m blocks, the first and the last always kept). With b = t / B the kept set
+ * is {0, b} plus the best m - 2 of blocks 1 .. b-1 by score (ties to the
+ * lowest id); when those candidates all fit, blocks 0 .. b are kept.
+ *   block_scores fp32 [batch][nq][n_rows] as written by hisa_block_score.
+ *   block_idx    int32 [batch][nq][m], ascending, -1 padded. */
+hisa_status_t hisa_select_blocks(const float* block_scores, const int32_t* q_pos, int batch,
+                                 int nq, int n_rows, int B, int m, int32_t* block_idx,
+                                 hisa_stream_t stream);
+
+/* Step 4: token top-k inside the kept blocks (HISA explainer 1.2.2; HISA news
+ * article, fine token selection). Candidates are the tokens j <= t of the
+ * blocks in block_idx; each scores qidx . kidx[j]; the best min(k, #cand)
+ * are kept (ties to the lowest j).
+ *   token_idx     int32 [batch][nq][k], ascending, -1 padded.
+ *   token_scores  optional fp32 [batch][nq][k], the score of each kept token
+ *                 (NaN in padded slots).
+ *   workspace     device scratch of at least hisa_token_select_workspace_bytes()
+ *                 bytes, 256-byte aligned; contents on entry are ignored. */
+hisa_status_t hisa_token_select(const void* qidx, hisa_strides_t qs, const void* kidx,
+                                hisa_strides_t ks, const int32_t* q_pos, const int32_t* block_idx,
+                                int batch, int nq, int L, int d, int B, int m, int k,
+                                int32_t* token_idx, float* token_scores, void* workspace,
+                                size_t workspace_bytes, hisa_stream_t stream);
+size_t hisa_token_select_workspace_bytes(int batch, int nq, int L, int B, int m, int k);
+
+/* Flat comparison indexer (HISA explainer 1.1 item 1; HISA news article: the
+ * original indexer scores every earlier token). Candidates are all j <= t;
+ * output format as hisa_token_select. */
+hisa_status_t flat_indexer_topk(const void* qidx, hisa_strides_t qs, const void* kidx,
+                                hisa_strides_t ks, const int32_t* q_pos, int batch, int nq, int L,
+                                int d, int k, int32_t* token_idx, float* token_scores,
+                                void* workspace, size_t workspace_bytes, hisa_stream_t stream);
+size_t flat_indexer_topk_workspace_bytes(int batch, int nq, int L, int k);
+
+/* Step 5: softmax attention over the selected tokens only (HISA explainer
+ * 1.1; HISA news article: the downstream sparse attention is unchanged).
+ *   q    bf16 [batch][nq][Hq][Dk]   strides qs (batch, token, head).
+ *   k    bf16 [batch][L][Hkv][Dk]   strides ks.
+ *   v    bf16 [batch][L][Hkv][Dv]   strides vs; may alias k (the first Dv
+ *        columns of a latent row, as in multi-head latent attention).
+ *   token_idx int32 [batch][nq][topk]; entries < 0 are skipped; every entry
+ *        must be < L.
+ *   out  bf16 [batch][nq][Hq][Dv]   strides os.
+ *   lse  optional fp32 [batch][nq][Hq]: natural-log sum of exp(scale*q.k)
+ *        over the kept tokens (-inf for an empty set, whose output is 0).
+ * Query head h reads kv head h / (Hq / Hkv). */
+hisa_status_t sparse_attn_fwd(const void* q, hisa_strides_t qs, const void* k, hisa_strides_t ks,
+                              const void* v, hisa_strides_t vs, int batch, int nq, int L, int Hq,
+                              int Hkv, int Dk, int Dv, const int32_t* token_idx, int topk,
+                              float scale, void* out, hisa_strides_t os, float* lse,
+                              hisa_stream_t stream);
+
+/* Two-level (chunk x token) softmax decode at position t = L - 1 (HiLS
+ * chapter, "hierarchical softmax decomposition"; HiLS-7B write-up, "what is
+ * HiLS-Attention"). For each (sequence, head) the output is
+ *   sum over chosen chunks c of softmax_c(scale_chunk * q . khat_c)
+ *       * sum over tokens j of chunk c, j <= t, of softmax_j(scale_token * q . k_j) v_j.
+ *   q         bf16 [batch][H][D], strides qs (batch, head).
+ *   k, v      bf16 [batch][L][H][D], strides (batch, token, head).
+ *   khat      fp32 [batch*H][n_rows][D]: chunk keys from hisa_block_summary
+ *             run with batch*H sequences (row b*H + h).
+ *   chunk_idx int32 [batch*H][m]: chosen chunks (from hisa_select_blocks),
+ *             ascending, -1 padded.
+ *   out       bf16 [batch][H][D], strides os (batch, head). */
+hisa_status_t hils_two_level_attn_fwd(const void* q, hisa_strides_t qs, const void* k,
+                                      hisa_strides_t ks, const void* v, hisa_strides_t vs,
+                                      const float* khat, const int32_t* chunk_idx, int batch,
+                                      int L, int H, int D, int C, int n_rows, int m,
+                                      float scale_chunk, float scale_token, void* out,
+                                      hisa_strides_t os, hisa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HISA_H */

@@ -1,0 +1,142 @@
+// Device helpers shared by the gfx950 kernels: bf16 packing, matrix-core
+// (MFMA) fragments, wavefront reductions and scans.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hisa {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// ---------------------------------------------------------------- MFMA
+// v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] * B[32x16].
+// Lane l holds A row (l % 16) and B column (l % 16), each with 8 consecutive
+// k values of group (l / 16); D lane l holds column (l % 16), rows
+// 4*(l/16) .. 4*(l/16)+3. Any consistent assignment of data to k slots gives
+// the same contraction, which the kernels use to pick convenient layouts.
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// ---------------------------------------------------------------- waves
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+template <class T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+// Inclusive prefix sum across the 64 lanes.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    uint32_t u = __shfl_up(v, o, kWave);
+    if (l >= o) v += u;
+  }
+  return v;
+}
+
+// Block-wide reductions over NT threads; `red` is LDS scratch of >= NT/64
+// words. Every thread of the block must call them (they synchronise).
+template <int NT>
+__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* red) {
+  v = wave_sum(v);
+  if constexpr (NT == kWave) {
+    return v;
+  } else {
+    const int w = threadIdx.x / kWave;
+    __syncthreads();
+    if (lane_id() == 0) red[w] = v;
+    __syncthreads();
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < NT / kWave; ++i) s += red[i];
+    return s;
+  }
+}
+template <int NT>
+__device__ __forceinline__ void block_minmax(float& mn, float& mx, float* red) {
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  if constexpr (NT != kWave) {
+    const int w = threadIdx.x / kWave;
+    __syncthreads();
+    if (lane_id() == 0) {
+      red[2 * w] = mn;
+      red[2 * w + 1] = mx;
+    }
+    __syncthreads();
+    mn = red[0];
+    mx = red[1];
+#pragma unroll
+    for (int i = 1; i < NT / kWave; ++i) {
+      mn = fminf(mn, red[2 * i]);
+      mx = fmaxf(mx, red[2 * i + 1]);
+    }
+  }
+}
+// Block-wide exclusive scan; returns the exclusive prefix, `total` the sum.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t& total, uint32_t* red) {
+  uint32_t inc = wave_incl_scan(v);
+  if constexpr (NT == kWave) {
+    total = __shfl(inc, kWave - 1, kWave);
+    return inc - v;
+  } else {
+    const int w = threadIdx.x / kWave;
+    __syncthreads();
+    if (lane_id() == kWave - 1) red[w] = inc;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int i = 0; i < NT / kWave; ++i) {
+      const uint32_t r = red[i];
+      before += (i < w) ? r : 0u;
+      all += r;
+    }
+    total = all;
+    return before + inc - v;
+  }
+}
+
+}  // namespace hisa

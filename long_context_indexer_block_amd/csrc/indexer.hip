@@ -1,0 +1,239 @@
+// Block level of the hierarchical indexer: block summaries, block scores
+// and the top-m block choice.
+//
+// Block summaries follow the HISA explainer, section 1.2.1 (fixed-size
+// blocks, mean pooling) and the HISA news article ("block-level coarse
+// filter"); block scores use the indexer's own dot product against the
+// block features (same sources); the block choice keeps the first block and
+// the query's own block and fills the rest with the best-scoring complete
+// blocks before it (HISA explainer 1.2.1 item 3, HISA news article).
+#include "common.hpp"
+#include "internal.h"
+#include "select.hpp"
+
+namespace hisa {
+
+// ------------------------------------------------------------------ summary
+// One workgroup per (block, sequence). Threads read 16-byte column groups of
+// the block's rows (coalesced), sum in fp32, reduce the row-parallel partial
+// sums through LDS, optionally project with proj (fp32, fixed order), and
+// write the mean plus the exact bf16 hi/mid/lo split of the (projected) sum.
+template <int D>
+__global__ __launch_bounds__(256) void block_summary_kernel(
+    const uint16_t* __restrict__ kidx, int64_t ksb, int64_t kst, int L, int B, int n_rows,
+    const uint16_t* __restrict__ proj, float* __restrict__ summary, uint16_t* __restrict__ split) {
+  constexpr int TPR = D / 8;      // threads per row (8 columns each)
+  constexpr int RP = 256 / TPR;   // rows summed in parallel
+  __shared__ float part[RP][D + 1];
+  __shared__ float sums[D];
+  const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int col0 = (tid % TPR) * 8, r0 = tid / TPR;
+  const int j0 = c * B, j1 = min(L, j0 + B);
+  const uint16_t* base = kidx + b * ksb;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  for (int j = j0 + r0; j < j1; j += RP) {
+    const uint4 w = *reinterpret_cast<const uint4*>(base + j * kst + col0);
+    acc[0] += bf16_lo(w.x); acc[1] += bf16_hi(w.x);
+    acc[2] += bf16_lo(w.y); acc[3] += bf16_hi(w.y);
+    acc[4] += bf16_lo(w.z); acc[5] += bf16_hi(w.z);
+    acc[6] += bf16_lo(w.w); acc[7] += bf16_hi(w.w);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[r0][col0 + e] = acc[e];
+  __syncthreads();
+  float s = 0.0f;
+  if (tid < D) {
+    for (int r = 0; r < RP; ++r) s += part[r][tid];
+    sums[tid] = s;
+  }
+  __syncthreads();
+  if (tid < D) {
+    if (proj != nullptr) {
+      const uint16_t* wr = proj + tid * D;
+      float p = 0.0f;
+      for (int i = 0; i < D; i += 8) {
+        const uint4 w = *reinterpret_cast<const uint4*>(wr + i);
+        p = fmaf(bf16_lo(w.x), sums[i + 0], p); p = fmaf(bf16_hi(w.x), sums[i + 1], p);
+        p = fmaf(bf16_lo(w.y), sums[i + 2], p); p = fmaf(bf16_hi(w.y), sums[i + 3], p);
+        p = fmaf(bf16_lo(w.z), sums[i + 4], p); p = fmaf(bf16_hi(w.z), sums[i + 5], p);
+        p = fmaf(bf16_lo(w.w), sums[i + 6], p); p = fmaf(bf16_hi(w.w), sums[i + 7], p);
+      }
+      s = p;
+    }
+    const int64_t row = static_cast<int64_t>(b) * n_rows + c;
+    if (summary != nullptr) summary[row * D + tid] = s / static_cast<float>(j1 - j0);
+    if (split != nullptr) {
+      // hi + mid + lo == s exactly: each remainder is exact (the rounded
+      // term lies within a factor of two of the value it is taken from) and
+      // the last remainder has at most 8 significant bits.
+      const uint16_t hi = f32_to_bf16(s);
+      const float r1 = s - bf16_to_f32(hi);
+      const uint16_t mid = f32_to_bf16(r1);
+      const float r2 = r1 - bf16_to_f32(mid);
+      const uint16_t lo = f32_to_bf16(r2);
+      uint16_t* o = split + row * 3 * D;
+      o[tid] = hi;
+      o[D + tid] = mid;
+      o[2 * D + tid] = lo;
+    }
+  }
+}
+
+hipError_t launch_block_summary(const uint16_t* kidx, Str3 ks, int batch, int L, int d, int B,
+                                const uint16_t* proj, float* summary, uint16_t* split,
+                                hipStream_t s) {
+  const int n_rows = (L + B - 1) / B;
+  dim3 grid(n_rows, batch);
+  if (d == 64)
+    hipLaunchKernelGGL(block_summary_kernel<64>, grid, dim3(256), 0, s, kidx, ks.b, ks.t, L, B,
+                       n_rows, proj, summary, split);
+  else
+    hipLaunchKernelGGL(block_summary_kernel<128>, grid, dim3(256), 0, s, kidx, ks.b, ks.t, L, B,
+                       n_rows, proj, summary, split);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ scores
+// Tile: 64 queries x 64 blocks per workgroup, 16 queries per wave. The
+// contraction q . (hi + mid + lo) runs on the bf16 matrix cores with fp32
+// accumulation (K = 3*D); for integer-valued keys every partial sum is an
+// integer below 2^24, so the score is exact, then scaled by 1/B (exact for
+// a power-of-two B).
+template <int D>
+__global__ __launch_bounds__(256) void block_score_kernel(
+    const uint16_t* __restrict__ qidx, int64_t qsb, int64_t qst, const int32_t* __restrict__ q_pos,
+    int nq, const uint16_t* __restrict__ split, int n_rows, int B, float invB,
+    float* __restrict__ out) {
+  constexpr int KS = D / 32;
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  const int b = blockIdx.z;
+  const int q0 = blockIdx.y * 64 + wave * 16;
+  const int c0 = blockIdx.x * 64;
+  const int g = lane / 16, r16 = lane % 16;
+  if (q0 >= nq) return;
+  // positions of the four output rows this lane stores, and the wave's max
+  int bt_row[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int qq = q0 + 4 * g + r;
+    bt_row[r] = qq < nq ? min(max(q_pos[static_cast<int64_t>(b) * nq + qq], 0), n_rows * B - 1) / B
+                        : -1;
+  }
+  int btmax = max(max(bt_row[0], bt_row[1]), max(bt_row[2], bt_row[3]));
+  btmax = static_cast<int>(wave_max(static_cast<float>(btmax)));
+  // A fragments: the query row of this lane, 8 values per k step.
+  const int qa = min(q0 + r16, nq - 1);
+  const uint16_t* qrow = qidx + b * qsb + static_cast<int64_t>(qa) * qst + 8 * g;
+  bf16x8 a[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) a[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 32 * s));
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int cb = c0 + nt * 16;
+    if (cb >= n_rows) break;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (cb < btmax) {
+      const int cc = min(cb + r16, n_rows - 1);
+      const uint16_t* srow = split + (static_cast<int64_t>(b) * n_rows + cc) * 3 * D + 8 * g;
+#pragma unroll
+      for (int term = 0; term < 3; ++term)
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          acc = mfma16(a[s], as_bf16x8(*reinterpret_cast<const uint4*>(srow + term * D + 32 * s)),
+                       acc);
+    }
+    const int c = cb + r16;
+    if (c < n_rows) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int qq = q0 + 4 * g + r;
+        if (qq < nq)
+          out[(static_cast<int64_t>(b) * nq + qq) * n_rows + c] =
+              c < bt_row[r] ? acc[r] * invB : -INFINITY;
+      }
+    }
+  }
+}
+
+hipError_t launch_block_score(const uint16_t* qidx, Str3 qs, const int32_t* q_pos, int batch,
+                              int nq, const uint16_t* split, int n_rows, int d, int B,
+                              float* scores, hipStream_t s) {
+  dim3 grid((n_rows + 63) / 64, (nq + 63) / 64, batch);
+  const float invB = 1.0f / static_cast<float>(B);
+  if (d == 64)
+    hipLaunchKernelGGL(block_score_kernel<64>, grid, dim3(256), 0, s, qidx, qs.b, qs.t, q_pos, nq,
+                       split, n_rows, B, invB, scores);
+  else
+    hipLaunchKernelGGL(block_score_kernel<128>, grid, dim3(256), 0, s, qidx, qs.b, qs.t, q_pos,
+                       nq, split, n_rows, B, invB, scores);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ top-m
+// One workgroup per query. Candidates are blocks 1 .. b-1 (position p is
+// block p+1); the first block and the local block b are added around the
+// free picks, which keeps the output ascending.
+template <int NT, int ITEMS, bool CACHED>
+__global__ __launch_bounds__(NT) void select_blocks_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ q_pos, int nq, int n_rows,
+    int B, int m, int32_t* __restrict__ block_idx) {
+  constexpr int NB = NT >= 256 ? 2048 : 256;
+  __shared__ SelectLds<NT, NB> sh;
+  const int64_t qi = static_cast<int64_t>(blockIdx.y) * nq + blockIdx.x;
+  const float* row = scores + qi * n_rows;
+  int32_t* out = block_idx + qi * m;
+  const int t = min(max(q_pos[qi], 0), n_rows * B - 1);
+  const int bt = t / B;
+  const int n = max(bt - 1, 0);
+  const int free_slots = m - (bt == 0 ? 1 : 2);
+  if (n <= free_slots) {
+    for (int i = threadIdx.x; i < m; i += NT) out[i] = i <= bt ? i : -1;
+    return;
+  }
+  constexpr int CH = NT * ITEMS;
+  const int nchunks = (n + CH - 1) / CH;
+  float vals[CACHED ? ITEMS : 1];
+  if constexpr (CACHED) {
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      const int p = threadIdx.x * ITEMS + i;
+      vals[i] = p < n ? row[1 + p] : 0.0f;
+    }
+  }
+  auto get = [&](int c, int i, float& v) -> bool {
+    const int p = c * CH + threadIdx.x * ITEMS + i;
+    if (p >= n) return false;
+    if constexpr (CACHED) v = vals[i]; else v = row[1 + p];
+    return true;
+  };
+  const Threshold th = select_threshold<NT, ITEMS, NB>(get, nchunks, free_slots, sh);
+  uint32_t kept = 0, ties = 0;
+  for (int c = 0; c < nchunks; ++c) {
+    select_compact<NT, ITEMS, NB>(get, c, th, kept, ties, sh, [&](uint32_t pos, int i, float) {
+      out[1 + pos] = c * CH + threadIdx.x * ITEMS + i + 1;
+    });
+  }
+  if (threadIdx.x == 0) {
+    out[0] = 0;
+    out[1 + free_slots] = bt;
+  }
+}
+
+hipError_t launch_select_blocks(const float* scores, const int32_t* q_pos, int batch, int nq,
+                                int n_rows, int B, int m, int32_t* block_idx, hipStream_t s) {
+  dim3 grid(nq, batch);
+  if (n_rows <= 64 * 16)
+    hipLaunchKernelGGL((select_blocks_kernel<64, 16, true>), grid, dim3(64), 0, s, scores, q_pos,
+                       nq, n_rows, B, m, block_idx);
+  else if (n_rows <= 1024 * 16)
+    hipLaunchKernelGGL((select_blocks_kernel<1024, 16, true>), grid, dim3(1024), 0, s, scores,
+                       q_pos, nq, n_rows, B, m, block_idx);
+  else
+    hipLaunchKernelGGL((select_blocks_kernel<1024, 16, false>), grid, dim3(1024), 0, s, scores,
+                       q_pos, nq, n_rows, B, m, block_idx);
+  return hipGetLastError();
+}
+
+}  // namespace hisa

@@ -1,0 +1,50 @@
+// Launchers shared between the C ABI layer and the kernel files. Every
+// launcher assumes its arguments were validated by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hisa {
+
+struct Str3 {
+  int64_t b, t, h;
+};
+
+// indexer.hip
+hipError_t launch_block_summary(const uint16_t* kidx, Str3 ks, int batch, int L, int d, int B,
+                                const uint16_t* proj, float* summary, uint16_t* split,
+                                hipStream_t s);
+hipError_t launch_block_score(const uint16_t* qidx, Str3 qs, const int32_t* q_pos, int batch,
+                              int nq, const uint16_t* split, int n_rows, int d, int B,
+                              float* scores, hipStream_t s);
+hipError_t launch_select_blocks(const float* scores, const int32_t* q_pos, int batch, int nq,
+                                int n_rows, int B, int m, int32_t* block_idx, hipStream_t s);
+
+// tokens.hip
+size_t token_select_workspace(int batch, int nq, int L, int B, int m, int k);
+hipError_t launch_token_select(const uint16_t* qidx, Str3 qs, const uint16_t* kidx, Str3 ks,
+                              const int32_t* q_pos, const int32_t* block_idx, int batch, int nq,
+                              int L, int d, int B, int m, int k, int32_t* token_idx,
+                              float* token_scores, void* ws, hipStream_t s);
+size_t flat_workspace(int batch, int nq, int L, int k);
+hipError_t launch_flat_topk(const uint16_t* qidx, Str3 qs, const uint16_t* kidx, Str3 ks,
+                            const int32_t* q_pos, int batch, int nq, int L, int d, int k,
+                            int32_t* token_idx, float* token_scores, void* ws, hipStream_t s);
+
+// attention.hip
+hipError_t launch_sparse_attn(const uint16_t* q, Str3 qs, const uint16_t* k, Str3 ks,
+                              const uint16_t* v, Str3 vs, int batch, int nq, int L, int Hq,
+                              int Hkv, int Dk, int Dv, const int32_t* token_idx, int topk,
+                              float scale, uint16_t* out, Str3 os, float* lse, hipStream_t s);
+
+// hils.hip
+hipError_t launch_hils(const uint16_t* q, Str3 qs, const uint16_t* k, Str3 ks, const uint16_t* v,
+                       Str3 vs, const float* khat, const int32_t* chunk_idx, int batch, int L,
+                       int H, int D, int C, int n_rows, int m, float scale_chunk,
+                       float scale_token, uint16_t* out, Str3 os, hipStream_t s);
+
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace hisa

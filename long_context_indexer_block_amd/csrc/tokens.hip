@@ -1,0 +1,398 @@
+// Token level: score every token of the kept blocks and keep the top k
+// (HISA explainer 1.2.2; HISA news article, "fine token selection"), plus
+// the flat comparison indexer that scores every causal token (HISA
+// explainer 1.1 item 1).
+//
+// Hierarchical path, block-major: each query keeps m different blocks, so a
+// query-major product degenerates to a gather-bound matrix-vector product.
+// Instead the (query, slot) pairs are bucketed by key block (counting sort),
+// and each workgroup multiplies one key block (B tokens x d) by up to 64
+// gathered query rows on the bf16 matrix cores (fp32 accumulation, exact for
+// integer-valued indexer data). Scores land in a per-query candidate buffer
+// [query][slot][B] whose position order is ascending token id, and one
+// workgroup per query then selects the top k from it.
+#include "common.hpp"
+#include "internal.h"
+#include "select.hpp"
+
+namespace hisa {
+
+constexpr int kTQ = 64;  // pairs per scoring tile
+
+struct TokWs {
+  uint32_t* cnt;        // [nkeys]
+  uint32_t* cursor;     // [nkeys]
+  uint32_t* offs;       // [nkeys]
+  uint32_t* tile_off;   // [nkeys]
+  uint32_t* total;      // [4]
+  uint32_t* pairs;      // [npairs]
+  uint32_t* tiles;      // [max_tiles]
+  float* scores;        // [batch*nq*m*B]
+};
+
+static TokWs carve(void* ws, int batch, int nq, int L, int B, int m, size_t* bytes) {
+  const size_t nblk = (L + B - 1) / B;
+  const size_t nkeys = static_cast<size_t>(batch) * nblk;
+  const size_t npairs = static_cast<size_t>(batch) * nq * m;
+  const size_t max_tiles = (npairs + kTQ - 1) / kTQ + nkeys;
+  char* p = static_cast<char*>(ws);
+  size_t off = 0;
+  TokWs w;
+  auto take = [&](size_t n) { char* r = p ? p + off : nullptr; off += align256(n); return r; };
+  w.cnt = reinterpret_cast<uint32_t*>(take(nkeys * 4));
+  w.cursor = reinterpret_cast<uint32_t*>(take(nkeys * 4));
+  w.offs = reinterpret_cast<uint32_t*>(take(nkeys * 4));
+  w.tile_off = reinterpret_cast<uint32_t*>(take(nkeys * 4));
+  w.total = reinterpret_cast<uint32_t*>(take(16));
+  w.pairs = reinterpret_cast<uint32_t*>(take(npairs * 4));
+  w.tiles = reinterpret_cast<uint32_t*>(take(max_tiles * 4));
+  w.scores = reinterpret_cast<float*>(take(npairs * B * 4));
+  if (bytes) *bytes = off;
+  return w;
+}
+
+size_t token_select_workspace(int batch, int nq, int L, int B, int m, int /*k*/) {
+  size_t bytes = 0;
+  carve(nullptr, batch, nq, L, B, m, &bytes);
+  return bytes;
+}
+
+// ------------------------------------------------------------ pair buckets
+__global__ void zero_u32_kernel(uint32_t* __restrict__ p, size_t n) {
+  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    p[i] = 0u;
+}
+
+__global__ void count_pairs_kernel(const int32_t* __restrict__ block_idx, int nq, int m, int nblk,
+                                   size_t npairs, uint32_t* __restrict__ cnt) {
+  const size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x;
+  if (i >= npairs) return;
+  const int c = block_idx[i];
+  if (c < 0 || c >= nblk) return;
+  const size_t b = i / (static_cast<size_t>(nq) * m);
+  atomicAdd(&cnt[b * nblk + c], 1u);
+}
+
+// One workgroup of 1024 threads scans the bucket counts (pair offsets and
+// tile offsets) in key order.
+__global__ __launch_bounds__(1024) void scan_buckets_kernel(const uint32_t* __restrict__ cnt,
+                                                            int nkeys, uint32_t* __restrict__ offs,
+                                                            uint32_t* __restrict__ tile_off,
+                                                            uint32_t* __restrict__ total) {
+  __shared__ uint32_t red[32];
+  const int per = (nkeys + 1023) / 1024;
+  const int k0 = threadIdx.x * per, k1 = min(nkeys, k0 + per);
+  uint32_t sp = 0, st = 0;
+  for (int k = k0; k < k1; ++k) {
+    sp += cnt[k];
+    st += (cnt[k] + kTQ - 1) / kTQ;
+  }
+  uint32_t tp, tt;
+  uint32_t ep = block_excl_scan<1024>(sp, tp, red);
+  uint32_t et = block_excl_scan<1024>(st, tt, red);
+  for (int k = k0; k < k1; ++k) {
+    offs[k] = ep;
+    tile_off[k] = et;
+    ep += cnt[k];
+    et += (cnt[k] + kTQ - 1) / kTQ;
+  }
+  if (threadIdx.x == 0) {
+    total[0] = tp;
+    total[1] = tt;
+  }
+}
+
+__global__ void scatter_pairs_kernel(const int32_t* __restrict__ block_idx, int nq, int m,
+                                     int nblk, size_t npairs, const uint32_t* __restrict__ offs,
+                                     uint32_t* __restrict__ cursor, uint32_t* __restrict__ pairs) {
+  const size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x;
+  if (i >= npairs) return;
+  const int c = block_idx[i];
+  if (c < 0 || c >= nblk) return;
+  const size_t key = (i / (static_cast<size_t>(nq) * m)) * nblk + c;
+  const uint32_t pos = offs[key] + atomicAdd(&cursor[key], 1u);
+  pairs[pos] = static_cast<uint32_t>(i);
+}
+
+__global__ void tile_table_kernel(const uint32_t* __restrict__ cnt,
+                                  const uint32_t* __restrict__ tile_off, int nkeys,
+                                  uint32_t* __restrict__ tiles) {
+  const int key = blockIdx.x * blockDim.x + threadIdx.x;
+  if (key >= nkeys) return;
+  const uint32_t nt = (cnt[key] + kTQ - 1) / kTQ;
+  for (uint32_t t = 0; t < nt; ++t) tiles[tile_off[key] + t] = static_cast<uint32_t>(key);
+}
+
+// ------------------------------------------------------------ scoring
+// S^T[token, pair] = K_blk[token, :] . Q[pair, :]. Wave w owns tokens
+// [w*BS/4, (w+1)*BS/4) of the key block (A operand, straight from global),
+// all 64 pairs of the tile are the B operand (gathered query rows). The
+// accumulator lane layout (column = pair, 4 consecutive tokens) is stored
+// as one 16-byte write per pair.
+template <int D, int BS>
+__global__ __launch_bounds__(256) void token_score_kernel(
+    const uint16_t* __restrict__ qidx, int64_t qsb, int64_t qst, const uint16_t* __restrict__ kidx,
+    int64_t ksb, int64_t kst, int L, int nq, int m, int nblk, const uint32_t* __restrict__ tiles,
+    const uint32_t* __restrict__ total, const uint32_t* __restrict__ tile_off,
+    const uint32_t* __restrict__ offs, const uint32_t* __restrict__ cnt,
+    const uint32_t* __restrict__ pairs, float* __restrict__ scores) {
+  constexpr int KS = D / 32;
+  constexpr int MT = BS / 64;  // 16-token tiles per wave
+  const uint32_t tile = blockIdx.x;
+  if (tile >= total[1]) return;
+  const uint32_t key = tiles[tile];
+  const uint32_t sub = tile - tile_off[key];
+  const uint32_t p0 = offs[key] + sub * kTQ;
+  const uint32_t np = min(static_cast<uint32_t>(kTQ), cnt[key] - sub * kTQ);
+  const int b = key / nblk, c = key % nblk;
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  const int g = lane / 16, r16 = lane % 16;
+
+  bf16x8 a[MT][KS];
+  const int tok0 = c * BS + wave * (BS / 4);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int j = min(tok0 + mt * 16 + r16, L - 1);
+    const uint16_t* kr = kidx + b * ksb + static_cast<int64_t>(j) * kst + 8 * g;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) a[mt][s] = as_bf16x8(*reinterpret_cast<const uint4*>(kr + 32 * s));
+  }
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    if (nt * 16 >= static_cast<int>(np)) break;
+    const uint32_t pl = min(static_cast<uint32_t>(nt * 16 + r16), np - 1);
+    const uint32_t pid = pairs[p0 + pl];
+    const uint32_t qrow = pid / m;  // b*nq + q
+    const int qq = qrow % nq;
+    const uint16_t* qr = qidx + b * qsb + static_cast<int64_t>(qq) * qst + 8 * g;
+    bf16x8 bq[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) bq[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + 32 * s));
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) acc = mfma16(a[mt][s], bq[s], acc);
+      if (nt * 16 + r16 < static_cast<int>(np)) {
+        const int tk = wave * (BS / 4) + mt * 16 + 4 * g;
+        *reinterpret_cast<f32x4*>(scores + static_cast<int64_t>(pid) * BS + tk) = acc;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ selection
+// One workgroup (256 threads) per query; thread t owns candidate positions
+// t*ITEMS .. t*ITEMS+ITEMS-1 of the query's [m][B] buffer (slot-major, so
+// position order is ascending token id). Tokens after the query and empty
+// slots are not candidates.
+template <int ITEMS>
+__global__ __launch_bounds__(256) void token_topk_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ block_idx,
+    const int32_t* __restrict__ q_pos, int m, int B, int k, int L, int32_t* __restrict__ token_idx,
+    float* __restrict__ token_scores) {
+  constexpr int NT = 256, NB = 2048;
+  __shared__ SelectLds<NT, NB> sh;
+  __shared__ int blk[1024];
+  const int64_t qi = blockIdx.x;
+  const int t = min(max(q_pos[qi], 0), L - 1);
+  const int nblk = (L + B - 1) / B;
+  for (int i = threadIdx.x; i < m; i += NT) {
+    const int c = block_idx[qi * m + i];
+    blk[i] = c < nblk ? c : -1;
+  }
+  __syncthreads();
+  const float* row = scores + qi * m * B;
+  const int n_all = m * B;
+  float vals[ITEMS];
+  bool ok[ITEMS];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int p = threadIdx.x * ITEMS + i;
+    ok[i] = false;
+    vals[i] = 0.0f;
+    if (p < n_all) {
+      const int c = blk[p / B];
+      const int j = c * B + p % B;
+      if (c >= 0 && j <= t) {
+        ok[i] = true;
+        vals[i] = row[p];
+      }
+    }
+  }
+  auto get = [&](int, int i, float& v) -> bool {
+    v = vals[i];
+    return ok[i];
+  };
+  const Threshold th = select_threshold<NT, ITEMS, NB>(get, 1, k, sh);
+  uint32_t kept = 0, ties = 0;
+  int32_t* oi = token_idx + qi * k;
+  float* os = token_scores ? token_scores + qi * k : nullptr;
+  select_compact<NT, ITEMS, NB>(get, 0, th, kept, ties, sh, [&](uint32_t pos, int i, float v) {
+    const int p = threadIdx.x * ITEMS + i;
+    oi[pos] = blk[p / B] * B + p % B;
+    if (os) os[pos] = v;
+  });
+  for (int i = kept + threadIdx.x; i < k; i += NT) {
+    oi[i] = -1;
+    if (os) os[i] = __uint_as_float(0x7fc00000u);
+  }
+}
+
+hipError_t launch_token_select(const uint16_t* qidx, Str3 qs, const uint16_t* kidx, Str3 ks,
+                              const int32_t* q_pos, const int32_t* block_idx, int batch, int nq,
+                              int L, int d, int B, int m, int k, int32_t* token_idx,
+                              float* token_scores, void* ws, hipStream_t s) {
+  const int nblk = (L + B - 1) / B;
+  const int nkeys = batch * nblk;
+  const size_t npairs = static_cast<size_t>(batch) * nq * m;
+  const size_t max_tiles = (npairs + kTQ - 1) / kTQ + nkeys;
+  TokWs w = carve(ws, batch, nq, L, B, m, nullptr);
+  // cnt and cursor are adjacent: clear both with one fill kernel
+  const size_t zero_n = (reinterpret_cast<char*>(w.offs) - reinterpret_cast<char*>(w.cnt)) / 4;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(std::min<size_t>((zero_n + 255) / 256, 4096)),
+                     dim3(256), 0, s, w.cnt, zero_n);
+  const unsigned pg = static_cast<unsigned>((npairs + 255) / 256);
+  hipLaunchKernelGGL(count_pairs_kernel, dim3(pg), dim3(256), 0, s, block_idx, nq, m, nblk,
+                     npairs, w.cnt);
+  hipLaunchKernelGGL(scan_buckets_kernel, dim3(1), dim3(1024), 0, s, w.cnt, nkeys, w.offs,
+                     w.tile_off, w.total);
+  hipLaunchKernelGGL(scatter_pairs_kernel, dim3(pg), dim3(256), 0, s, block_idx, nq, m, nblk,
+                     npairs, w.offs, w.cursor, w.pairs);
+  hipLaunchKernelGGL(tile_table_kernel, dim3((nkeys + 255) / 256), dim3(256), 0, s, w.cnt,
+                     w.tile_off, nkeys, w.tiles);
+#define HISA_TS(D_, B_)                                                                       \
+  hipLaunchKernelGGL((token_score_kernel<D_, B_>), dim3(static_cast<unsigned>(max_tiles)),   \
+                     dim3(256), 0, s, qidx, qs.b, qs.t, kidx, ks.b, ks.t, L, nq, m, nblk,     \
+                     w.tiles, w.total, w.tile_off, w.offs, w.cnt, w.pairs, w.scores)
+  if (d == 64) {
+    if (B == 64) HISA_TS(64, 64); else if (B == 128) HISA_TS(64, 128); else HISA_TS(64, 256);
+  } else {
+    if (B == 64) HISA_TS(128, 64); else if (B == 128) HISA_TS(128, 128); else HISA_TS(128, 256);
+  }
+#undef HISA_TS
+  const int items = (m * B + 255) / 256;
+  dim3 g(static_cast<unsigned>(static_cast<size_t>(batch) * nq));
+#define HISA_TK(I_)                                                                          \
+  hipLaunchKernelGGL((token_topk_kernel<I_>), g, dim3(256), 0, s, w.scores, block_idx, q_pos, m, \
+                     B, k, L, token_idx, token_scores)
+  if (items <= 2) HISA_TK(2);
+  else if (items <= 4) HISA_TK(4);
+  else if (items <= 8) HISA_TK(8);
+  else if (items <= 16) HISA_TK(16);
+  else if (items <= 32) HISA_TK(32);
+  else HISA_TK(64);
+#undef HISA_TK
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ flat path
+// Dense causal scoring: workgroup tile = 128 keys x 64 queries, wave w owns
+// 32 keys. Rows of the score buffer have stride ldw = round_up(L, 4); only
+// keys j <= t are read back by the selection.
+template <int D>
+__global__ __launch_bounds__(256) void flat_score_kernel(
+    const uint16_t* __restrict__ qidx, int64_t qsb, int64_t qst, const uint16_t* __restrict__ kidx,
+    int64_t ksb, int64_t kst, const int32_t* __restrict__ q_pos, int L, int nq, int64_t ldw,
+    float* __restrict__ scores) {
+  constexpr int KS = D / 32;
+  const int b = blockIdx.z;
+  const int j0 = blockIdx.x * 128, q0 = blockIdx.y * 64;
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  const int g = lane / 16, r16 = lane % 16;
+  // skip tiles entirely above every query of the tile
+  int tmax = -1;
+  for (int i = lane; i < 64; i += kWave) {
+    const int qq = q0 + i;
+    if (qq < nq) tmax = max(tmax, q_pos[static_cast<int64_t>(b) * nq + qq]);
+  }
+  tmax = static_cast<int>(wave_max(static_cast<float>(tmax)));
+  if (j0 > tmax) return;
+  bf16x8 a[2][KS];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int j = min(j0 + wave * 32 + mt * 16 + r16, L - 1);
+    const uint16_t* kr = kidx + b * ksb + static_cast<int64_t>(j) * kst + 8 * g;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) a[mt][s] = as_bf16x8(*reinterpret_cast<const uint4*>(kr + 32 * s));
+  }
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int qq = q0 + nt * 16 + r16;
+    const uint16_t* qr = qidx + b * qsb + static_cast<int64_t>(min(qq, nq - 1)) * qst + 8 * g;
+    bf16x8 bq[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) bq[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + 32 * s));
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) acc = mfma16(a[mt][s], bq[s], acc);
+      const int j = j0 + wave * 32 + mt * 16 + 4 * g;
+      if (qq < nq && j < L) {
+        float* dst = scores + (static_cast<int64_t>(b) * nq + qq) * ldw + j;
+        *reinterpret_cast<f32x4*>(dst) = acc;  // ldw % 4 == 0, j % 4 == 0
+      }
+    }
+  }
+}
+
+// One workgroup (1024 threads) per query streams its row in chunks of
+// 16384 candidates (thread t owns 16 consecutive positions per chunk).
+__global__ __launch_bounds__(1024) void flat_topk_kernel(const float* __restrict__ scores,
+                                                         const int32_t* __restrict__ q_pos,
+                                                         int64_t ldw, int L, int k,
+                                                         int32_t* __restrict__ token_idx,
+                                                         float* __restrict__ token_scores) {
+  constexpr int NT = 1024, ITEMS = 16, NB = 2048, CH = NT * ITEMS;
+  __shared__ SelectLds<NT, NB> sh;
+  const int64_t qi = blockIdx.x;
+  const int n = min(max(q_pos[qi], 0), L - 1) + 1;
+  const float* row = scores + qi * ldw;
+  const int nchunks = (n + CH - 1) / CH;
+  auto get = [&](int c, int i, float& v) -> bool {
+    const int p = c * CH + threadIdx.x * ITEMS + i;
+    if (p >= n) return false;
+    v = row[p];
+    return true;
+  };
+  const Threshold th = select_threshold<NT, ITEMS, NB>(get, nchunks, k, sh);
+  uint32_t kept = 0, ties = 0;
+  int32_t* oi = token_idx + qi * k;
+  float* os = token_scores ? token_scores + qi * k : nullptr;
+  for (int c = 0; c < nchunks; ++c) {
+    select_compact<NT, ITEMS, NB>(get, c, th, kept, ties, sh, [&](uint32_t pos, int i, float v) {
+      oi[pos] = c * CH + threadIdx.x * ITEMS + i;
+      if (os) os[pos] = v;
+    });
+  }
+  for (int i = kept + threadIdx.x; i < k; i += NT) {
+    oi[i] = -1;
+    if (os) os[i] = __uint_as_float(0x7fc00000u);
+  }
+}
+
+size_t flat_workspace(int batch, int nq, int L, int /*k*/) {
+  const size_t ldw = (static_cast<size_t>(L) + 3) & ~static_cast<size_t>(3);
+  return align256(static_cast<size_t>(batch) * nq * ldw * 4);
+}
+
+hipError_t launch_flat_topk(const uint16_t* qidx, Str3 qs, const uint16_t* kidx, Str3 ks,
+                            const int32_t* q_pos, int batch, int nq, int L, int d, int k,
+                            int32_t* token_idx, float* token_scores, void* ws, hipStream_t s) {
+  const int64_t ldw = (static_cast<int64_t>(L) + 3) & ~static_cast<int64_t>(3);
+  float* sc = static_cast<float*>(ws);
+  dim3 grid((L + 127) / 128, (nq + 63) / 64, batch);
+  if (d == 64)
+    hipLaunchKernelGGL(flat_score_kernel<64>, grid, dim3(256), 0, s, qidx, qs.b, qs.t, kidx, ks.b,
+                       ks.t, q_pos, L, nq, ldw, sc);
+  else
+    hipLaunchKernelGGL(flat_score_kernel<128>, grid, dim3(256), 0, s, qidx, qs.b, qs.t, kidx,
+                       ks.b, ks.t, q_pos, L, nq, ldw, sc);
+  hipLaunchKernelGGL(flat_topk_kernel, dim3(static_cast<unsigned>(static_cast<size_t>(batch) * nq)),
+                     dim3(1024), 0, s, sc, q_pos, ldw, L, k, token_idx, token_scores);
+  return hipGetLastError();
+}
+
+}  // namespace hisa

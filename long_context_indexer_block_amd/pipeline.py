@@ -1,0 +1,135 @@
+"""Whole paths over preallocated device buffers (every step is a libhisa call).
+
+HierPipeline: block summary -> block score -> top-m blocks -> token top-k
+              -> sparse attention (HISA explainer 1.2-1.3; HISA news article).
+FlatPipeline: flat indexer top-k -> sparse attention (the comparison path).
+HilsDecode:   chunk keys (once per cache) -> chunk scores -> top-m chunks
+              -> two-level softmax attention (HiLS chapter).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (flat_indexer_topk, flat_indexer_topk_workspace_bytes, hils_two_level_attn_fwd,
+               hisa_block_score, hisa_block_summary, hisa_select_blocks, hisa_token_select,
+               hisa_token_select_workspace_bytes, sparse_attn_fwd)
+
+
+class HierPipeline:
+    def __init__(self, kidx, qidx, q_pos, q, k, v, B, m, k_top, scale, want_scores=False,
+                 want_lse=False):
+        self.kidx, self.qidx, self.q_pos, self.q, self.k, self.v = kidx, qidx, q_pos, q, k, v
+        self.B, self.m, self.k_top, self.scale = B, m, k_top, scale
+        b, L, d = kidx.shape
+        nq = qidx.shape[1]
+        dev = kidx.device
+        n = -(-L // B)
+        self.summary = torch.empty(b, n, d, dtype=torch.float32, device=dev)
+        self.split = torch.empty(b, n, 3, d, dtype=torch.bfloat16, device=dev)
+        self.block_scores = torch.empty(b, nq, n, dtype=torch.float32, device=dev)
+        self.block_idx = torch.empty(b, nq, m, dtype=torch.int32, device=dev)
+        self.token_idx = torch.empty(b, nq, k_top, dtype=torch.int32, device=dev)
+        self.token_scores = (torch.empty(b, nq, k_top, dtype=torch.float32, device=dev)
+                             if want_scores else None)
+        nbytes = hisa_token_select_workspace_bytes(b, nq, L, B, m, k_top)
+        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        Hq, Dv = q.shape[2], v.shape[-1]
+        self.out = torch.empty(b, nq, Hq, Dv, dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty(b, nq, Hq, dtype=torch.float32, device=dev) if want_lse else None
+
+    def summarize(self):
+        hisa_block_summary(self.kidx, self.B, summary=self.summary, split=self.split)
+
+    def index(self, summarize=True):
+        if summarize:
+            self.summarize()
+        hisa_block_score(self.qidx, self.q_pos, self.split, self.B, out=self.block_scores)
+        hisa_select_blocks(self.block_scores, self.q_pos, self.B, self.m, out=self.block_idx)
+        hisa_token_select(self.qidx, self.kidx, self.q_pos, self.block_idx, self.B, self.k_top,
+                          token_idx=self.token_idx, token_scores=self.token_scores,
+                          want_scores=self.token_scores is not None, workspace=self.ws)
+
+    def attend(self):
+        sparse_attn_fwd(self.q, self.k, self.v, self.token_idx, self.scale, out=self.out,
+                        lse=self.lse, want_lse=self.lse is not None)
+
+    def run(self, summarize=True):
+        self.index(summarize)
+        self.attend()
+        return self.out
+
+
+class FlatPipeline:
+    def __init__(self, kidx, qidx, q_pos, q, k, v, k_top, scale, want_scores=False,
+                 want_lse=False):
+        self.kidx, self.qidx, self.q_pos, self.q, self.k, self.v = kidx, qidx, q_pos, q, k, v
+        self.k_top, self.scale = k_top, scale
+        b, L, d = kidx.shape
+        nq = qidx.shape[1]
+        dev = kidx.device
+        self.token_idx = torch.empty(b, nq, k_top, dtype=torch.int32, device=dev)
+        self.token_scores = (torch.empty(b, nq, k_top, dtype=torch.float32, device=dev)
+                             if want_scores else None)
+        nbytes = flat_indexer_topk_workspace_bytes(b, nq, L, k_top)
+        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        Hq, Dv = q.shape[2], v.shape[-1]
+        self.out = torch.empty(b, nq, Hq, Dv, dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty(b, nq, Hq, dtype=torch.float32, device=dev) if want_lse else None
+
+    def index(self):
+        flat_indexer_topk(self.qidx, self.kidx, self.q_pos, self.k_top, token_idx=self.token_idx,
+                          token_scores=self.token_scores,
+                          want_scores=self.token_scores is not None, workspace=self.ws)
+
+    def attend(self):
+        sparse_attn_fwd(self.q, self.k, self.v, self.token_idx, self.scale, out=self.out,
+                        lse=self.lse, want_lse=self.lse is not None)
+
+    def run(self):
+        self.index()
+        self.attend()
+        return self.out
+
+
+class HilsDecode:
+    """Two-level decode at position L-1 for every (sequence, head)."""
+
+    def __init__(self, q, k, v, w_proj, C, m, scale_chunk, scale_token):
+        self.q, self.k, self.v, self.w_proj = q, k, v, w_proj
+        self.C, self.m, self.scale_chunk, self.scale_token = C, m, scale_chunk, scale_token
+        b, L, H, D = k.shape
+        dev = k.device
+        n = -(-L // C)
+        self.n = n
+        self.khat = torch.empty(b * H, n, D, dtype=torch.float32, device=dev)
+        self.split = torch.empty(b * H, n, 3, D, dtype=torch.bfloat16, device=dev)
+        self.q_pos = torch.full((b * H, 1), L - 1, dtype=torch.int32, device=dev)
+        self.scores = torch.empty(b * H, 1, n, dtype=torch.float32, device=dev)
+        self.chunk_idx = torch.empty(b * H, 1, m, dtype=torch.int32, device=dev)
+        self.out = torch.empty(b, H, D, dtype=torch.bfloat16, device=dev)
+
+    def build_keys(self):
+        # every (sequence, head) pair is one routed sequence: x[bi] viewed as
+        # [H, L, D] (no copy) gives rows bi*H .. bi*H + H - 1 of the key table
+        b, L, H, D = self.k.shape
+        for bi in range(b):
+            kv = self.k[bi].permute(1, 0, 2)
+            hisa_block_summary(kv, self.C, proj=self.w_proj, summary=self.khat[bi * H:(bi + 1) * H],
+                               split=self.split[bi * H:(bi + 1) * H])
+
+    def route(self):
+        b, H, D = self.q.shape
+        qv = self.q.reshape(b * H, 1, D)
+        hisa_block_score(qv, self.q_pos, self.split, self.C, out=self.scores)
+        hisa_select_blocks(self.scores, self.q_pos, self.C, self.m, out=self.chunk_idx)
+
+    def attend(self):
+        hils_two_level_attn_fwd(self.q, self.k, self.v, self.khat, self.chunk_idx.view(-1, self.m),
+                                self.C, self.scale_chunk, self.scale_token, out=self.out)
+
+    def run(self, build=False):
+        if build:
+            self.build_keys()
+        self.route()
+        self.attend()
+        return self.out

@@ -232,11 +232,11 @@ def hier_query(qidx_t, kidx, summary, t, B, m, k):
 def hier_pipeline(kidx, qidx, q, K, V, positions, rows, B, m, k, scale):
     """Steps 1-5 for the queries at `rows` (rows of qidx/q) with positions
     `positions` (absolute token positions).  Returns a dict of arrays."""
-    kidx = _f64(kidx)
+    kidx, qidx, q, K, V = _f64(kidx), _f64(qidx), _f64(q), _f64(K), _f64(V)
     summary = block_summary(kidx, B)
     out = {"block_idx": [], "token_idx": [], "token_scores": [], "out": [], "lse": []}
     for r, t in zip(rows, positions):
-        bidx, _, tidx, tval = hier_query(_f64(qidx[r]), kidx, summary, int(t), B, m, k)
+        bidx, _, tidx, tval = hier_query(qidx[r], kidx, summary, int(t), B, m, k)
         o, lse = sparse_attention_for_query(q[r], K, V, tidx, scale)
         out["block_idx"].append(bidx)
         out["token_idx"].append(tidx)
@@ -247,10 +247,10 @@ def hier_pipeline(kidx, qidx, q, K, V, positions, rows, B, m, k, scale):
 
 
 def flat_pipeline(kidx, qidx, q, K, V, positions, rows, k, scale):
-    kidx = _f64(kidx)
+    kidx, qidx, q, K, V = _f64(kidx), _f64(qidx), _f64(q), _f64(K), _f64(V)
     out = {"token_idx": [], "token_scores": [], "out": [], "lse": []}
     for r, t in zip(rows, positions):
-        tidx, tval = flat_select_for_query(_f64(qidx[r]), kidx, int(t), k)
+        tidx, tval = flat_select_for_query(qidx[r], kidx, int(t), k)
         o, lse = sparse_attention_for_query(q[r], K, V, tidx, scale)
         out["token_idx"].append(tidx)
         out["token_scores"].append(tval)

@@ -1,0 +1,119 @@
+"""C ABI contract, checked on the CPU: the library loads, exports every symbol
+the header declares, and rejects bad arguments before launching anything
+(only argument errors are exercised here, so no kernel runs)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_indexer_block_amd as H
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hisa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(H.LIB_PATH), reason="libhisa.so not built")
+
+FAKE = ctypes.c_void_p(0x10000)     # aligned, never dereferenced: every call below fails validation
+NULL = ctypes.c_void_p(0)
+S = H.Strides
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:hisa_status_t|size_t|const char\*|int)\s+(\w+)\(",
+                                 txt, flags=re.M)))
+
+
+def test_exports_match_header():
+    names = _declared()
+    assert len(names) == 11
+    lib = ctypes.CDLL(H.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(H.EXPORTS) == names
+    assert H.lib().hisa_abi_version() == 1
+
+
+def _err():
+    return H.lib().hisa_last_error().decode()
+
+
+def test_block_summary_validation():
+    L = H.lib()
+    st = L.hisa_block_summary(NULL, S(0, 64, 0), 1, 128, 64, 64, NULL, FAKE, NULL, NULL)
+    assert st == 1 and "kidx" in _err()
+    st = L.hisa_block_summary(FAKE, S(0, 64, 0), 1, 128, 96, 64, NULL, FAKE, NULL, NULL)
+    assert st == 3 and "d=96" in _err()
+    st = L.hisa_block_summary(FAKE, S(0, 64, 0), 1, 128, 64, 48, NULL, FAKE, NULL, NULL)
+    assert st == 3 and "B=48" in _err()
+    st = L.hisa_block_summary(FAKE, S(0, 60, 0), 1, 128, 64, 64, NULL, FAKE, NULL, NULL)
+    assert st == 2 and "strides" in _err()
+    st = L.hisa_block_summary(ctypes.c_void_p(0x10002), S(0, 64, 0), 1, 128, 64, 64, NULL, FAKE,
+                              NULL, NULL)
+    assert st == 2 and "aligned" in _err()
+    st = L.hisa_block_summary(FAKE, S(0, 64, 0), 1, 128, 64, 64, NULL, NULL, NULL, NULL)
+    assert st == 1
+
+
+def test_select_and_token_validation():
+    L = H.lib()
+    assert L.hisa_select_blocks(FAKE, FAKE, 1, 4, 8, 64, 1, FAKE, NULL) == 3      # m < 2
+    assert "m=1" in _err()
+    # token select: workspace too small, missing, k too large, m*B too large
+    args = [FAKE, S(0, 64, 0), FAKE, S(0, 64, 0), FAKE, FAKE, 1, 16, 1024, 64, 64, 4, 8, FAKE,
+            NULL]
+    need = L.hisa_token_select_workspace_bytes(1, 16, 1024, 64, 4, 8)
+    assert need > 0
+    assert L.hisa_token_select(*args, NULL, need, NULL) == 5
+    assert L.hisa_token_select(*args, FAKE, need - 1, NULL) == 5 and "needs" in _err()
+    bad = list(args)
+    bad[12] = 20000
+    assert L.hisa_token_select(*bad, FAKE, need, NULL) == 3
+    bad = list(args)
+    bad[11] = 512
+    bad[10] = 64
+    assert L.hisa_token_select(*bad, FAKE, 1 << 40, NULL) == 3 and "m*B" in _err()
+
+
+def test_attention_validation():
+    L = H.lib()
+    s = S(0, 128, 128)
+    base = [FAKE, s, FAKE, s, FAKE, s, 1, 4, 64, 6, 4, 128, 128, FAKE, 8, 0.1, FAKE, s, NULL,
+            NULL]
+    assert L.sparse_attn_fwd(*base) == 2 and "multiple" in _err()     # Hq % Hkv
+    b2 = list(base)
+    b2[9], b2[10] = 128, 1
+    assert L.sparse_attn_fwd(*b2) == 3                               # group > 64
+    b3 = list(base)
+    b3[9], b3[10], b3[11], b3[12] = 4, 4, 96, 96
+    assert L.sparse_attn_fwd(*b3) == 3 and "(96, 96)" in _err()
+    b4 = list(base)
+    b4[9], b4[10], b4[15] = 4, 4, -1.0
+    assert L.sparse_attn_fwd(*b4) == 2 and "scale" in _err()
+    b5 = list(base)
+    b5[0] = NULL
+    assert L.sparse_attn_fwd(*b5) == 1
+
+
+def test_hils_validation():
+    L = H.lib()
+    s = S(0, 64, 64)
+    args = [FAKE, s, FAKE, s, FAKE, s, FAKE, FAKE, 1, 4096, 16, 64, 64, 64, 32, 0.125, 0.125,
+            FAKE, s, NULL]
+    a = list(args)
+    a[13] = 63                                                       # n_rows != ceil(L/C)
+    assert L.hils_two_level_attn_fwd(*a) == 2
+    a = list(args)
+    a[14] = 65                                                       # m > 64
+    assert L.hils_two_level_attn_fwd(*a) == 3
+    a = list(args)
+    a[11] = 32                                                       # D unsupported
+    assert L.hils_two_level_attn_fwd(*a) == 3
+
+
+def test_missing_library_raises(monkeypatch):
+    monkeypatch.setattr(H, "_lib", None)
+    monkeypatch.setattr(H, "LIB_PATH", "/nonexistent/libhisa.so")
+    with pytest.raises(H.HisaError):
+        H.lib()
