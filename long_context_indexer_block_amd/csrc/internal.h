@@ -39,6 +39,11 @@ hipError_t launch_sparse_attn(const uint16_t* q, Str3 qs, const uint16_t* k, Str
                               int Hkv, int Dk, int Dv, const int32_t* token_idx, int topk,
                               float scale, uint16_t* out, Str3 os, float* lse, hipStream_t s);
 
+// attention_mla.hip: 64 query heads over one 576-wide latent row (V = first 512 columns)
+hipError_t launch_mla_attn(const uint16_t* q, Str3 qs, const uint16_t* kv, Str3 ks, int batch,
+                           int nq, int L, int Hkv, const int32_t* token_idx, int topk, float scale,
+                           uint16_t* out, Str3 os, float* lse, hipStream_t s);
+
 // hils.hip
 hipError_t launch_hils(const uint16_t* q, Str3 qs, const uint16_t* k, Str3 ks, const uint16_t* v,
                        Str3 vs, const float* khat, const int32_t* chunk_idx, int batch, int L,
