@@ -26,6 +26,9 @@ COMMON_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wno-unused-result",
+    # matrix-core accumulators in VGPRs: the attention kernels keep their
+    # resident operands in AGPRs and the accumulators next to the VALU
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

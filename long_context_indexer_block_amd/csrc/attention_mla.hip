@@ -34,15 +34,15 @@ namespace mla {
 
 constexpr int H = 64, DK = 576, DV = 512, NT = 64;
 constexpr int RCH = DK / 8;     // 16-byte chunks per latent row (72)
-constexpr int PITCH = RCH + 1;  // LDS row pitch in chunks: odd, so 16 rows at one chunk
-                                // (292 words apart, 36 mod 64) hit distinct banks
-constexpr int TSL = NT * PITCH; // chunk slots per tile (4672 = 73 load instructions)
+constexpr int TCH = NT * RCH;   // chunk slots per tile (4608)
 constexpr int KS = DK / 16;     // k steps of S (36)
-constexpr int PP = 9;           // P row pitch in chunks (8 + 1)
+constexpr int PP = 8;           // P row pitch in chunks
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef __attribute__((address_space(1))) void* glb_ptr;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short v4s;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint2 tr16(const unsigned char* lds_byte) {
   const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -52,37 +52,49 @@ __device__ __forceinline__ uint2 tr16(const unsigned char* lds_byte) {
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
 // LDS-only barrier: wait for this wave's LDS operations, then s_barrier.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
 }
 
-__shared__ uint4 g_tile_a[TSL];
-__shared__ uint4 g_tile_b[TSL];
-__shared__ uint4 g_p[H * PP];       // P as [head][8 chunks of 8 tokens] + 1 pad chunk
+__shared__ uint4 g_tile_a[TCH];
+__shared__ uint4 g_tile_b[TCH];
+__shared__ uint4 g_p[H * PP];       // P as [head][8 chunks of 8 tokens], swizzled
 __shared__ float g_mx[2][H];
-__shared__ float g_lsum[2][H];
 
-// Gather the 64 latent rows of one tile into `dst` (row r, chunk c at slot
-// r*PITCH + c). The 73 direct-to-LDS instructions of a tile each fill 64
-// consecutive slots (wave 0 issues 19, the others 18); lane l of
-// instruction i takes slot s = 64i + l, i.e. row s / PITCH, chunk s % PITCH
-// (the pad chunk re-reads chunk 71). Adjacent lanes read adjacent 16-byte
-// chunks of a row, so the loads are coalesced.
+// Tile layout: 8-row x 8-chunk blocks of 1 KB; block (r/8, c/8) is block
+// number (r/8)*9 + c/8 and row r%8 of it holds the row's 8 chunks permuted
+// by XOR with swz(r). Sixteen consecutive rows at one chunk (the S reads) and
+// 4 rows x 2 chunks (the transposed V reads) then fall on distinct banks.
+__device__ __forceinline__ int swz(int r) {
+  const int j = (r >> 1) & 7;
+  return ((j << 1) | (j >> 2)) & 7;
+}
+__device__ __forceinline__ int slot(int r, int c) {
+  return ((r >> 3) * 9 + (c >> 3)) * 64 + (r & 7) * 8 + ((c & 7) ^ swz(r));
+}
+
+// Gather the 64 latent rows of one tile into `dst`: wave w loads rows
+// 16w .. 16w+15 as 18 direct-to-LDS instructions, each filling one 1 KB block
+// (8 rows x 128 bytes; lane l takes row r = 8*rg + l/8 and its logical chunk
+// 8*ln + ((l%8) ^ swz(r)), so 8 adjacent lanes read one 128-byte line).
 __device__ __forceinline__ void dma_tile(uint4* dst, const uint16_t* kvb, int64_t kst, int ids,
                                          int w, int l) {
-  const int i0 = w == 0 ? 0 : 19 + 18 * (w - 1);
-  const int cnt = w == 0 ? 19 : 18;
 #pragma unroll
-  for (int j = 0; j < 19; ++j) {
-    if (j < cnt) {
-      const int s = 64 * (i0 + j) + l;
-      const int r = s / PITCH, c = s - r * PITCH;
-      const int id = __shfl(ids, r, kWave);
-      const uint16_t* src = kvb + static_cast<int64_t>(id < 0 ? 0 : id) * kst + 8 * min(c, RCH - 1);
-      __builtin_amdgcn_global_load_lds((glb_ptr)(src), (lds_ptr)(dst + 64 * (i0 + j)), 16, 0, 0);
-    }
+  for (int k = 0; k < 2; ++k) {
+    const int rg = 2 * w + k;
+    const int r = 8 * rg + (l >> 3);
+    const int id = __shfl(ids, r, kWave);
+    const uint16_t* src = kvb + static_cast<int64_t>(id < 0 ? 0 : id) * kst + 8 * ((l & 7) ^ swz(r));
+#pragma unroll
+    for (int ln = 0; ln < 9; ++ln)
+      __builtin_amdgcn_global_load_lds((glb_ptr)(src + 64 * ln), (lds_ptr)(dst + (rg * 9 + ln) * 64),
+                                       16, 0, 0);
   }
 }
 
@@ -112,56 +124,81 @@ __device__ __forceinline__ void tile_step(const uint4* cur, uint4* nxt, State& s
   // ids of tile+2 are loaded before the tile+1 gather: load counters retire
   // in order, so waiting for the ids later never drains the gather
   const int idx = (tile + 2) * NT + l;
-  int jraw = tix[min(idx, topk - 1)];
+  const int jraw = tix[min(idx, topk - 1)];
   dma_tile(nxt, kvb, kst, ids_next, w, l);
   ids_cur = ids_next;
   ids_next = (idx < topk && jraw >= 0 && jraw < L) ? jraw : -1;
 
-  // ---- S^T[tokens 32tt + (0..31)][heads 32hh + (0..31)] = K Q^T
+  // ---- S^T[tokens 32tt + (0..31)][heads 32hh + (0..31)] = K Q^T; each
+  // fragment read is issued two MFMAs ahead of its use
   f32x16 sacc;
 #pragma unroll
   for (int e = 0; e < 16; ++e) sacc[e] = 0.0f;
   {
-    const uint4* ka = cur + (32 * tt + l32) * PITCH + lh;
+    const int r = 32 * tt + l32;
+    const unsigned char* tb = reinterpret_cast<const unsigned char*>(cur);
+    int base[4];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) sacc = mfma32(as_bf16x8(ka[2 * s]), st.qf[s], sacc);
+    for (int x = 0; x < 4; ++x) base[x] = 16 * slot(r, 2 * x + lh);
+    uint4 kf[KS];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      kf[s] = *reinterpret_cast<const uint4*>(tb + base[s & 3] + 1024 * (s >> 2));
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      if (s + 2 < KS)
+        kf[s + 2] = *reinterpret_cast<const uint4*>(tb + base[(s + 2) & 3] + 1024 * ((s + 2) >> 2));
+      sacc = mfma32(as_bf16x8(kf[s]), st.qf[s], sacc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
+  // ---- softmax over the tile (base 2, scale folded into the exponent)
   float sv[16];
-  float mloc = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int tk = 32 * tt + 8 * (e >> 2) + 4 * lh + (e & 3);
-    sv[e] = ((vmask >> tk) & 1ull) ? sacc[e] * scale_log2 : -INFINITY;
-    mloc = fmaxf(mloc, sv[e]);
+  for (int e = 0; e < 16; ++e) sv[e] = sacc[e];
+  if (vmask != ~0ull) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int tk = 32 * tt + 8 * (e >> 2) + 4 * lh + (e & 3);
+      if (!((vmask >> tk) & 1ull)) sv[e] = -INFINITY;
+    }
   }
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
+  float mloc = sv[0];
+#pragma unroll
+  for (int e = 1; e < 16; ++e) mloc = fmaxf(mloc, sv[e]);
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave)) * scale_log2;
   if (lh == 0) g_mx[tt][head] = mloc;
   lds_barrier();
   // Lazy rescaling: the reference maximum moves only when the tile maximum
   // exceeds it by more than 8 (a factor 256 in p), so most tiles leave O
   // untouched. Every lane holding a head takes the same decision.
   const float mtile = fmaxf(mloc, g_mx[tt ^ 1][head]);
-  const bool move = mtile > st.m_run + 8.0f;
-  const float mref = move ? mtile : st.m_run;
-  const float alpha = move ? exp2f(st.m_run - mtile) : 1.0f;
+  const float mold = st.m_run;
+  const bool move = mtile > mold + 8.0f;
+  const float mref = move ? mtile : mold;
+  const float mneg = mref == -INFINITY ? 0.0f : -mref;
   float psum = 0.0f;
   uint32_t pk[8];
 #pragma unroll
   for (int e = 0; e < 16; e += 2) {
-    const uint16_t a = f32_to_bf16(exp2f(sv[e] - mref));
-    const uint16_t c = f32_to_bf16(exp2f(sv[e + 1] - mref));
-    psum += bf16_to_f32(a) + bf16_to_f32(c);
-    pk[e >> 1] = static_cast<uint32_t>(a) | (static_cast<uint32_t>(c) << 16);
+    const float a = __builtin_amdgcn_exp2f(fmaf(sv[e], scale_log2, mneg));
+    const float c = __builtin_amdgcn_exp2f(fmaf(sv[e + 1], scale_log2, mneg));
+    psum += a + c;
+    pk[e >> 1] = pack2(a, c);
   }
+  // O and l are zero until the first valid tile, so no rescale is needed then
+  const bool rescale = move && mold != -INFINITY;
+  const float alpha = rescale ? __builtin_amdgcn_exp2f(mold - mtile) : 1.0f;
   st.m_run = mref;
   st.l_run = st.l_run * alpha + psum;
   // P[head][token 32tt + 8q + 4lh + (0..3)]: chunk 4tt + q, half lh
   {
-    uint2* prow = reinterpret_cast<uint2*>(g_p + head * PP + 4 * tt) + lh;
+    uint2* prow = reinterpret_cast<uint2*>(g_p + head * PP);
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) prow[2 * qq] = make_uint2(pk[2 * qq], pk[2 * qq + 1]);
+    for (int qq = 0; qq < 4; ++qq)
+      prow[2 * ((4 * tt + qq) ^ (head & 7)) + lh] = make_uint2(pk[2 * qq], pk[2 * qq + 1]);
   }
-  if (__ballot(move) != 0ull) {
+  if (__ballot(rescale) != 0ull) {
 #pragma unroll
     for (int d = 0; d < 8; ++d)
 #pragma unroll
@@ -169,26 +206,38 @@ __device__ __forceinline__ void tile_step(const uint4* cur, uint4* nxt, State& s
   }
   lds_barrier();
 
-  // ---- O^T[dv 256tt + 32dt + (0..31)][heads] += V^T P^T over the tile's 64 tokens
+  // ---- O^T[dv 256tt + 32dt + (0..31)][heads] += V^T P^T over the tile's 64
+  // tokens; V^T fragments (two transposed reads each) run one MFMA ahead
   {
     const int G = l >> 4, sl = l & 15;
     const int trow = 8 * (G >> 1) + (sl >> 2);
     const int dcol = 16 * (G & 1) + 4 * (sl & 3);
-    // token row 16s + trow + 4h, value column 256tt + 32dt + dcol: one base
-    // address per lane, everything else a compile-time offset
-    const unsigned char* vb = reinterpret_cast<const unsigned char*>(cur) +
-                              16 * (trow * PITCH + 32 * tt + (dcol >> 3)) + 2 * (dcol & 7);
-    const uint4* pa = g_p + head * PP + lh;
+    // row 16s + trow + 4h, chunk 32tt + 4dt + dcol/8: the s and dt/2 parts
+    // are whole blocks (constant offsets), the rest one base per (h, dt&1)
+    int vb[2][2];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bf16x8 pb = as_bf16x8(pa[2 * s]);
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const int off = 16 * ((16 * s) * PITCH + 4 * dt);
-        const uint2 lo = tr16(vb + off);
-        const uint2 hi = tr16(vb + off + 16 * 4 * PITCH);
-        st.o[dt] = mfma32(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb, st.o[dt]);
-      }
+      for (int dp = 0; dp < 2; ++dp)
+        vb[h][dp] = 16 * slot(trow + 4 * h, 32 * tt + 4 * dp + (dcol >> 3)) + 2 * (dcol & 7);
+    const unsigned char* tb = reinterpret_cast<const unsigned char*>(cur);
+    auto vfrag = [&](int s, int dt) -> uint4 {
+      const int off = s * 18 * 1024 + 1024 * (dt >> 1);
+      const uint2 lo = tr16(tb + vb[0][dt & 1] + off);
+      const uint2 hi = tr16(tb + vb[1][dt & 1] + off);
+      return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    };
+    bf16x8 pb[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) pb[s] = as_bf16x8(g_p[head * PP + ((2 * s + lh) ^ (head & 7))]);
+    uint4 vf[32];
+    vf[0] = vfrag(0, 0);
+    vf[1] = vfrag(0, 1);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (i + 2 < 32) vf[i + 2] = vfrag((i + 2) >> 3, (i + 2) & 7);
+      st.o[i & 7] = mfma32(as_bf16x8(vf[i]), pb[i >> 3], st.o[i & 7]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -214,13 +263,20 @@ void mla_attn_kernel(const uint16_t* __restrict__ q, Str3 qs, const uint16_t* __
   State st;
   {
     const uint16_t* qp = q + b * qs.b + qi * qs.t + (g * H + head) * qs.h + 8 * lh;
+    // Q lives in AGPRs (the matrix cores read B operands from them directly),
+    // leaving the VGPRs to the O accumulators and the fragment pipeline.
 #pragma unroll
-    for (int s = 0; s < KS; ++s) st.qf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + 16 * s));
+    for (int s = 0; s < KS; ++s) {
+      st.qf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + 16 * s));
+      asm volatile("" : "+a"(st.qf[s]));
+    }
   }
 #pragma unroll
-  for (int d = 0; d < 8; ++d)
+  for (int d = 0; d < 8; ++d) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) st.o[d][e] = 0.0f;
+    asm volatile("" : "+v"(st.o[d]));
+  }
   st.m_run = -INFINITY;
   st.l_run = 0.0f;
   auto read_id = [&](int idx) -> int {
@@ -242,9 +298,11 @@ void mla_attn_kernel(const uint16_t* __restrict__ q, Str3 qs, const uint16_t* __
   __builtin_amdgcn_s_waitcnt(0x0070);
   // ---- normalise: row sum over the lane pair and both token halves
   const float lw = st.l_run + __shfl_xor(st.l_run, 32, kWave);
-  if (lh == 0) g_lsum[tt][head] = lw;
+  float* lsum = reinterpret_cast<float*>(g_tile_b);   // tile memory is free now
   __syncthreads();
-  const float ltot = g_lsum[0][head] + g_lsum[1][head];
+  if (lh == 0) lsum[tt * H + head] = lw;
+  __syncthreads();
+  const float ltot = lsum[head] + lsum[H + head];
   const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
   // stage O as [head][512] bf16 in the first tile buffer, then store rows
   uint16_t* ost = reinterpret_cast<uint16_t*>(g_tile_a);
