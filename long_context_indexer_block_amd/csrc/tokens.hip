@@ -11,6 +11,8 @@
 // integer-valued indexer data). Scores land in a per-query candidate buffer
 // [query][slot][B] whose position order is ascending token id, and one
 // workgroup per query then selects the top k from it.
+#include <algorithm>
+
 #include "common.hpp"
 #include "internal.h"
 #include "select.hpp"
@@ -64,14 +66,31 @@ __global__ void zero_u32_kernel(uint32_t* __restrict__ p, size_t n) {
     p[i] = 0u;
 }
 
-__global__ void count_pairs_kernel(const int32_t* __restrict__ block_idx, int nq, int m, int nblk,
-                                   size_t npairs, uint32_t* __restrict__ cnt) {
-  const size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x;
-  if (i >= npairs) return;
-  const int c = block_idx[i];
-  if (c < 0 || c >= nblk) return;
-  const size_t b = i / (static_cast<size_t>(nq) * m);
-  atomicAdd(&cnt[b * nblk + c], 1u);
+// Bucket counts with per-workgroup aggregation: one workgroup takes `qpw`
+// consecutive queries of one sequence, counts their blocks in an LDS
+// histogram, then adds each non-empty bin to the global count with one
+// atomic. Block 0 and the local blocks are shared by thousands of queries, so
+// direct global atomics would serialise on a few addresses.
+constexpr int kHistMax = 8192;  // largest block count with LDS histograms (64 KB)
+
+__global__ __launch_bounds__(256) void count_pairs_kernel(const int32_t* __restrict__ block_idx,
+                                                          int nq, int m, int nblk, int qpw,
+                                                          uint32_t* __restrict__ cnt) {
+  extern __shared__ uint32_t hist[];
+  const int b = blockIdx.y;
+  const int q0 = blockIdx.x * qpw, q1 = min(nq, q0 + qpw);
+  for (int c = threadIdx.x; c < nblk; c += 256) hist[c] = 0u;
+  __syncthreads();
+  const int32_t* bi = block_idx + (static_cast<int64_t>(b) * nq + q0) * m;
+  const int n = (q1 - q0) * m;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const int c = bi[i];
+    if (c >= 0 && c < nblk) atomicAdd(&hist[c], 1u);
+  }
+  __syncthreads();
+  uint32_t* cb = cnt + static_cast<int64_t>(b) * nblk;
+  for (int c = threadIdx.x; c < nblk; c += 256)
+    if (hist[c] != 0u) atomicAdd(&cb[c], hist[c]);
 }
 
 // One workgroup of 1024 threads scans the bucket counts (pair offsets and
@@ -103,9 +122,56 @@ __global__ __launch_bounds__(1024) void scan_buckets_kernel(const uint32_t* __re
   }
 }
 
-__global__ void scatter_pairs_kernel(const int32_t* __restrict__ block_idx, int nq, int m,
-                                     int nblk, size_t npairs, const uint32_t* __restrict__ offs,
-                                     uint32_t* __restrict__ cursor, uint32_t* __restrict__ pairs) {
+// Scatter with the same aggregation: each workgroup reserves one contiguous
+// range per non-empty bucket, then ranks its own entries inside it.
+__global__ __launch_bounds__(256) void scatter_pairs_kernel(
+    const int32_t* __restrict__ block_idx, int nq, int m, int nblk, int qpw,
+    const uint32_t* __restrict__ offs, uint32_t* __restrict__ cursor,
+    uint32_t* __restrict__ pairs) {
+  extern __shared__ uint32_t hist[];  // [0, nblk): counts then bases; [nblk, 2nblk): ranks
+  uint32_t* rank = hist + nblk;
+  const int b = blockIdx.y;
+  const int q0 = blockIdx.x * qpw, q1 = min(nq, q0 + qpw);
+  for (int c = threadIdx.x; c < nblk; c += 256) {
+    hist[c] = 0u;
+    rank[c] = 0u;
+  }
+  __syncthreads();
+  const int64_t e0 = (static_cast<int64_t>(b) * nq + q0) * m;
+  const int32_t* bi = block_idx + e0;
+  const int n = (q1 - q0) * m;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const int c = bi[i];
+    if (c >= 0 && c < nblk) atomicAdd(&hist[c], 1u);
+  }
+  __syncthreads();
+  const int64_t kb = static_cast<int64_t>(b) * nblk;
+  for (int c = threadIdx.x; c < nblk; c += 256) {
+    const uint32_t h = hist[c];
+    if (h != 0u) hist[c] = offs[kb + c] + atomicAdd(&cursor[kb + c], h);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const int c = bi[i];
+    if (c >= 0 && c < nblk) pairs[hist[c] + atomicAdd(&rank[c], 1u)] = static_cast<uint32_t>(e0 + i);
+  }
+}
+
+// Fallback for very many blocks per sequence: one global atomic per entry.
+__global__ void count_pairs_direct_kernel(const int32_t* __restrict__ block_idx, int nq, int m,
+                                          int nblk, size_t npairs, uint32_t* __restrict__ cnt) {
+  const size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x;
+  if (i >= npairs) return;
+  const int c = block_idx[i];
+  if (c < 0 || c >= nblk) return;
+  const size_t b = i / (static_cast<size_t>(nq) * m);
+  atomicAdd(&cnt[b * nblk + c], 1u);
+}
+__global__ void scatter_pairs_direct_kernel(const int32_t* __restrict__ block_idx, int nq, int m,
+                                            int nblk, size_t npairs,
+                                            const uint32_t* __restrict__ offs,
+                                            uint32_t* __restrict__ cursor,
+                                            uint32_t* __restrict__ pairs) {
   const size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x;
   if (i >= npairs) return;
   const int c = block_idx[i];
@@ -254,12 +320,23 @@ hipError_t launch_token_select(const uint16_t* qidx, Str3 qs, const uint16_t* ki
   hipLaunchKernelGGL(zero_u32_kernel, dim3(std::min<size_t>((zero_n + 255) / 256, 4096)),
                      dim3(256), 0, s, w.cnt, zero_n);
   const unsigned pg = static_cast<unsigned>((npairs + 255) / 256);
-  hipLaunchKernelGGL(count_pairs_kernel, dim3(pg), dim3(256), 0, s, block_idx, nq, m, nblk,
-                     npairs, w.cnt);
+  const bool lds_hist = nblk <= kHistMax;
+  const int qpw = std::max(1, 4096 / m);
+  const dim3 hg((nq + qpw - 1) / qpw, batch);
+  if (lds_hist)
+    hipLaunchKernelGGL(count_pairs_kernel, hg, dim3(256), nblk * 4, s, block_idx, nq, m, nblk, qpw,
+                       w.cnt);
+  else
+    hipLaunchKernelGGL(count_pairs_direct_kernel, dim3(pg), dim3(256), 0, s, block_idx, nq, m,
+                       nblk, npairs, w.cnt);
   hipLaunchKernelGGL(scan_buckets_kernel, dim3(1), dim3(1024), 0, s, w.cnt, nkeys, w.offs,
                      w.tile_off, w.total);
-  hipLaunchKernelGGL(scatter_pairs_kernel, dim3(pg), dim3(256), 0, s, block_idx, nq, m, nblk,
-                     npairs, w.offs, w.cursor, w.pairs);
+  if (lds_hist)
+    hipLaunchKernelGGL(scatter_pairs_kernel, hg, dim3(256), nblk * 8, s, block_idx, nq, m, nblk,
+                       qpw, w.offs, w.cursor, w.pairs);
+  else
+    hipLaunchKernelGGL(scatter_pairs_direct_kernel, dim3(pg), dim3(256), 0, s, block_idx, nq, m,
+                       nblk, npairs, w.offs, w.cursor, w.pairs);
   hipLaunchKernelGGL(tile_table_kernel, dim3((nkeys + 255) / 256), dim3(256), 0, s, w.cnt,
                      w.tile_off, nkeys, w.tiles);
 #define HISA_TS(D_, B_)                                                                       \
