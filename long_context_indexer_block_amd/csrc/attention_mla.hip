@@ -64,17 +64,16 @@ __device__ __forceinline__ void lds_barrier() {
 
 __shared__ uint4 g_tile_a[TCH];
 __shared__ uint4 g_tile_b[TCH];
-__shared__ uint4 g_p[H * PP];       // P as [head][8 chunks of 8 tokens], swizzled
+__shared__ uint4 g_p[H * PP];       // P as [head][8 chunks of 8 tokens], chunk ^ swz(head)
 __shared__ float g_mx[2][H];
 
 // Tile layout: 8-row x 8-chunk blocks of 1 KB; block (r/8, c/8) is block
 // number (r/8)*9 + c/8 and row r%8 of it holds the row's 8 chunks permuted
-// by XOR with swz(r). Sixteen consecutive rows at one chunk (the S reads) and
-// 4 rows x 2 chunks (the transposed V reads) then fall on distinct banks.
-__device__ __forceinline__ int swz(int r) {
-  const int j = (r >> 1) & 7;
-  return ((j << 1) | (j >> 2)) & 7;
-}
+// by XOR with swz(r), a permutation of (r/2)%8 whose values for rows r and
+// r+2 (r%4 < 2) differ in bit 2. Sixteen consecutive rows at one chunk (one
+// phase of the S fragment reads) and 4 rows x 4 chunks (one 32-lane phase of
+// the transposed V reads) then fall on distinct banks.
+__device__ __forceinline__ int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 __device__ __forceinline__ int slot(int r, int c) {
   return ((r >> 3) * 9 + (c >> 3)) * 64 + (r & 7) * 8 + ((c & 7) ^ swz(r));
 }
@@ -196,7 +195,7 @@ __device__ __forceinline__ void tile_step(const uint4* cur, uint4* nxt, State& s
     uint2* prow = reinterpret_cast<uint2*>(g_p + head * PP);
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq)
-      prow[2 * ((4 * tt + qq) ^ (head & 7)) + lh] = make_uint2(pk[2 * qq], pk[2 * qq + 1]);
+      prow[2 * ((4 * tt + qq) ^ swz(head)) + lh] = make_uint2(pk[2 * qq], pk[2 * qq + 1]);
   }
   if (__ballot(rescale) != 0ull) {
 #pragma unroll
@@ -229,7 +228,7 @@ __device__ __forceinline__ void tile_step(const uint4* cur, uint4* nxt, State& s
     };
     bf16x8 pb[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) pb[s] = as_bf16x8(g_p[head * PP + ((2 * s + lh) ^ (head & 7))]);
+    for (int s = 0; s < 4; ++s) pb[s] = as_bf16x8(g_p[head * PP + ((2 * s + lh) ^ swz(head))]);
     uint4 vf[32];
     vf[0] = vfrag(0, 0);
     vf[1] = vfrag(0, 1);
