@@ -129,7 +129,7 @@ __device__ __forceinline__ void tile_step(const uint4* cur, uint4* nxt, State& s
   ids_next = (idx < topk && jraw >= 0 && jraw < L) ? jraw : -1;
 
   // ---- S^T[tokens 32tt + (0..31)][heads 32hh + (0..31)] = K Q^T; each
-  // fragment read is issued two MFMAs ahead of its use
+  // fragment read is issued four MFMAs ahead of its use
   f32x16 sacc;
 #pragma unroll
   for (int e = 0; e < 16; ++e) sacc[e] = 0.0f;
@@ -140,13 +140,15 @@ __device__ __forceinline__ void tile_step(const uint4* cur, uint4* nxt, State& s
 #pragma unroll
     for (int x = 0; x < 4; ++x) base[x] = 16 * slot(r, 2 * x + lh);
     uint4 kf[KS];
+    constexpr int AHEAD = 4;
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int s = 0; s < AHEAD; ++s)
       kf[s] = *reinterpret_cast<const uint4*>(tb + base[s & 3] + 1024 * (s >> 2));
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      if (s + 2 < KS)
-        kf[s + 2] = *reinterpret_cast<const uint4*>(tb + base[(s + 2) & 3] + 1024 * ((s + 2) >> 2));
+      if (s + AHEAD < KS)
+        kf[s + AHEAD] =
+            *reinterpret_cast<const uint4*>(tb + base[(s + AHEAD) & 3] + 1024 * ((s + AHEAD) >> 2));
       sacc = mfma32(as_bf16x8(kf[s]), st.qf[s], sacc);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -206,7 +208,7 @@ __device__ __forceinline__ void tile_step(const uint4* cur, uint4* nxt, State& s
   lds_barrier();
 
   // ---- O^T[dv 256tt + 32dt + (0..31)][heads] += V^T P^T over the tile's 64
-  // tokens; V^T fragments (two transposed reads each) run one MFMA ahead
+  // tokens; V^T fragments (two transposed reads each) run three MFMAs ahead
   {
     const int G = l >> 4, sl = l & 15;
     const int trow = 8 * (G >> 1) + (sl >> 2);
@@ -229,12 +231,13 @@ __device__ __forceinline__ void tile_step(const uint4* cur, uint4* nxt, State& s
     bf16x8 pb[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) pb[s] = as_bf16x8(g_p[head * PP + ((2 * s + lh) ^ swz(head))]);
+    constexpr int AHEAD = 3;
     uint4 vf[32];
-    vf[0] = vfrag(0, 0);
-    vf[1] = vfrag(0, 1);
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) vf[i] = vfrag(i >> 3, i & 7);
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      if (i + 2 < 32) vf[i + 2] = vfrag((i + 2) >> 3, (i + 2) & 7);
+      if (i + AHEAD < 32) vf[i + AHEAD] = vfrag((i + AHEAD) >> 3, (i + AHEAD) & 7);
       st.o[i & 7] = mfma32(as_bf16x8(vf[i]), pb[i >> 3], st.o[i & 7]);
       __builtin_amdgcn_sched_barrier(0);
     }
