@@ -66,6 +66,7 @@ __shared__ uint4 g_tile_a[TCH];
 __shared__ uint4 g_tile_b[TCH];
 __shared__ uint4 g_p[H * PP];       // P as [head][8 chunks of 8 tokens], chunk ^ swz(head)
 __shared__ float g_mx[2][H];
+__shared__ int g_flag[4];
 
 // Tile layout: 8-row x 8-chunk blocks of 1 KB; block (r/8, c/8) is block
 // number (r/8)*9 + c/8 and row r%8 of it holds the row's 8 chunks permuted
@@ -78,35 +79,52 @@ __device__ __forceinline__ int slot(int r, int c) {
   return ((r >> 3) * 9 + (c >> 3)) * 64 + (r & 7) * 8 + ((c & 7) ^ swz(r));
 }
 
-// Gather the 64 latent rows of one tile into `dst`: wave w loads rows
-// 16w .. 16w+15 as 18 direct-to-LDS instructions, each filling one 1 KB block
-// (8 rows x 128 bytes; lane l takes row r = 8*rg + l/8 and its logical chunk
+// Gather of one tile into `dst`: wave w loads rows 16w .. 16w+15 as 18
+// direct-to-LDS instructions, each filling one 1 KB block (8 rows x 128
+// bytes; lane l takes row r = 8*rg + l/8 and its logical chunk
 // 8*ln + ((l%8) ^ swz(r)), so 8 adjacent lanes read one 128-byte line).
-__device__ __forceinline__ void dma_tile(uint4* dst, const uint16_t* kvb, int64_t kst, int ids,
-                                         int w, int l) {
+// The instructions are issued one by one between matrix-core operations:
+// the address unit processes them at a fixed rate per CU, and issued in one
+// burst they would stall the wave.
+struct Gather {
+  const uint16_t* src[2];
+  __device__ __forceinline__ void setup(const uint16_t* kvb, int64_t kst, int ids, int w, int l) {
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int rg = 2 * w + k;
-    const int r = 8 * rg + (l >> 3);
-    const int id = __shfl(ids, r, kWave);
-    const uint16_t* src = kvb + static_cast<int64_t>(id < 0 ? 0 : id) * kst + 8 * ((l & 7) ^ swz(r));
-#pragma unroll
-    for (int ln = 0; ln < 9; ++ln)
-      __builtin_amdgcn_global_load_lds((glb_ptr)(src + 64 * ln), (lds_ptr)(dst + (rg * 9 + ln) * 64),
-                                       16, 0, 0);
+    for (int k = 0; k < 2; ++k) {
+      const int r = 8 * (2 * w + k) + (l >> 3);
+      const int id = __shfl(ids, r, kWave);
+      src[k] = kvb + static_cast<int64_t>(id < 0 ? 0 : id) * kst + 8 * ((l & 7) ^ swz(r));
+    }
   }
-}
+  __device__ __forceinline__ void issue(uint4* dst, int w, int j) const {
+    const int k = j / 9, ln = j % 9;
+    __builtin_amdgcn_global_load_lds((glb_ptr)(src[k] + 64 * ln),
+                                     (lds_ptr)(dst + ((2 * w + k) * 9 + ln) * 64), 16, 0, 0);
+  }
+};
 
 struct State {
   bf16x8 qf[KS];
   f32x16 o[8];
   float m_run, l_run;
+  bool seen;  // a valid token was seen (same in every wave: ids are shared)
 };
 
+// Reference maximum handling (base-2 logits, scale folded in): P of a tile
+// is exponentiated against the reference agreed so far, so the two waves
+// sharing a head need no exchange before the exponentials. Tile maxima are
+// exchanged with P at the one barrier before P.V; afterwards the reference
+// moves (and O, l are rescaled) when a tile maximum exceeds it by more than
+// kLazy. Only the first valid tile, and a tile whose maximum exceeds the
+// reference by more than kRedo (p would leave the fp32 range), take a second
+// barrier and exponentiate against the exchanged maximum.
+constexpr float kLazy = 8.0f, kRedo = 64.0f;
+
 // One tile: S^T, softmax, P, O^T update. `cur` holds the tile; the next
-// tile's loads into `nxt` are issued first, always (past the last tile every
-// id is -1 and the loads fetch row 0 again, which hits in cache), so the
-// code is straight-line and the compiler's load-counter waits stay exact.
+// tile's gather into `nxt` is interleaved with the S products (always issued:
+// past the last tile every id is -1 and the loads fetch row 0 again, which
+// hits in cache), so the code is straight-line and the compiler's
+// load-counter waits stay exact.
 __device__ __forceinline__ void tile_step(const uint4* cur, uint4* nxt, State& st,
                                           int& ids_cur, int& ids_next, const int32_t* tix, int topk,
                                           int L, int tile, const uint16_t* kvb, int64_t kst,
@@ -124,12 +142,14 @@ __device__ __forceinline__ void tile_step(const uint4* cur, uint4* nxt, State& s
   // in order, so waiting for the ids later never drains the gather
   const int idx = (tile + 2) * NT + l;
   const int jraw = tix[min(idx, topk - 1)];
-  dma_tile(nxt, kvb, kst, ids_next, w, l);
+  Gather ga;
+  ga.setup(kvb, kst, ids_next, w, l);
   ids_cur = ids_next;
   ids_next = (idx < topk && jraw >= 0 && jraw < L) ? jraw : -1;
 
   // ---- S^T[tokens 32tt + (0..31)][heads 32hh + (0..31)] = K Q^T; each
-  // fragment read is issued four MFMAs ahead of its use
+  // fragment read is issued four MFMAs ahead of its use, and one gather
+  // instruction of the next tile follows every second MFMA
   f32x16 sacc;
 #pragma unroll
   for (int e = 0; e < 16; ++e) sacc[e] = 0.0f;
@@ -150,6 +170,7 @@ __device__ __forceinline__ void tile_step(const uint4* cur, uint4* nxt, State& s
         kf[s + AHEAD] =
             *reinterpret_cast<const uint4*>(tb + base[(s + AHEAD) & 3] + 1024 * ((s + AHEAD) >> 2));
       sacc = mfma32(as_bf16x8(kf[s]), st.qf[s], sacc);
+      if (s & 1) ga.issue(nxt, w, s >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -169,43 +190,64 @@ __device__ __forceinline__ void tile_step(const uint4* cur, uint4* nxt, State& s
   for (int e = 1; e < 16; ++e) mloc = fmaxf(mloc, sv[e]);
   mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave)) * scale_log2;
   if (lh == 0) g_mx[tt][head] = mloc;
-  lds_barrier();
-  // Lazy rescaling: the reference maximum moves only when the tile maximum
-  // exceeds it by more than 8 (a factor 256 in p), so most tiles leave O
-  // untouched. Every lane holding a head takes the same decision.
-  const float mtile = fmaxf(mloc, g_mx[tt ^ 1][head]);
-  const float mold = st.m_run;
-  const bool move = mtile > mold + 8.0f;
-  const float mref = move ? mtile : mold;
-  const float mneg = mref == -INFINITY ? 0.0f : -mref;
-  float psum = 0.0f;
-  uint32_t pk[8];
+  float mref = st.m_run;
+  float mtile;
+  const float l_prev = st.l_run;
+  // exponentials of the tile against reference m; returns their sum and
+  // writes P[head][token 32tt + 8q + 4lh + (0..3)] (chunk 4tt + q, half lh)
+  auto make_p = [&](float m) -> float {
+    const float mneg = m == -INFINITY ? 0.0f : -m;
+    float ps = 0.0f;
+    uint32_t pk[8];
 #pragma unroll
-  for (int e = 0; e < 16; e += 2) {
-    const float a = __builtin_amdgcn_exp2f(fmaf(sv[e], scale_log2, mneg));
-    const float c = __builtin_amdgcn_exp2f(fmaf(sv[e + 1], scale_log2, mneg));
-    psum += a + c;
-    pk[e >> 1] = pack2(a, c);
-  }
-  // O and l are zero until the first valid tile, so no rescale is needed then
-  const bool rescale = move && mold != -INFINITY;
-  const float alpha = rescale ? __builtin_amdgcn_exp2f(mold - mtile) : 1.0f;
-  st.m_run = mref;
-  st.l_run = st.l_run * alpha + psum;
-  // P[head][token 32tt + 8q + 4lh + (0..3)]: chunk 4tt + q, half lh
-  {
+    for (int e = 0; e < 16; e += 2) {
+      const float a = __builtin_amdgcn_exp2f(fmaf(sv[e], scale_log2, mneg));
+      const float c = __builtin_amdgcn_exp2f(fmaf(sv[e + 1], scale_log2, mneg));
+      ps += a + c;
+      pk[e >> 1] = pack2(a, c);
+    }
     uint2* prow = reinterpret_cast<uint2*>(g_p + head * PP);
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq)
       prow[2 * ((4 * tt + qq) ^ swz(head)) + lh] = make_uint2(pk[2 * qq], pk[2 * qq + 1]);
-  }
-  if (__ballot(rescale) != 0ull) {
+    return ps;
+  };
+  auto rescale_o = [&](float a) {
+    if (__ballot(a != 1.0f) != 0ull) {
 #pragma unroll
-    for (int d = 0; d < 8; ++d)
+      for (int d = 0; d < 8; ++d)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) st.o[d][e] *= alpha;
+        for (int e = 0; e < 16; ++e) st.o[d][e] *= a;
+    }
+  };
+  if (!st.seen) {
+    // no valid token seen before this tile (the same in every wave): agree
+    // on the tile maximum first
+    lds_barrier();
+    mtile = fmaxf(mloc, g_mx[tt ^ 1][head]);
+    mref = mtile;
+    st.l_run = make_p(mref);
+    lds_barrier();
+  } else {
+    g_flag[w] = __ballot(mloc > mref + kRedo) != 0ull ? 1 : 0;
+    const float ps = make_p(mref);
+    st.l_run = l_prev + ps;
+    lds_barrier();
+    mtile = fmaxf(mloc, g_mx[tt ^ 1][head]);
+    if ((g_flag[0] | g_flag[1] | g_flag[2] | g_flag[3]) != 0) {
+      // a score left the safe range above the reference: every wave redoes
+      // the tile against the new maximum (S is still in registers)
+      const float mnew = fmaxf(mref, mtile);
+      const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
+      rescale_o(alpha);
+      lds_barrier();  // everyone has read P and the maxima
+      st.l_run = l_prev * alpha + make_p(mnew);
+      mref = mnew;
+      lds_barrier();
+    }
   }
-  lds_barrier();
+  st.m_run = mref;
+  st.seen = st.seen || vmask != 0ull;
 
   // ---- O^T[dv 256tt + 32dt + (0..31)][heads] += V^T P^T over the tile's 64
   // tokens; V^T fragments (two transposed reads each) run three MFMAs ahead
@@ -241,6 +283,18 @@ __device__ __forceinline__ void tile_step(const uint4* cur, uint4* nxt, State& s
       st.o[i & 7] = mfma32(as_bf16x8(vf[i]), pb[i >> 3], st.o[i & 7]);
       __builtin_amdgcn_sched_barrier(0);
     }
+  }
+  // lazy move of the reference: the tile maximum (both token halves) is
+  // known to every lane of a head, so all four copies decide alike
+  const bool move = mtile > st.m_run + kLazy;
+  if (__ballot(move) != 0ull) {
+    const float a2 = move ? __builtin_amdgcn_exp2f(st.m_run - mtile) : 1.0f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st.o[d][e] *= a2;
+    st.l_run *= a2;
+    st.m_run = move ? mtile : st.m_run;
   }
 }
 
@@ -281,12 +335,18 @@ void mla_attn_kernel(const uint16_t* __restrict__ q, Str3 qs, const uint16_t* __
   }
   st.m_run = -INFINITY;
   st.l_run = 0.0f;
+  st.seen = false;
   auto read_id = [&](int idx) -> int {
     const int j = tix[min(idx, topk - 1)];
     return (idx < topk && j >= 0 && j < L) ? j : -1;
   };
   int ids_cur = read_id(l);
-  dma_tile(g_tile_a, kvb, ks.t, ids_cur, w, l);
+  {
+    Gather ga;
+    ga.setup(kvb, ks.t, ids_cur, w, l);
+#pragma unroll
+    for (int j = 0; j < 18; ++j) ga.issue(g_tile_a, w, j);
+  }
   int ids_next = read_id(NT + l);
 
   // an odd tile count gets one extra, fully masked tile
