@@ -13,6 +13,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -39,6 +40,8 @@ def parse():
     ap.add_argument("--no-flat", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="only run a plain device copy of this many bytes (counter calibration)")
     return ap.parse_args()
 
 
@@ -74,7 +77,7 @@ def cpu_baseline(w, inp, budget_s):
     summ = O.block_summary(kidx, w.B)
     t_summary = time.perf_counter() - t0
     rng = np.random.default_rng(0)
-    pos = sample_positions(w, 64)
+    pos = sample_positions(w, 400)
     rng.shuffle(pos)
     done = 0
     t0 = time.perf_counter()
@@ -98,28 +101,82 @@ def cpu_baseline(w, inp, budget_s):
                       f"not included; host cpu_count={os.cpu_count()}, affinity={aff}"}
 
 
-def main():
-    a = parse()
-    if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the path has no "
-              "multi-GPU form in this build", file=sys.stderr)
-        sys.exit(2)
+def kernel_source_hash():
+    import hashlib
+    path = os.path.join(ROOT, "long_context_indexer_block_amd", "csrc", "attention_mla.hip")
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed counter summary
+    (rocprofv3 FETCH_SIZE and WRITE_SIZE, scaled by the factor a plain copy
+    of known size gives), or None when the kernel changed since then."""
+    path = os.path.join(ROOT, "profiles", "attention_mla_64k_traffic.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_probe(nbytes):
+    """A plain device copy of `nbytes` (for calibrating the byte counters)."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes}))
+
+
+def timed(calls, steps, warmup):
+    """Run `calls` (a list of thunks) as one step; HIP events around each."""
+    import torch
+    for _ in range(warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        for i, c in enumerate(calls):
+            ev[s][i].record()
+            c()
+        ev[s][-1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage = [sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps
+             for i in range(len(calls))]
+    return wall, stage
+
+
+def base_record(w, a, nq, wall, dtype="bf16"):
+    ms_step = wall * 1e3 / a.steps
+    return {
+        "metric": METRIC, "value": nq * a.steps / wall, "unit": "queries/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+        "config": {"workload": w.name, "kind": w.kind, "batch": w.batch, "queries": nq, "L": w.L,
+                   "B": w.B, "m": w.m, "k": w.k, "indexer_d": w.d_idx, "Hq": w.Hq,
+                   "Hkv": w.Hkv, "Dk": w.Dk, "Dv": w.Dv},
+    }
+
+
+def bench_prefill(w, a, inp):
     import torch
 
-    import long_context_indexer_block_amd as H  # noqa: F401  (raises without libhisa.so)
+    import long_context_indexer_block_amd as H
     from long_context_indexer_block_amd.pipeline import FlatPipeline, HierPipeline
-    from workloads import WORKLOADS, make_inputs
 
-    w = WORKLOADS[a.workload]
-    assert w.kind == "prefill", "the timed step is the prefill path"
-    torch.cuda.set_device(0)
-    log(f"generating {w.name} inputs on the GPU")
-    inp = make_inputs(w, "cuda", seed=0)
-    torch.cuda.synchronize()
     nq = w.batch * w.queries
     p = HierPipeline(inp["kidx"], inp["qidx"], inp["q_pos"], inp["q"], inp["k"], inp["v"], w.B,
                      w.m, w.k, w.scale)
-
     stages = ["summary", "block_score", "select_blocks", "token_select", "attention"]
     calls = [
         p.summarize,
@@ -129,83 +186,158 @@ def main():
                                     token_idx=p.token_idx, want_scores=False, workspace=p.ws),
         p.attend,
     ]
-
-    def step(evs=None):
-        for i, c in enumerate(calls):
-            if evs is not None:
-                evs[i].record()
-            c()
-        if evs is not None:
-            evs[-1].record()
-
-    log(f"warmup {a.warmup}")
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
+    log(f"timing {a.steps} steps (warmup {a.warmup})")
+    wall, stage = timed(calls, a.steps, a.warmup)
+    stage_ms = dict(zip(stages, stage))
     # algorithmic work of the attention launch: 2*(Dk+Dv) flop per (query, head, kept token)
     n_sel = int((p.token_idx >= 0).sum().item())
     attn_flop = 2.0 * n_sel * w.Hq * (w.Dk + w.Dv)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
-          for _ in range(a.steps)]
-    log(f"timing {a.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(a.steps):
-        step(ev[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    stage_ms = {n: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(a.steps)) / a.steps
-                for i, n in enumerate(stages)}
-    ms_step = wall * 1e3 / a.steps
-    qps = nq * a.steps / wall
-    attn_ms = stage_ms["attention"]
-    achieved = attn_flop / (attn_ms * 1e-3) / 1e12
-    indexer_ms = sum(stage_ms[s] for s in stages[:4])
-
-    res = {
-        "metric": METRIC, "value": qps, "unit": "queries/s", "n_gpus": 1, "steps": a.steps,
-        "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "queries": nq, "L": w.L, "B": w.B,
-                   "m": w.m, "k": w.k, "indexer_d": w.d_idx, "Hq": w.Hq, "Hkv": w.Hkv,
-                   "Dk": w.Dk, "Dv": w.Dv, "kv": "MLA latent, V = first 512 columns of K"},
-        "stage_ms": stage_ms,
-        "roofline": {"kernel": "sparse_attn (MLA 576/512, 64 heads)", "bound": "mfma",
-                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-                     "alg_flop_per_launch": attn_flop, "kept_tokens": n_sel},
-    }
+    achieved = attn_flop / (stage_ms["attention"] * 1e-3) / 1e12
+    res = base_record(w, a, nq, wall)
+    ms_step = res["ms_per_step"]
+    res["config"]["kv"] = ("MLA latent, V = first 512 columns of K" if w.mla else
+                           f"{w.Hkv} kv head(s)")
+    res["stage_ms"] = stage_ms
+    traffic = measured_traffic() if (w.mla and w.name == "prefill_64k_mla") else None
+    res["roofline"] = {"kernel": f"sparse_attn ({w.Hq} heads, Dk {w.Dk}, Dv {w.Dv})",
+                       "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                       "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                       "traffic": traffic, "alg_flop_per_launch": attn_flop,
+                       "kept_tokens": n_sel}
     idx_flop = indexer_flop(w)
     t_roof = (attn_flop + idx_flop) / (PEAK_BF16_TFLOPS * 1e12)
     res["path_roofline"] = {"bound": "mfma", "alg_flop": attn_flop + idx_flop,
                             "t_roof_ms": t_roof * 1e3, "frac": t_roof / (ms_step * 1e-3)}
-    del ev
     if not a.no_flat:
         log("flat comparison")
+        ws_needed = H.flat_indexer_topk_workspace_bytes(w.batch, w.queries, w.L, w.k)
         del p
         torch.cuda.empty_cache()
-        f = FlatPipeline(inp["kidx"], inp["qidx"], inp["q_pos"], inp["q"], inp["k"], inp["v"], w.k,
-                         w.scale)
-        for _ in range(max(1, a.warmup - 1)):
-            f.run()
+        f = FlatPipeline(inp["kidx"], inp["qidx"], inp["q_pos"], inp["q"], inp["k"], inp["v"],
+                         w.k, w.scale)
+        fwall, fstage = timed([f.index, f.attend], max(2, a.steps // 2), max(1, a.warmup - 1))
         fs = max(2, a.steps // 2)
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3 * fs)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for s in range(fs):
-            e[3 * s].record()
-            f.index()
-            e[3 * s + 1].record()
-            f.attend()
-            e[3 * s + 2].record()
-        torch.cuda.synchronize()
-        fwall = (time.perf_counter() - t0) * 1e3 / fs
-        f_idx = sum(e[3 * s].elapsed_time(e[3 * s + 1]) for s in range(fs)) / fs
-        res["flat"] = {"ms_per_step": fwall, "indexer_ms": f_idx,
-                       "speedup_vs_flat": fwall / ms_step,
-                       "indexer_speedup_vs_flat": f_idx / indexer_ms}
+        f_ms = fwall * 1e3 / fs
+        idx_ms = sum(stage_ms[s] for s in stages[:4])
+        res["flat"] = {"ms_per_step": f_ms, "indexer_ms": fstage[0], "attention_ms": fstage[1],
+                       "workspace_bytes": ws_needed, "speedup_vs_flat": f_ms / ms_step,
+                       "indexer_speedup_vs_flat": fstage[0] / idx_ms}
         del f
-    if not a.no_cpu:
+    return res
+
+
+def bench_decode(w, a, inp):
+    import torch
+
+    import long_context_indexer_block_amd as H
+    from long_context_indexer_block_amd.pipeline import HierPipeline
+
+    nq = w.batch * w.queries
+    p = HierPipeline(inp["kidx"], inp["qidx"], inp["q_pos"], inp["q"], inp["k"], inp["v"], w.B,
+                     w.m, w.k, w.scale)
+    # the block summaries belong to the cache: built once, timed apart
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    p.summarize()
+    e1.record()
+    torch.cuda.synchronize()
+    summary_ms = e0.elapsed_time(e1)
+    # Per-step HBM bytes exceed a single step's cache reuse only if the cache
+    # is cold: rotate through 4 query sets so the 235 MB working set of one
+    # step is not served from the 256 MB last-level cache every time.
+    qsets = [inp["qidx"]] + [torch.roll(inp["qidx"], shifts=i, dims=0) for i in (1, 2, 3)]
+    qs = [inp["q"]] + [torch.roll(inp["q"], shifts=i, dims=0) for i in (1, 2, 3)]
+    state = {"i": 0}
+
+    def pick():
+        i = state["i"] = (state["i"] + 1) % 4
+        p.qidx, p.q = qsets[i], qs[i]
+
+    stages = ["rotate_query_set", "block_score", "select_blocks", "token_select", "attention"]
+    calls = [
+        pick,
+        lambda: H.hisa_block_score(p.qidx, p.q_pos, p.split, p.B, out=p.block_scores),
+        lambda: H.hisa_select_blocks(p.block_scores, p.q_pos, p.B, p.m, out=p.block_idx),
+        lambda: H.hisa_token_select(p.qidx, p.kidx, p.q_pos, p.block_idx, p.B, p.k_top,
+                                    token_idx=p.token_idx, want_scores=False, workspace=p.ws),
+        p.attend,
+    ]
+    wall, stage = timed(calls, a.steps, a.warmup)
+    res = base_record(w, a, nq, wall)
+    res["stage_ms"] = dict(zip(stages, stage))
+    res["summary_build_ms"] = summary_ms
+    # per-step compulsory HBM bytes: summaries (hi/mid/lo), the kept blocks'
+    # keys, the kept tokens' K and V rows
+    n_sel = int((p.token_idx >= 0).sum().item())
+    nblk_kept = int((p.block_idx >= 0).sum().item())
+    # (fp32 block summaries of the candidate blocks, as the method defines them;
+    # the kernel reads their exact bf16 hi/mid/lo form, 1.5x these bytes)
+    bytes_step = (w.batch * w.n_blocks * w.d_idx * 4 + nblk_kept * w.B * w.d_idx * 2 +
+                  n_sel * (w.Dk + w.Dv) * 2 * w.Hkv)
+    ms = res["ms_per_step"]
+    res["roofline"] = {"kernel": "whole decode step", "bound": "hbm",
+                       "achieved": bytes_step / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                       "unit": "GB/s", "frac": bytes_step / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                       "traffic": None, "alg_bytes_per_step": bytes_step}
+    return res
+
+
+def bench_hils(w, a, inp):
+    import torch
+
+    from long_context_indexer_block_amd.pipeline import HilsDecode
+
+    sc = 1.0 / math.sqrt(w.Dk)
+    hd = HilsDecode(inp["q"], inp["k"], inp["v"], inp["w_proj"], w.B, w.m, sc, sc)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    hd.build_keys()
+    e1.record()
+    torch.cuda.synchronize()
+    wall, stage = timed([hd.route, hd.attend], a.steps, a.warmup)
+    res = base_record(w, a, w.batch * w.Hq, wall)
+    res["config"]["queries"] = w.batch
+    res["value"] = w.batch * a.steps / wall
+    res["stage_ms"] = {"route": stage[0], "two_level_attention": stage[1]}
+    res["chunk_key_build_ms"] = e0.elapsed_time(e1)
+    n = hd.n
+    # fp32 chunk keys of every chunk, then the chosen chunks' K and V rows
+    bytes_step = (w.batch * w.Hq * n * w.Dk * 4 +
+                  w.batch * w.Hq * w.m * w.B * w.Dk * 2 * 2)
+    ms = res["ms_per_step"]
+    res["roofline"] = {"kernel": "whole two-level decode step", "bound": "hbm",
+                       "achieved": bytes_step / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                       "unit": "GB/s", "frac": bytes_step / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                       "traffic": None, "alg_bytes_per_step": bytes_step}
+    return res
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the path has no "
+              "multi-GPU form in this build", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import long_context_indexer_block_amd as H  # noqa: F401  (raises without libhisa.so)
+    from workloads import WORKLOADS, make_inputs
+
+    if a.copy_probe:
+        copy_probe(a.copy_probe)
+        return
+    w = WORKLOADS[a.workload]
+    torch.cuda.set_device(0)
+    log(f"generating {w.name} inputs on the GPU")
+    inp = make_inputs(w, "cuda", seed=0)
+    torch.cuda.synchronize()
+    if w.kind == "prefill":
+        res = bench_prefill(w, a, inp)
+    elif w.kind == "decode":
+        res = bench_decode(w, a, inp)
+    else:
+        res = bench_hils(w, a, inp)
+    if not a.no_cpu and w.kind == "prefill":
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_seconds)
     print(json.dumps(res), flush=True)
