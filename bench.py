@@ -24,7 +24,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak
-METRIC = "indexer+sparse-attn queries/s at 64K"
+METRIC = "indexer+sparse-attn queries/s at 64K; % HBM/MFMA roofline; speedup vs flat"
 
 
 def log(*a):
