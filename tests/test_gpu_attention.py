@@ -1,0 +1,100 @@
+"""GPU parity of sparse_attn_fwd on hand-built token lists, output and
+log-sum-exp, against the oracle's attention over the same lists.
+
+The lists exercise what the indexer never produces but the entry point
+accepts: ragged lengths (1, 33, 77 tokens), -1 holes in the middle, ids at
+or past L (skipped by contract, dropped for the oracle), repeated ids (a
+multiset: counted twice on both sides), a list with no valid token (zero
+output, log-sum-exp -inf), and logit ranges wide enough that the running
+reference of the online softmax must move or be redone."""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_indexer_block_amd as H
+import oracle.hisa_oracle as O
+from parity import check_attention, f64, log
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+# name, L, nq, topk, Hq, Hkv, Dk, Dv, latent (V = K[..., :Dv]), q scale, k scale, list pattern
+CASES = [
+    ("mla_k1", 300, 6, 1, 64, 1, 576, 512, True, 1 / 24, 1 / 24, "sorted"),
+    ("mla_k33_holes", 1000, 8, 33, 64, 1, 576, 512, True, 1.0, 1 / 24, "holes"),
+    ("mla_k77_dups_oob", 700, 8, 77, 64, 1, 576, 512, True, 1 / 24, 1 / 24, "dups_oob"),
+    ("mla_k2048", 4096, 4, 2048, 64, 1, 576, 512, True, 1 / 24, 1 / 24, "sorted"),
+    ("mla_lazy_moves", 3000, 6, 600, 64, 1, 576, 512, True, 24 * 30, 1 / 24, "sorted"),
+    ("mla_redo", 3000, 6, 600, 64, 1, 576, 512, True, 24 * 60, 1 / 24, "late_peak"),
+    ("mla_empty", 512, 3, 64, 64, 1, 576, 512, True, 1.0, 1 / 24, "empty"),
+    ("mqa_holes", 1000, 8, 100, 16, 1, 128, 128, False, 1.0, 1.0, "holes"),
+    ("gqa_dups_oob", 800, 8, 45, 8, 2, 64, 64, False, 1.0, 1.0, "dups_oob"),
+]
+
+
+def _lists(pattern, L, nq, topk, g):
+    """token_idx [nq, topk] int32 for the GPU and the oracle's view of it."""
+    rows = []
+    for _ in range(nq):
+        if pattern == "empty":
+            r = np.full(topk, -1)
+        else:
+            n = min(topk, L)
+            r = np.sort(g.choice(L, size=n, replace=False))
+            r = np.concatenate([r, np.full(topk - n, -1)])
+            if pattern == "late_peak":
+                # every list ends with the 8 last tokens, whose keys are boosted
+                r = np.concatenate([np.sort(g.choice(L - 8, size=topk - 8, replace=False)),
+                                    np.arange(L - 8, L)])
+            elif pattern == "holes":
+                r[g.random(topk) < 0.2] = -1
+            elif pattern == "dups_oob":
+                k = max(1, topk // 5)
+                r[g.choice(topk, k, replace=False)] = r[g.choice(topk, k, replace=False)]
+                r[g.choice(topk, k, replace=False)] = L + g.integers(0, 1000, size=k)
+        rows.append(r)
+    gpu = np.stack(rows).astype(np.int32)
+    ref = np.where(gpu >= L, -1, gpu)
+    return gpu, ref
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_sparse_attention_lists(case):
+    name, L, nq, topk, Hq, Hkv, Dk, Dv, latent, qs, ks, pattern = case
+    log(f"case attention {name}")
+    seed = zlib.crc32(name.encode())
+    tg = torch.Generator(device="cpu").manual_seed(seed)
+    g = np.random.default_rng(seed)
+    q = (torch.randn(1, nq, Hq, Dk, generator=tg) * qs).to(torch.bfloat16)
+    kk = (torch.randn(1, L, Hkv, Dk, generator=tg) * ks).to(torch.bfloat16)
+    vv = kk[..., :Dv] if latent else (torch.randn(1, L, Hkv, Dv, generator=tg) * ks).to(
+        torch.bfloat16)
+    idx, ref_idx = _lists(pattern, L, nq, topk, g)
+    if pattern == "late_peak":
+        # the largest keys sit in the last tiles of every list: the reference
+        # set on the first tile is exceeded by far later on
+        kk[0, L - 8:, :, :] *= 4
+        vv = kk[..., :Dv]
+    scale = 1.0 / math.sqrt(Dk)
+    qd, kd = q.to(DEV), kk.to(DEV)
+    vd = kd[..., :Dv] if latent else vv.to(DEV)
+    out, lse = H.sparse_attn_fwd(qd, kd, vd, torch.from_numpy(idx)[None].to(DEV), scale,
+                                 want_lse=True)
+    torch.cuda.synchronize()
+    go = out[0].float().cpu().numpy()
+    gl = lse[0].cpu().numpy().astype(np.float64)
+    K64, V64 = f64(kk[0]), f64(vv[0])
+    for r in range(nq):
+        ro, rl = O.sparse_attention_for_query(f64(q[0, r]), K64, V64, ref_idx[r], scale)
+        check_attention(go[r], ro, f"{name} row {r}")
+        if np.isinf(rl).all():
+            assert np.isneginf(gl[r]).all(), f"{name} row {r}: lse {gl[r][:4]}"
+            assert (go[r] == 0).all()
+        else:
+            err = np.abs(gl[r] - rl)
+            assert err.max() <= 1e-3 + 1e-5 * np.abs(rl).max(), f"{name} row {r}: lse err {err.max()}"
+    log(f"  {name}: ok")
