@@ -131,11 +131,14 @@ __device__ __forceinline__ uint4* pbuf() {
 
 // Tile layout: 8-row x 8-chunk blocks of 1 KB; block (r/8, c/8) is block
 // number (r/8)*9 + c/8 and row r%8 of it holds the row's 8 chunks permuted
-// by XOR with swz(r), a permutation of (r/2)%8 whose values for rows r and
-// r+2 (r%4 < 2) differ in bit 2. Sixteen consecutive rows at one chunk (one
-// phase of the S fragment reads) and 4 rows x 4 chunks (one 32-lane phase of
-// the transposed V reads) then fall on distinct banks.
-__device__ __forceinline__ int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+// by XOR with swz(r), which swaps bits 1 and 2 of r (bit 0 and bit 3 drop
+// out). The LDS serves a 16-byte read 16 lanes at a time, the lanes of one
+// cycle being the four lane quads whose quad index (lane bits 2..4) has one
+// parity, within each 32-lane half; it serves a transposing 8-byte read 32
+// lanes at a time. With this swizzle the 16 lanes of each cycle of an S
+// fragment read (16 rows at two adjacent chunks) and the 32 lanes of each
+// cycle of a transposed V read (4 rows x 4 chunks) fall on distinct banks.
+__device__ __forceinline__ int swz(int r) { return ((r & 4) >> 1) | ((r & 2) << 1); }
 __device__ __forceinline__ int slot(int r, int c) {
   return ((r >> 3) * 9 + (c >> 3)) * 64 + (r & 7) * 8 + ((c & 7) ^ swz(r));
 }
@@ -149,18 +152,19 @@ __device__ __forceinline__ void ids_issue(const int32_t* tix, int topk, int tile
   __builtin_amdgcn_global_load_lds((glb_ptr)(tix + min(tile * NT + (l & 31), topk - 1)),
                                    (lds_ptr)(&g_ids[tile & 7][0]), 4, 0, 0);
 }
-__device__ __forceinline__ uint32_t id_addr(int tile, int l) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int*)(&g_ids[tile & 7][l & 31]);
+__device__ __forceinline__ uint32_t id_addr(int tile, int t) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int*)(&g_ids[tile & 7][t]);
 }
-// Lane l's ids of two tiles. Ids are loaded several tiles ahead and are
-// covered by an earlier barrier's load-counter wait; the reads are written
-// out here because the compiler cannot tell the ring slots apart and would
-// otherwise drain every load in flight first.
-__device__ __forceinline__ int2 lane_ids_of(int tile_a, int tile_b, int l) {
+// Two ids (tile a, token ta) and (tile b, token tb) per lane. Ids are loaded
+// several tiles ahead and are covered by an earlier barrier's load-counter
+// wait; the reads are written out here because the compiler cannot tell the
+// ring slots apart and would otherwise drain every load in flight first. The
+// wait also covers any LDS read the caller issued just before.
+__device__ __forceinline__ int2 read_ids(int tile_a, int ta, int tile_b, int tb) {
   int a, b;
   asm volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %3\n\ts_waitcnt lgkmcnt(0)"
                : "=&v"(a), "=&v"(b)
-               : "v"(id_addr(tile_a, l)), "v"(id_addr(tile_b, l))
+               : "v"(id_addr(tile_a, ta)), "v"(id_addr(tile_b, tb))
                : "memory");
   return make_int2(a, b);
 }
@@ -174,10 +178,10 @@ __device__ __forceinline__ uint32_t tile_mask(int id, int topk, int L, int tile,
 // 8 adjacent lanes read one 128-byte line. The instructions are spread
 // between matrix-core operations: the address unit processes them at a fixed
 // rate per CU, and issued in one burst they would stall the wave.
+// id: the id of row r = 8rg + l/8 of the tile
 __device__ __forceinline__ const uint16_t* gather_src(const uint16_t* kvb, int64_t kst, int L,
-                                                      int id_lane, int rg, int l) {
+                                                      int id, int rg, int l) {
   const int r = 8 * rg + (l >> 3);
-  const int id = __shfl(id_lane, r, kWave);
   const int row = static_cast<unsigned>(id) < static_cast<unsigned>(L) ? id : 0;
   return kvb + static_cast<int64_t>(row) * kst + 8 * ((l & 7) ^ swz(r));
 }
@@ -352,9 +356,7 @@ __device__ __forceinline__ void scale_in_place(f32x16& o, float a) {
 // the raised reference and bring O to it. The products are written in place
 // (tied operands) so the accumulators keep their registers.
 template <int J>
-__device__ __forceinline__ void v_settle(VState& st, int l) {
-  const int* fl = flagbuf<J>();
-  const int any = __builtin_amdgcn_readfirstlane(fl[0] | fl[1] | fl[2] | fl[3]);
+__device__ __forceinline__ void v_settle(VState& st, int any, int l) {
   if (any != 0) {
     lds_barrier();
 #pragma unroll
@@ -371,20 +373,24 @@ __device__ __forceinline__ void v_settle(VState& st, int l) {
 }
 
 // The data movement of iteration i: the gather source of tile i+2, the mask
-// of tile i+1 (published for the score waves), the ids of tile i+5.
-__device__ __forceinline__ void v_ids(VState& st, const Ctx& cx, int i, int q4, int l) {
-  const int2 id = lane_ids_of(i + 2, i + 1, l);
+// of tile i+1 (published for the score waves), the ids of tile i+5. Returns
+// the redo flags of tile i-1 (parity J), read in the same LDS round trip.
+template <int J>
+__device__ __forceinline__ int v_ids(VState& st, const Ctx& cx, int i, int q4, int l) {
+  const int4 fl = *reinterpret_cast<const int4*>(flagbuf<J>());
+  const int2 id = read_ids(i + 2, 8 * q4 + (l >> 3), i + 1, l & 31);
   st.gsrc = gather_src(cx.kvb, cx.kst, cx.L, id.x, q4, l);
   const uint32_t m = tile_mask(id.y, cx.topk, cx.L, i + 1, l);
   if (q4 == 0 && l == 0) g_mask[(i + 1) & 1] = m;
   __builtin_amdgcn_sched_barrier(0);
   ids_issue(cx.tix, cx.topk, i + 5, l);
   __builtin_amdgcn_sched_barrier(0);
+  return __builtin_amdgcn_readfirstlane(fl.x | fl.y | fl.z | fl.w);
 }
 
 // O^T[dv 128q4 + 32dt + (0..31)][heads 32hb + (0..31)] += V^T P^T over the
 // tile of parity J; with GATHER, the 9 blocks of the tile being loaded are
-// issued between the first matrix-core operations
+// issued between the matrix-core operations
 template <int J, bool GATHER>
 __device__ __forceinline__ void v_accumulate(VState& st, int q4, int l, uint4* gdst) {
   // Opaque copy of the lane id: the fragment addresses derived from it are
@@ -428,7 +434,8 @@ __device__ __forceinline__ void v_accumulate(VState& st, int q4, int l, uint4* g
     for (int hb = 0; hb < 2; ++hb) {
       st.o[2 * dt + hb] = mfma32(as_bf16x8(vf[x]), pb[hb][ks], st.o[2 * dt + hb]);
       if constexpr (GATHER) {
-        if (2 * x + hb < NBLK) gather_issue(st.gsrc, gdst, q4, 2 * x + hb);
+        if (hb == 0) gather_issue(st.gsrc, gdst, q4, x);
+        else if (x == 7) gather_issue(st.gsrc, gdst, q4, 8);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -440,8 +447,8 @@ __device__ __forceinline__ void v_accumulate(VState& st, int q4, int l, uint4* g
 template <int I, bool FIRST>
 __device__ __forceinline__ void v_iter(VState& st, const Ctx& cx, int i, int l) {
   const int q4 = cx.w - 4;
-  if constexpr (!FIRST) v_settle<I + 3>(st, l);
-  v_ids(st, cx, i, q4, l);
+  const int any = v_ids<I + 3>(st, cx, i, q4, l);
+  if constexpr (!FIRST) v_settle<I + 3>(st, any, l);
   if constexpr (FIRST) {
 #pragma unroll
     for (int ln = 0; ln < NBLK; ++ln) gather_issue(st.gsrc, tbuf<I + 2>(), q4, ln);
@@ -542,8 +549,9 @@ void mla_attn_kernel(const uint16_t* __restrict__ q, Str3 qs, const uint16_t* __
     st.ro[0] = st.ro[1] = -INFINITY;
     __builtin_amdgcn_s_waitcnt(0x0070);  // the ids of tiles 0..4 have arrived
     {
-      const int2 id = lane_ids_of(0, 1, l);
-      const uint32_t m0 = tile_mask(id.x, topk, L, 0, l);
+      const int2 id = read_ids(0, 8 * q4 + (l >> 3), 1, 8 * q4 + (l >> 3));
+      const int2 idm = read_ids(0, l & 31, 0, l & 31);
+      const uint32_t m0 = tile_mask(idm.x, topk, L, 0, l);
       if (q4 == 0 && l == 0) g_mask[0] = m0;
       const uint16_t* s0 = gather_src(cx.kvb, cx.kst, L, id.x, q4, l);
 #pragma unroll
@@ -566,7 +574,10 @@ void mla_attn_kernel(const uint16_t* __restrict__ q, Str3 qs, const uint16_t* __
     v_iter<2, false>(st, cx, i + 1, l);
     v_iter<3, false>(st, cx, i + 2, l);
     // the last tile (nt4-1, parity 3)
-    v_settle<3>(st, l);
+    {
+      const int* fl = flagbuf<3>();
+      v_settle<3>(st, __builtin_amdgcn_readfirstlane(fl[0] | fl[1] | fl[2] | fl[3]), l);
+    }
     v_accumulate<3, false>(st, q4, l, nullptr);
     __builtin_amdgcn_s_waitcnt(0x0070);  // drain the gathers past the end
     __syncthreads();
