@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
+    ap.add_argument("--write-traffic", default="",
+                    help="only summarise rocprofv3 byte counters found under this folder "
+                         "(fetch/, write/, cfetch/, cwrite/) into the traffic record")
     return ap.parse_args()
 
 
@@ -119,6 +122,69 @@ def measured_traffic():
     if rec.get("source_sha256") != kernel_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_mla_64k_traffic.json")
+TRAFFIC_PASSES = {
+    "fetch": "FETCH_SIZE", "write": "WRITE_SIZE", "cfetch": "FETCH_SIZE", "cwrite": "WRITE_SIZE"}
+
+
+def counter_rows(folder, counter):
+    """(kernel name, value) of every dispatch in a rocprofv3 counter csv."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter csv under {folder}")
+    rows = []
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def write_traffic(folder, copy_bytes=1 << 30):
+    """Traffic record of the MLA attention kernel from four counter passes:
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of one bench step, and the
+    same counters over a plain copy of `copy_bytes`, whose known size gives
+    the factor from counter units to bytes."""
+    def one(sub, pick):
+        rows = [v for name, v in counter_rows(os.path.join(folder, sub), TRAFFIC_PASSES[sub])
+                if pick(name)]
+        if not rows:
+            raise SystemExit(f"no matching dispatch in {sub}")
+        return rows
+    attn = lambda n: "mla_attn_kernel" in n
+    copy = lambda n: "copyBuffer" in n or ("copy" in n.lower() and "Fill" not in n)
+    f_kib = one("fetch", attn)
+    w_kib = one("write", attn)
+    cf = max(one("cfetch", copy))
+    cw = max(one("cwrite", copy))
+    fs, ws = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    fk, wk = sum(f_kib) / len(f_kib), sum(w_kib) / len(w_kib)
+    rec = {
+        "kernel": "hisa::mla::mla_attn_kernel", "workload": "prefill_64k_mla",
+        "source_file": "long_context_indexer_block_amd/csrc/attention_mla.hip",
+        "source_sha256": kernel_source_hash(),
+        "fetch_size_kib": fk, "write_size_kib": wk, "copy_probe_bytes": copy_bytes,
+        "copy_fetch_size_kib": cf, "copy_write_size_kib": cw,
+        "fetch_scale": fs, "write_scale": ws,
+        "hbm_bytes_per_launch": int(round(fk * 1024 * fs + wk * 1024 * ws)),
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch -o run -- "
+            "python3 bench.py --no-cpu --no-flat --steps 1 --warmup 0",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write -o run -- "
+            "python3 bench.py --no-cpu --no-flat --steps 1 --warmup 0",
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/cfetch -o run -- "
+            f"python3 bench.py --copy-probe {copy_bytes}",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/cwrite -o run -- "
+            f"python3 bench.py --copy-probe {copy_bytes}",
+            "python3 bench.py --write-traffic <dir>"],
+    }
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
 
 
 def copy_probe(nbytes):
@@ -314,6 +380,9 @@ def bench_hils(w, a, inp):
 
 def main():
     a = parse()
+    if a.write_traffic:
+        write_traffic(a.write_traffic)
+        return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the path has no "
               "multi-GPU form in this build", file=sys.stderr)
