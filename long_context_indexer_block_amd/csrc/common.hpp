@@ -76,6 +76,49 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return v;
 }
 
+// The same through the VALU's data-parallel lane moves (DPP): shifts within
+// 16-lane rows, then the row broadcasts of lanes 15 and 31. No LDS traffic;
+// the result of a reduction is complete in lane 63.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t old, uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      static_cast<int>(old), static_cast<int>(v), CTRL, ROWMASK, 0xf, false));
+}
+// inclusive prefix sum across the 64 lanes
+__device__ __forceinline__ uint32_t wave_scan_dpp(uint32_t v) {
+  v += dpp_move<0x111, 0xf>(0u, v);  // row_shr:1
+  v += dpp_move<0x112, 0xf>(0u, v);  // row_shr:2
+  v += dpp_move<0x114, 0xf>(0u, v);  // row_shr:4
+  v += dpp_move<0x118, 0xf>(0u, v);  // row_shr:8
+  v += dpp_move<0x142, 0xa>(0u, v);  // row_bcast:15 into rows 1, 3
+  v += dpp_move<0x143, 0xc>(0u, v);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_sum_dpp(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wave_scan_dpp(v)), 63));
+}
+// maximum / minimum across the 64 lanes (NaN lanes are ignored, as fmaxf does)
+template <bool MAX>
+__device__ __forceinline__ float wave_ext_dpp(float x) {
+  auto step = [&](uint32_t moved) {
+    const float o = __uint_as_float(moved);
+    x = MAX ? fmaxf(x, o) : fminf(x, o);
+  };
+  step(dpp_move<0x111, 0xf>(__float_as_uint(x), __float_as_uint(x)));
+  step(dpp_move<0x112, 0xf>(__float_as_uint(x), __float_as_uint(x)));
+  step(dpp_move<0x114, 0xf>(__float_as_uint(x), __float_as_uint(x)));
+  step(dpp_move<0x118, 0xf>(__float_as_uint(x), __float_as_uint(x)));
+  step(dpp_move<0x142, 0xa>(__float_as_uint(x), __float_as_uint(x)));
+  step(dpp_move<0x143, 0xc>(__float_as_uint(x), __float_as_uint(x)));
+  return __uint_as_float(
+      static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(__float_as_uint(x)), 63)));
+}
+// number of set bits of `mask` in the lanes below this one
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+}
+
 // Block-wide reductions over NT threads; `red` is LDS scratch of >= NT/64
 // words. Every thread of the block must call them (they synchronise).
 template <int NT>

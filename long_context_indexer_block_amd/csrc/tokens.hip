@@ -306,6 +306,148 @@ __global__ __launch_bounds__(256) void token_topk_kernel(
   }
 }
 
+// The same selection with the candidates laid out by rows: one workgroup of
+// 4 waves per query, wave w holding rows RW*w .. RW*w+RW-1, lane l position
+// 64r + l of row r. Each row is one slot's 64 consecutive tokens (B is a
+// multiple of 64), so the slot's block id is uniform per row and the loads
+// are coalesced. Candidates that are not valid (empty slot, token after the
+// query) are held as NaN, which no comparison keeps. The threshold search is
+// the shared one; the compaction ranks each row with ballots and takes the
+// waves' offsets from one scan of their (kept, tied) counts.
+// row r of a candidate buffer (NaN past the last row); the loads are issued
+// together, before any of them is used
+__device__ __forceinline__ float r_load(const float* row, int r, int nrows, int l) {
+  return r < nrows ? row[r * 64 + l] : __uint_as_float(0x7fc00000u);
+}
+template <int RW>
+__global__ __launch_bounds__(256) void token_topk_rows_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ block_idx,
+    const int32_t* __restrict__ q_pos, int m, int B, int k, int L, int32_t* __restrict__ token_idx,
+    float* __restrict__ token_scores) {
+  constexpr int NT = 256, NB = 2048;
+  __shared__ SelectLds<NT, NB> sh;
+  __shared__ uint32_t wcnt[2][4];
+  extern __shared__ uint4 stage[];  // k ids, then k scores when asked for
+  const int64_t qi = blockIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  const int t = min(max(q_pos[qi], 0), L - 1);
+  const int nblk = (L + B - 1) / B;
+  const int lrpb = __builtin_ctz(B >> 6);  // log2 of the rows per slot (B = 64, 128, 256)
+  const int nrows = (m * B) >> 6;
+  const float* row = scores + qi * static_cast<int64_t>(m) * B;
+  const float qnan = __uint_as_float(0x7fc00000u);
+  // the slots' block ids, one per lane (m <= 128), read by row with readlane;
+  // a slot that is empty or past the end of the keys gets -1
+  int cv0 = -1, cv1 = -1;
+  if (l < m) cv0 = block_idx[qi * m + l];
+  if (64 + l < m) cv1 = block_idx[qi * m + 64 + l];
+  cv0 = cv0 >= 0 && cv0 < nblk ? cv0 : -1;
+  cv1 = cv1 >= 0 && cv1 < nblk ? cv1 : -1;
+  auto slot_block = [&](int sl) {
+    return __builtin_amdgcn_readlane(sl < 64 ? cv0 : cv1, sl & 63);
+  };
+  float v[RW];
+#pragma unroll
+  for (int i = 0; i < RW; ++i) v[i] = r_load(row, RW * wv + i, nrows, l);
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    const int r = RW * wv + i;
+    if (r < nrows) {
+      const int sl = r >> lrpb;
+      const int c = slot_block(sl);
+      const int j = c * B + (r & ((1 << lrpb) - 1)) * 64 + l;
+      if (c < 0 || j > t) v[i] = qnan;
+    }
+  }
+  auto get = [&](int, int i, float& x) -> bool {
+    x = v[i];
+    return x == x;
+  };
+  const Threshold th = select_threshold<NT, RW, NB>(get, 1, k, sh);
+  // ---- compaction: this wave's counts, then the waves before it; the kept
+  // ids (and scores) are ranked into LDS and written out with 16-byte stores
+  const uint32_t need = static_cast<uint32_t>(th.need);
+  uint32_t gtw = 0, eqw = 0;
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    gtw += static_cast<uint32_t>(__popcll(__ballot(v[i] > th.T)));
+    eqw += static_cast<uint32_t>(__popcll(__ballot(v[i] == th.T)));
+  }
+  if (l == 0) {
+    wcnt[0][wv] = gtw;
+    wcnt[1][wv] = eqw;
+  }
+  __syncthreads();
+  uint32_t gtb = 0, ties = 0, gta = 0, tia = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    gtb += u < wv ? wcnt[0][u] : 0u;
+    ties += u < wv ? wcnt[1][u] : 0u;
+    gta += wcnt[0][u];
+    tia += wcnt[1][u];
+  }
+  const uint32_t kept_all = gta + min(tia, need);
+  uint32_t kept = gtb + min(ties, need);
+  int32_t* sid = reinterpret_cast<int32_t*>(stage);
+  float* ssc = token_scores ? reinterpret_cast<float*>(stage) + k : nullptr;
+  uint32_t kept0 = kept, ties0 = ties;
+  // the masks of the counting pass are recomputed, not kept in scalar registers
+#pragma unroll
+  for (int i = 0; i < RW; ++i) asm volatile("" : "+v"(v[i]));
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    const int r = RW * wv + i;
+    const uint64_t em = __ballot(v[i] == th.T);
+    const bool keep = v[i] > th.T || (v[i] == th.T && ties + lanes_below(em) < need);
+    const uint64_t km = __ballot(keep);
+    const int id = slot_block(r >> lrpb) * B + (r & ((1 << lrpb) - 1)) * 64 + l;
+    if (keep) sid[kept + lanes_below(km)] = id;
+    ties += static_cast<uint32_t>(__popcll(em));
+    kept += static_cast<uint32_t>(__popcll(km));
+  }
+  if (ssc) {
+    // the same ranks for the scores
+#pragma unroll
+    for (int i = 0; i < RW; ++i) asm volatile("" : "+v"(v[i]));
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const uint64_t em = __ballot(v[i] == th.T);
+      const bool keep = v[i] > th.T || (v[i] == th.T && ties0 + lanes_below(em) < need);
+      const uint64_t km = __ballot(keep);
+      if (keep) ssc[kept0 + lanes_below(km)] = v[i];
+      ties0 += static_cast<uint32_t>(__popcll(em));
+      kept0 += static_cast<uint32_t>(__popcll(km));
+    }
+  }
+  __syncthreads();
+  int32_t* oi = token_idx + qi * k;
+  float* os = token_scores ? token_scores + qi * k : nullptr;
+  if ((k & 3) == 0) {
+    for (int i = 4 * static_cast<int>(threadIdx.x); i < k; i += 4 * NT) {
+      int4 o;
+      o.x = i + 0 < static_cast<int>(kept_all) ? sid[i + 0] : -1;
+      o.y = i + 1 < static_cast<int>(kept_all) ? sid[i + 1] : -1;
+      o.z = i + 2 < static_cast<int>(kept_all) ? sid[i + 2] : -1;
+      o.w = i + 3 < static_cast<int>(kept_all) ? sid[i + 3] : -1;
+      *reinterpret_cast<int4*>(oi + i) = o;
+      if (os) {
+        float4 f;
+        f.x = i + 0 < static_cast<int>(kept_all) ? ssc[i + 0] : qnan;
+        f.y = i + 1 < static_cast<int>(kept_all) ? ssc[i + 1] : qnan;
+        f.z = i + 2 < static_cast<int>(kept_all) ? ssc[i + 2] : qnan;
+        f.w = i + 3 < static_cast<int>(kept_all) ? ssc[i + 3] : qnan;
+        *reinterpret_cast<float4*>(os + i) = f;
+      }
+    }
+  } else {
+    for (int i = static_cast<int>(threadIdx.x); i < k; i += NT) {
+      oi[i] = i < static_cast<int>(kept_all) ? sid[i] : -1;
+      if (os) os[i] = i < static_cast<int>(kept_all) ? ssc[i] : qnan;
+    }
+  }
+}
+
 hipError_t launch_token_select(const uint16_t* qidx, Str3 qs, const uint16_t* kidx, Str3 ks,
                               const int32_t* q_pos, const int32_t* block_idx, int batch, int nq,
                               int L, int d, int B, int m, int k, int32_t* token_idx,
@@ -349,6 +491,23 @@ hipError_t launch_token_select(const uint16_t* qidx, Str3 qs, const uint16_t* ki
     if (B == 64) HISA_TS(128, 64); else if (B == 128) HISA_TS(128, 128); else HISA_TS(128, 256);
   }
 #undef HISA_TS
+  const int64_t nq_total = static_cast<int64_t>(batch) * nq;
+  const size_t stage_bytes = static_cast<size_t>(k) * 4 * (token_scores ? 2 : 1);
+  if (B % 64 == 0 && m * B <= 8192 && stage_bytes <= 65536) {
+    const int rw = (m * B / 64 + 3) / 4;  // rows per wave
+    const dim3 gr(static_cast<unsigned>(nq_total));
+#define HISA_TR(R_)                                                                           \
+  hipLaunchKernelGGL((token_topk_rows_kernel<R_>), gr, dim3(256), stage_bytes, s, w.scores,    \
+                     block_idx,                                                               \
+                     q_pos, m, B, k, L, token_idx, token_scores)
+    if (rw <= 2) HISA_TR(2);
+    else if (rw <= 4) HISA_TR(4);
+    else if (rw <= 8) HISA_TR(8);
+    else if (rw <= 16) HISA_TR(16);
+    else HISA_TR(32);
+#undef HISA_TR
+    return hipGetLastError();
+  }
   const int items = (m * B + 255) / 256;
   dim3 g(static_cast<unsigned>(static_cast<size_t>(batch) * nq));
 #define HISA_TK(I_)                                                                          \

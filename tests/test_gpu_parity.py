@@ -40,6 +40,10 @@ SMALL = [
     _mk("mla_unit", L=640, B=64, m=3, k=160, d_idx=64, Hq=64, Hkv=1, Dk=576, Dv=512, mla=True,
         sigma=1.0),
     _mk("k1_decode", kind="decode", batch=3, L=3000, B=128, m=6, k=1, d_idx=128, Hq=16, Hkv=1),
+    # an odd k (ids written one by one), and more than 8192 candidates per
+    # query (the block-parallel select instead of the row-parallel one)
+    _mk("odd_k", L=1500, B=128, m=5, k=77, d_idx=64, Hq=2, Hkv=1),
+    _mk("wide_10240", L=12288, nq=48, B=256, m=40, k=500, d_idx=64, Hq=1, Hkv=1),
 ]
 
 
