@@ -39,6 +39,10 @@
 // tile maximum (rescaling the partial sums and O). Numerators far below R
 // underflow to zero, which is exact to fp32 since R never exceeds the true
 // maximum. With kRedo = 64 the fp32 sums stay below 2^64 * 2^14 per head.
+//
+// The last two iterations gather nothing (there is no tile past the end),
+// and the value waves store the normalised O straight from registers, so a
+// workgroup's end overlaps little with the start of the next one on its CU.
 #include "common.hpp"
 #include "internal.h"
 
@@ -444,7 +448,7 @@ __device__ __forceinline__ void v_accumulate(VState& st, int q4, int l, uint4* g
 
 // Value wave, iteration i: settle tile i-1, the data movement, O += P(i-1)
 // V(i-1) with the gathers of tile i+2 interleaved, barrier.
-template <int I, bool FIRST>
+template <int I, bool FIRST, bool GATHER = true>
 __device__ __forceinline__ void v_iter(VState& st, const Ctx& cx, int i, int l) {
   const int q4 = cx.w - 4;
   const int any = v_ids<I + 3>(st, cx, i, q4, l);
@@ -460,11 +464,13 @@ __device__ __forceinline__ void v_iter(VState& st, const Ctx& cx, int i, int l) 
       st.ro[hb] = fmaxf(g_mx[0][h], g_mx[1][h]);
     }
   } else {
-    v_accumulate<I + 3, true>(st, q4, l, tbuf<I + 2>());
+    v_accumulate<I + 3, GATHER>(st, q4, l, tbuf<I + 2>());
   }
-  // tile i+1 is complete once at most this iteration's 10 loads (the ids of
-  // tile i+5 and the 9 gather blocks of tile i+2) are outstanding
-  __builtin_amdgcn_s_waitcnt(0x007A);  // vmcnt(10) lgkmcnt(0)
+  // tile i+1 is complete once at most this iteration's loads (the ids of
+  // tile i+5 and, but in the last two iterations, the 9 gather blocks of
+  // tile i+2) are outstanding
+  if constexpr (GATHER) __builtin_amdgcn_s_waitcnt(0x007A);  // vmcnt(10) lgkmcnt(0)
+  else __builtin_amdgcn_s_waitcnt(0x0071);                    // vmcnt(1) lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
 }
 
@@ -533,8 +539,6 @@ void mla_attn_kernel(const uint16_t* __restrict__ q, Str3 qs, const uint16_t* __
       lsum_x[tt * H + 32 * hh + 16 + (l & 15)] = l1;
     }
     __syncthreads();
-    // (the value waves normalise and stage O here)
-    __syncthreads();
   } else {
     // ================================================= value waves
     const int q4 = w - 4;
@@ -571,51 +575,50 @@ void mla_attn_kernel(const uint16_t* __restrict__ q, Str3 qs, const uint16_t* __
       v_iter<0, false>(st, cx, i + 3, l);
     }
     v_iter<1, false>(st, cx, i, l);
-    v_iter<2, false>(st, cx, i + 1, l);
-    v_iter<3, false>(st, cx, i + 2, l);
+    v_iter<2, false, false>(st, cx, i + 1, l);  // tiles i+3 = nt4 and nt4+1 do not exist
+    v_iter<3, false, false>(st, cx, i + 2, l);
     // the last tile (nt4-1, parity 3)
     {
       const int* fl = flagbuf<3>();
       v_settle<3>(st, __builtin_amdgcn_readfirstlane(fl[0] | fl[1] | fl[2] | fl[3]), l);
     }
     v_accumulate<3, false>(st, q4, l, nullptr);
-    __builtin_amdgcn_s_waitcnt(0x0070);  // drain the gathers past the end
+    __builtin_amdgcn_s_waitcnt(0x0070);  // the ids loaded past the end
     __syncthreads();
     // (the score waves write the row sums here)
     __syncthreads();
-    // ---- normalise and stage O as [head][512] bf16: heads 0..31 in tile
-    // buffer 0, 32..63 in tile buffer 1
+    // ---- normalise O and store it from registers. Lane l holds head
+    // 32hb + l%32 and, per 32-column block, the columns 8i + 4(l/32) + (0..3);
+    // one swap across the lane halves gives every lane 8 consecutive columns.
+    uint16_t* orow = out + b * os.b + qi * os.t + g * H * os.h;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       const int h = 32 * hb + (l & 31);
       const float ltot = lsum_x[h] + lsum_x[H + h];
       const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
-      uint16_t* ost = reinterpret_cast<uint16_t*>(hb ? g_t1 : g_t0) + (l & 31) * DV;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const int d = 128 * q4 + 32 * dt + 8 * qq + 4 * (l >> 5);
-          const f32x16& o = st.o[2 * dt + hb];
-          *reinterpret_cast<uint2*>(ost + d) =
-              make_uint2(pack_bf16x2(o[4 * qq + 0] * inv, o[4 * qq + 1] * inv),
-                         pack_bf16x2(o[4 * qq + 2] * inv, o[4 * qq + 3] * inv));
-        }
       if (lse != nullptr && q4 == 0 && (l >> 5) == 0)
         lse[qrow * (static_cast<int64_t>(H) * Hkv) + g * H + h] =
             ltot > 0.0f ? (st.ro[hb] + log2f(ltot)) * 0.69314718055994530942f : -INFINITY;
-    }
-    __syncthreads();
-  }
-  // ---- all waves: coalesced store of the staged rows
-  uint16_t* ob = out + b * os.b + qi * os.t + g * H * os.h;
+      uint16_t* op = orow + static_cast<int64_t>(h) * os.h + 128 * q4 + 8 * ((l >> 5) ^ 1);
 #pragma unroll
-  for (int j = 0; j < (H * DV / 8) / 512; ++j) {
-    const int u = tid + 512 * j;
-    const int hr = u / (DV / 8), c = u % (DV / 8);
-    const uint16_t* src = reinterpret_cast<const uint16_t*>(hr < 32 ? g_t0 : g_t1);
-    *reinterpret_cast<uint4*>(ob + hr * os.h + 8 * c) =
-        *reinterpret_cast<const uint4*>(src + (hr & 31) * DV + 8 * c);
+      for (int dt = 0; dt < 4; ++dt) {
+        const f32x16& o = st.o[2 * dt + hb];
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          // quads 2pr (columns 16pr + 4(l/32) + (0..3)) and 2pr+1 (+8)
+          const int e0 = 8 * pr, e1 = 8 * pr + 4;
+          const uint32_t x0 = pack2(o[e1 + 0] * inv, o[e1 + 1] * inv);
+          const uint32_t x1 = pack2(o[e1 + 2] * inv, o[e1 + 3] * inv);
+          const uint32_t y0 = pack2(o[e0 + 0] * inv, o[e0 + 1] * inv);
+          const uint32_t y1 = pack2(o[e0 + 2] * inv, o[e0 + 3] * inv);
+          const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+          // lanes < 32: columns 16pr + 8 .. +15; lanes >= 32: 16pr + 0 .. +7
+          *reinterpret_cast<uint4*>(op + 32 * dt + 16 * pr) =
+              make_uint4(s0[0], s1[0], s0[1], s1[1]);
+        }
+      }
+    }
   }
 }
 
