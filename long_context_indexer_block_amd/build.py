@@ -18,8 +18,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhisa.so")
 ARCH = "gfx950"
 
-SOURCES = ["indexer.hip", "tokens.hip", "attention.hip", "attention_mla.hip", "hils.hip",
-           "capi.cpp"]
+SOURCES = ["indexer.hip", "tokens.hip", "attention.hip", "attention_mla.hip", "attention_d128.hip",
+           "hils.hip", "capi.cpp"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -208,6 +208,9 @@ hipError_t launch_sparse_attn(const uint16_t* q, Str3 qs, const uint16_t* k, Str
                                          topk, scale, out, os, lse, s)
   if (Dk == 576 && alias && G == 64)
     return launch_mla_attn(q, qs, k, ks, batch, nq, L, Hkv, token_idx, topk, scale, out, os, lse, s);
+  if (Dk == 128 && Dv == 128 && G <= 16)
+    return launch_attn_d128(q, qs, k, ks, v, vs, batch, nq, L, Hkv, G, token_idx, topk, scale, out,
+                            os, lse, s);
   if (Dk == 576) {
     if (alias) {
       if (G <= 16) HISA_ATT(16, 576, 512, true);

@@ -1,0 +1,323 @@
+// Sparse attention over the selected tokens for head width 128 (Dk = Dv =
+// 128) and at most 16 query heads per kv head: the MQA prefill (16 heads over
+// one kv head), the decode batch and the small prefill (HISA explainer 1.1:
+// attention over the selected tokens only; HISA news article: the downstream
+// attention is unchanged).
+//
+// One wave per (sequence, query, kv head), two independent waves per
+// workgroup, no workgroup barrier. The kept tokens stream through the wave's
+// own LDS ring of three 16-token tiles (K and V, 4 KB each), gathered
+// HBM/L2 -> LDS with 16-byte direct loads two tiles ahead; token ids take
+// the same path into a ring of their own, so the loop issues no other global
+// load and each load-counter wait covers exactly the loads it names.
+//
+// Per tile: S^T = K Q^T on 16x16x32 bf16 MFMA (K fragments from LDS, the
+// group's Q rows in registers). Its accumulator holds, in lane l, head l%16
+// and tokens 4(l/16)..+3, which is exactly the A operand of a 16x16x16 MFMA,
+// so the numerators P feed O += P V without passing through LDS; V^T
+// fragments come from the row-major V tile through ds_read_tr16_b64.
+//
+// Softmax reference: R per head is the maximum over the query's first tile's
+// valid tokens (base-2 logits, scale folded in); a later tile whose maximum
+// exceeds R by more than kRaise raises R to it, rescaling the row sums and O
+// (rare). Numerators far below R underflow to zero, exact to fp32 since R
+// never exceeds the true maximum; no numerator exceeds 2^64.
+#include "common.hpp"
+#include "internal.h"
+
+namespace hisa {
+namespace d128 {
+
+constexpr int D = 128;
+constexpr int NT = 16;             // tokens per tile
+constexpr int TCH = NT * D / 8;    // 16-byte chunks per K or V tile (256)
+constexpr int WAVES = 2;           // independent waves per workgroup
+constexpr float kRaise = 64.0f;
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(1))) void* glb_ptr;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short v4s;
+
+// The ring slots are separate objects (indexed by the wave), so a read of
+// one slot is never mistaken for a read of the slot being gathered into.
+__shared__ uint4 g_k0[WAVES][TCH];
+__shared__ uint4 g_k1[WAVES][TCH];
+__shared__ uint4 g_k2[WAVES][TCH];
+__shared__ uint4 g_v0[WAVES][TCH];
+__shared__ uint4 g_v1[WAVES][TCH];
+__shared__ uint4 g_v2[WAVES][TCH];
+__shared__ int g_ids[WAVES][8][64];  // ids of eight tiles (lanes 16..63 repeat)
+
+template <int I>
+__device__ __forceinline__ uint4* kbuf(int w) {
+  if constexpr (I % 3 == 0) return g_k0[w];
+  else if constexpr (I % 3 == 1) return g_k1[w];
+  else return g_k2[w];
+}
+template <int I>
+__device__ __forceinline__ uint4* vbuf(int w) {
+  if constexpr (I % 3 == 0) return g_v0[w];
+  else if constexpr (I % 3 == 1) return g_v1[w];
+  else return g_v2[w];
+}
+
+// Tile layout: row r (a token) holds its 16 chunks of 16 bytes permuted by
+// XOR with swz(r). The LDS serves a 16-byte read 16 lanes at a time (the
+// four lane quads whose quad index has one parity, within each 32-lane half)
+// and a transposing 8-byte read 32 lanes at a time; with this swizzle both
+// the K fragment reads (16 rows at one chunk) and the V^T reads (4 rows x 32
+// bytes per 16 lanes) fall on distinct banks.
+__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) ^ (r & 8); }
+
+__device__ __forceinline__ f32x4 mfma16k16(const v4s& a, const v4s& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v4s tr16(const unsigned char* lds_byte) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)(lds_byte));
+}
+__device__ __forceinline__ float max_x16_x32(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_x16_x32(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float exp2_ratio(float from, float to) {
+  return from == to ? 1.0f : __builtin_amdgcn_exp2f(from - to);
+}
+
+struct Item {
+  const uint16_t* kb;   // K rows of this kv head
+  const uint16_t* vb;   // V rows of this kv head
+  const int32_t* tix;   // this query's token ids
+  int64_t kst, vst;     // row strides (elements)
+  int topk, L, w;
+};
+
+// Ids of tile t into ring slot t % 8: lane p < 16 loads id 4(p%4) + p/4 of
+// the tile, so the four ids a gather lane needs (rows 4u + g, u = 0..3, for
+// its lane group g) sit next to each other. Ids past the list repeat the last
+// one; such tokens are masked.
+__device__ __forceinline__ void ids_issue(const Item& it, int t, int l) {
+  const int p = l & 15;
+  const int j = min(NT * t + 4 * (p & 3) + (p >> 2), it.topk - 1);
+  __builtin_amdgcn_global_load_lds((glb_ptr)(it.tix + j), (lds_ptr)(&g_ids[it.w][t & 7][0]), 4, 0,
+                                   0);
+}
+// The four ids of this lane's gather rows for tile t (landed by an earlier
+// load-counter wait). Written out because the compiler cannot tell the ring
+// slots apart and would otherwise drain every load in flight first.
+__device__ __forceinline__ int4 read_ids(const Item& it, int t, int l) {
+  const uint32_t a =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int*)(&g_ids[it.w][t & 7][4 * (l >> 4)]);
+  int4 v;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(a) : "memory");
+  return v;
+}
+
+// Gather of tile t into K and V slots: instruction u fills rows 4u .. 4u+3,
+// lane l taking row 4u + l/16 and logical chunk (l%16) ^ swz(row), so 16
+// adjacent lanes read one 256-byte row. Returns the tile's valid-token mask
+// (bit r: token r of the tile is in the list and its id is in [0, L)).
+__device__ __forceinline__ uint32_t gather(const Item& it, int t, uint4* kd, uint4* vd, int l) {
+  const int4 ids = read_ids(it, t, l);
+  const int g = l >> 4, p = l & 15;
+  uint32_t mask = 0;
+  const int idv[4] = {ids.x, ids.y, ids.z, ids.w};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = 4 * u + g;
+    const bool ok = NT * t + r < it.topk && static_cast<unsigned>(idv[u]) < static_cast<unsigned>(it.L);
+    const int row = ok ? idv[u] : 0;
+    const int c = p ^ swz(r);
+    __builtin_amdgcn_global_load_lds((glb_ptr)(it.kb + static_cast<int64_t>(row) * it.kst + 8 * c),
+                                     (lds_ptr)(kd + 64 * u), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_ptr)(it.vb + static_cast<int64_t>(row) * it.vst + 8 * c),
+                                     (lds_ptr)(vd + 64 * u), 16, 0, 0);
+    const uint64_t b = __ballot(ok);
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg)
+      mask |= static_cast<uint32_t>((b >> (16 * gg)) & 1u) << (4 * u + gg);
+  }
+  return mask;
+}
+
+struct State {
+  bf16x8 qf[4];      // Q^T fragments: head l%16, k 32s + 8(l/16) .. +8
+  f32x4 o[8];        // O block dvb: dv 16dvb + l%16, heads 4(l/16) + (0..3)
+  float R;           // reference of head l%16 (base 2)
+  float lsum;        // partial row sum of head l%16 over this lane's tokens
+  uint32_t m0, m1;   // valid masks of tiles t and t+1
+};
+
+// Tile t (slot I = t % 3): S^T, the softmax update, O += P V.
+template <int I>
+__device__ __forceinline__ void tile(State& st, const Item& it, int t, float scale_log2, int l) {
+  const int g = l >> 4;
+  // ---- S^T of the tile: lane l gets head l%16, tokens 4g + (0..3)
+  const uint4* kt = kbuf<I>(it.w);
+  const int r = l & 15;
+  f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+  uint4 kf[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) kf[k] = kt[r * 16 + ((4 * k + g) ^ swz(r))];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) s = mfma16(as_bf16x8(kf[k]), st.qf[k], s);
+  float sv[4];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    sv[e] = ((st.m0 >> (4 * g + e)) & 1u) ? s[e] * scale_log2 : -INFINITY;
+    tmax = fmaxf(tmax, sv[e]);
+  }
+  tmax = max_x16_x32(tmax);
+  // ---- reference: set on the first tile, raised when exceeded by far
+  const bool up = t == 0 || tmax > st.R + kRaise;
+  if (__ballot(up) != 0ull) {
+    const float rnew = up ? tmax : st.R;
+    const float a = exp2_ratio(st.R, rnew);
+    st.lsum *= t == 0 ? 0.0f : a;
+    // O rows are heads 4g + e: fetch their factors from the lanes holding them
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float ae = __shfl(a, 4 * g + e, 64);
+#pragma unroll
+      for (int dvb = 0; dvb < 8; ++dvb) st.o[dvb][e] *= (t == 0 ? 1.0f : ae);
+    }
+    st.R = rnew;
+  }
+  const float mneg = st.R == -INFINITY ? 0.0f : -st.R;
+  float p[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(sv[e] + mneg);
+  st.lsum += (p[0] + p[1]) + (p[2] + p[3]);
+  v4s pa;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) pa[e] = static_cast<short>(f32_to_bf16(p[e]));
+  // ---- O += P V: V^T fragment of dv block dvb: lane l (group g, sl = l%16)
+  // addresses row 4g + sl/4, columns 16dvb + 4(sl%4) .. +3 and receives
+  // column 16dvb + sl of rows 4g .. 4g+3
+  const unsigned char* vt = reinterpret_cast<const unsigned char*>(vbuf<I>(it.w));
+  const int sl = l & 15;
+  const int vrow = 4 * g + (sl >> 2);
+  const int vbase = vrow * 256 + 8 * (sl & 1);
+#pragma unroll
+  for (int dvb = 0; dvb < 8; ++dvb) {
+    const int chunk = 2 * dvb + ((sl & 3) >> 1);
+    const v4s vb = tr16(vt + vbase + 16 * (chunk ^ swz(vrow)));
+    st.o[dvb] = mfma16k16(pa, vb, st.o[dvb]);
+  }
+}
+
+// Iteration t: gather tile t+2 (and the ids of tile t+5), then tile t; wait
+// until tile t+1 has landed.
+template <int I>
+__device__ __forceinline__ void iter(State& st, const Item& it, int t, float scale_log2, int l) {
+  const uint32_t m2 = gather(it, t + 2, kbuf<I + 2>(it.w), vbuf<I + 2>(it.w), l);
+  ids_issue(it, t + 5, l);
+  tile<I>(st, it, t, scale_log2, l);
+  st.m0 = st.m1;
+  st.m1 = m2;
+  __builtin_amdgcn_s_waitcnt(0x0079);  // vmcnt(9): all but this iteration's 9 loads
+}
+
+}  // namespace d128
+
+using namespace d128;
+
+__global__ __launch_bounds__(128) void sparse_attn_d128_kernel(
+    const uint16_t* __restrict__ q, Str3 qs, const uint16_t* __restrict__ k, Str3 ks,
+    const uint16_t* __restrict__ v, Str3 vs, int nq, int L, int Hkv, int G,
+    const int32_t* __restrict__ token_idx, int topk, float scale_log2, uint16_t* __restrict__ out,
+    Str3 os, float* __restrict__ lse, int64_t nitems) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * WAVES + w;
+  if (item >= nitems) return;
+  // item = (b * nq + qi) * Hkv + gk
+  const int gk = static_cast<int>(item % Hkv);
+  const int64_t qrow = item / Hkv;
+  const int qi = static_cast<int>(qrow % nq), b = static_cast<int>(qrow / nq);
+  Item it;
+  it.kb = k + b * ks.b + gk * ks.h;
+  it.vb = v + b * vs.b + gk * vs.h;
+  it.kst = ks.t;
+  it.vst = vs.t;
+  it.tix = token_idx + qrow * topk;
+  it.topk = topk;
+  it.L = L;
+  it.w = w;
+  const int ntiles = (topk + NT - 1) / NT;
+  const int nt3 = (ntiles + 2) / 3 * 3;  // tiles processed: a multiple of 3, the extra ones masked
+
+  State st;
+  {
+    // Q^T fragments: head l%16 (zero past the group), k 32s + 8(l/16)
+    const int h = l & 15;
+    const uint16_t* qp = q + b * qs.b + qi * qs.t + (gk * G + h) * qs.h + 8 * (l >> 4);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      st.qf[s] = h < G ? as_bf16x8(*reinterpret_cast<const uint4*>(qp + 32 * s))
+                       : as_bf16x8(make_uint4(0, 0, 0, 0));
+  }
+#pragma unroll
+  for (int d = 0; d < 8; ++d) st.o[d] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  st.R = -INFINITY;
+  st.lsum = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 5; ++t) ids_issue(it, t, l);
+  __builtin_amdgcn_s_waitcnt(0x0070);  // Q and the ids of tiles 0..4
+  st.m0 = gather(it, 0, kbuf<0>(w), vbuf<0>(w), l);
+  st.m1 = gather(it, 1, kbuf<1>(w), vbuf<1>(w), l);
+  __builtin_amdgcn_s_waitcnt(0x0078);  // vmcnt(8): tile 0 has landed
+  int t = 0;
+  for (; t + 3 <= nt3; t += 3) {
+    iter<0>(st, it, t, scale_log2, l);
+    iter<1>(st, it, t + 1, scale_log2, l);
+    iter<2>(st, it, t + 2, scale_log2, l);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0070);  // the loads past the end
+
+  // ---- normalise and store: O rows are heads 4g + e; their row sums and
+  // references sit in the lanes whose column is that head
+  const float ltot = sum_x16_x32(st.lsum);
+  const int g = l >> 4;
+  uint16_t* orow = out + b * os.b + qi * os.t + gk * G * os.h;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int h = 4 * g + e;
+    const float lh = __shfl(ltot, h, 64);
+    const float inv = lh > 0.0f ? 1.0f / lh : 0.0f;
+    if (h < G) {
+#pragma unroll
+      for (int dvb = 0; dvb < 8; ++dvb)
+        orow[h * os.h + 16 * dvb + (l & 15)] = f32_to_bf16(st.o[dvb][e] * inv);
+    }
+  }
+  if (lse != nullptr && l < 16 && l < G)
+    lse[qrow * (static_cast<int64_t>(G) * Hkv) + gk * G + l] =
+        ltot > 0.0f ? (st.R + log2f(ltot)) * 0.69314718055994530942f : -INFINITY;
+}
+
+hipError_t launch_attn_d128(const uint16_t* q, Str3 qs, const uint16_t* k, Str3 ks,
+                            const uint16_t* v, Str3 vs, int batch, int nq, int L, int Hkv, int G,
+                            const int32_t* token_idx, int topk, float scale, uint16_t* out,
+                            Str3 os, float* lse, hipStream_t s) {
+  const int64_t nitems = static_cast<int64_t>(batch) * nq * Hkv;
+  const unsigned blocks = static_cast<unsigned>((nitems + WAVES - 1) / WAVES);
+  hipLaunchKernelGGL(sparse_attn_d128_kernel, dim3(blocks), dim3(64 * WAVES), 0, s, q, qs, k, ks,
+                     v, vs, nq, L, Hkv, G, token_idx, topk, scale * 1.44269504088896340736f, out,
+                     os, lse, nitems);
+  return hipGetLastError();
+}
+
+}  // namespace hisa

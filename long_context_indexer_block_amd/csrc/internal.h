@@ -40,6 +40,10 @@ hipError_t launch_sparse_attn(const uint16_t* q, Str3 qs, const uint16_t* k, Str
                               float scale, uint16_t* out, Str3 os, float* lse, hipStream_t s);
 
 // attention_mla.hip: 64 query heads over one 576-wide latent row (V = first 512 columns)
+hipError_t launch_attn_d128(const uint16_t* q, Str3 qs, const uint16_t* k, Str3 ks,
+                            const uint16_t* v, Str3 vs, int batch, int nq, int L, int Hkv, int G,
+                            const int32_t* token_idx, int topk, float scale, uint16_t* out,
+                            Str3 os, float* lse, hipStream_t s);
 hipError_t launch_mla_attn(const uint16_t* q, Str3 qs, const uint16_t* kv, Str3 ks, int batch,
                            int nq, int L, int Hkv, const int32_t* token_idx, int topk, float scale,
                            uint16_t* out, Str3 os, float* lse, hipStream_t s);
