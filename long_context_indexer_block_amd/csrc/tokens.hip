@@ -20,6 +20,8 @@
 namespace hisa {
 
 constexpr int kTQ = 64;  // pairs per scoring tile
+// keys per thread and per workgroup of the bucket-count scan
+constexpr int kScanPer = 16, kScanChunk = 256 * kScanPer;
 
 struct TokWs {
   uint32_t* cnt;        // [nkeys]
@@ -27,6 +29,7 @@ struct TokWs {
   uint32_t* offs;       // [nkeys]
   uint32_t* tile_off;   // [nkeys]
   uint32_t* total;      // [4]
+  uint32_t* part;       // [2 * chunks of the bucket scan]
   uint32_t* pairs;      // [npairs]
   uint32_t* tiles;      // [max_tiles]
   float* scores;        // [batch*nq*m*B]
@@ -46,6 +49,7 @@ static TokWs carve(void* ws, int batch, int nq, int L, int B, int m, size_t* byt
   w.offs = reinterpret_cast<uint32_t*>(take(nkeys * 4));
   w.tile_off = reinterpret_cast<uint32_t*>(take(nkeys * 4));
   w.total = reinterpret_cast<uint32_t*>(take(16));
+  w.part = reinterpret_cast<uint32_t*>(take(2 * 4 * ((nkeys + kScanChunk - 1) / kScanChunk)));
   w.pairs = reinterpret_cast<uint32_t*>(take(npairs * 4));
   w.tiles = reinterpret_cast<uint32_t*>(take(max_tiles * 4));
   w.scores = reinterpret_cast<float*>(take(npairs * B * 4));
@@ -93,32 +97,111 @@ __global__ __launch_bounds__(256) void count_pairs_kernel(const int32_t* __restr
     if (hist[c] != 0u) atomicAdd(&cb[c], hist[c]);
 }
 
-// One workgroup of 1024 threads scans the bucket counts (pair offsets and
-// tile offsets) in key order.
-__global__ __launch_bounds__(1024) void scan_buckets_kernel(const uint32_t* __restrict__ cnt,
-                                                            int nkeys, uint32_t* __restrict__ offs,
-                                                            uint32_t* __restrict__ tile_off,
-                                                            uint32_t* __restrict__ total) {
-  __shared__ uint32_t red[32];
-  const int per = (nkeys + 1023) / 1024;
-  const int k0 = threadIdx.x * per, k1 = min(nkeys, k0 + per);
+// Exclusive scans of the bucket counts (pair offsets and tile offsets) in
+// key order, in chunks of 4096 keys: thread t of a chunk's workgroup holds
+// keys 16t .. 16t+15, loaded as four 16-byte vectors. With more than one
+// chunk, a first kernel writes each chunk's two sums and the scan kernel adds
+// those of the chunks before its own.
+__device__ __forceinline__ uint32_t tiles_of(uint32_t c) { return (c + kTQ - 1) / kTQ; }
+
+__device__ __forceinline__ void load_counts(const uint32_t* __restrict__ cnt, int nkeys, int k0,
+                                            uint32_t (&c)[kScanPer]) {
+  if (k0 + kScanPer <= nkeys) {
+#pragma unroll
+    for (int j = 0; j < kScanPer / 4; ++j) {
+      const uint4 u = *reinterpret_cast<const uint4*>(cnt + k0 + 4 * j);
+      c[4 * j + 0] = u.x;
+      c[4 * j + 1] = u.y;
+      c[4 * j + 2] = u.z;
+      c[4 * j + 3] = u.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) c[j] = k0 + j < nkeys ? cnt[k0 + j] : 0u;
+  }
+}
+
+__global__ __launch_bounds__(256) void bucket_partials_kernel(const uint32_t* __restrict__ cnt,
+                                                              int nkeys,
+                                                              uint32_t* __restrict__ part) {
+  __shared__ uint32_t red[4];
+  uint32_t c[kScanPer];
+  load_counts(cnt, nkeys, blockIdx.x * kScanChunk + threadIdx.x * kScanPer, c);
   uint32_t sp = 0, st = 0;
-  for (int k = k0; k < k1; ++k) {
-    sp += cnt[k];
-    st += (cnt[k] + kTQ - 1) / kTQ;
+#pragma unroll
+  for (int j = 0; j < kScanPer; ++j) {
+    sp += c[j];
+    st += tiles_of(c[j]);
+  }
+  sp = block_sum<256>(sp, red);
+  st = block_sum<256>(st, red);
+  if (threadIdx.x == 0) {
+    part[2 * blockIdx.x] = sp;
+    part[2 * blockIdx.x + 1] = st;
+  }
+}
+
+// part == nullptr: one chunk only
+__global__ __launch_bounds__(256) void scan_buckets_kernel(const uint32_t* __restrict__ cnt,
+                                                           int nkeys,
+                                                           const uint32_t* __restrict__ part,
+                                                           int nchunks, uint32_t* __restrict__ offs,
+                                                           uint32_t* __restrict__ tile_off,
+                                                           uint32_t* __restrict__ total) {
+  __shared__ uint32_t red[4];
+  const int k0 = blockIdx.x * kScanChunk + threadIdx.x * kScanPer;
+  uint32_t c[kScanPer];
+  load_counts(cnt, nkeys, k0, c);
+  uint32_t bp = 0, bt = 0, ap = 0, at = 0;  // chunks before this one; all chunks
+  if (part) {
+    for (int i = threadIdx.x; i < nchunks; i += 256) {
+      const uint32_t p = part[2 * i], t = part[2 * i + 1];
+      ap += p;
+      at += t;
+      bp += i < static_cast<int>(blockIdx.x) ? p : 0u;
+      bt += i < static_cast<int>(blockIdx.x) ? t : 0u;
+    }
+    bp = block_sum<256>(bp, red);
+    bt = block_sum<256>(bt, red);
+    ap = block_sum<256>(ap, red);
+    at = block_sum<256>(at, red);
+  }
+  uint32_t sp = 0, st = 0;
+#pragma unroll
+  for (int j = 0; j < kScanPer; ++j) {
+    sp += c[j];
+    st += tiles_of(c[j]);
   }
   uint32_t tp, tt;
-  uint32_t ep = block_excl_scan<1024>(sp, tp, red);
-  uint32_t et = block_excl_scan<1024>(st, tt, red);
-  for (int k = k0; k < k1; ++k) {
-    offs[k] = ep;
-    tile_off[k] = et;
-    ep += cnt[k];
-    et += (cnt[k] + kTQ - 1) / kTQ;
+  uint32_t ep = bp + block_excl_scan<256>(sp, tp, red);
+  uint32_t et = bt + block_excl_scan<256>(st, tt, red);
+  uint32_t o[kScanPer], to[kScanPer];
+#pragma unroll
+  for (int j = 0; j < kScanPer; ++j) {
+    o[j] = ep;
+    to[j] = et;
+    ep += c[j];
+    et += tiles_of(c[j]);
   }
-  if (threadIdx.x == 0) {
-    total[0] = tp;
-    total[1] = tt;
+  if (k0 + kScanPer <= nkeys) {
+#pragma unroll
+    for (int j = 0; j < kScanPer / 4; ++j) {
+      *reinterpret_cast<uint4*>(offs + k0 + 4 * j) =
+          make_uint4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]);
+      *reinterpret_cast<uint4*>(tile_off + k0 + 4 * j) =
+          make_uint4(to[4 * j], to[4 * j + 1], to[4 * j + 2], to[4 * j + 3]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j)
+      if (k0 + j < nkeys) {
+        offs[k0 + j] = o[j];
+        tile_off[k0 + j] = to[j];
+      }
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    total[0] = part ? ap : tp;
+    total[1] = part ? at : tt;
   }
 }
 
@@ -307,7 +390,7 @@ __global__ __launch_bounds__(256) void token_topk_kernel(
 }
 
 // The same selection with the candidates laid out by rows: one workgroup of
-// 4 waves per query, wave w holding rows RW*w .. RW*w+RW-1, lane l position
+// W waves per query, wave w holding rows RW*w .. RW*w+RW-1, lane l position
 // 64r + l of row r. Each row is one slot's 64 consecutive tokens (B is a
 // multiple of 64), so the slot's block id is uniform per row and the loads
 // are coalesced. Candidates that are not valid (empty slot, token after the
@@ -319,14 +402,16 @@ __global__ __launch_bounds__(256) void token_topk_kernel(
 __device__ __forceinline__ float r_load(const float* row, int r, int nrows, int l) {
   return r < nrows ? row[r * 64 + l] : __uint_as_float(0x7fc00000u);
 }
-template <int RW>
-__global__ __launch_bounds__(256) void token_topk_rows_kernel(
-    const float* __restrict__ scores, const int32_t* __restrict__ block_idx,
-    const int32_t* __restrict__ q_pos, int m, int B, int k, int L, int32_t* __restrict__ token_idx,
-    float* __restrict__ token_scores) {
-  constexpr int NT = 256, NB = 2048;
+// The register budget allows 5 waves per SIMD: the kernel is latency bound
+// (barriers, LDS atomics), so more resident workgroups hide more of it.
+template <int RW, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(5, 8))) void
+token_topk_rows_kernel(const float* __restrict__ scores, const int32_t* __restrict__ block_idx,
+                       const int32_t* __restrict__ q_pos, int m, int B, int k, int L,
+                       int32_t* __restrict__ token_idx, float* __restrict__ token_scores) {
+  constexpr int NT = 64 * W, NB = 2048;
   __shared__ SelectLds<NT, NB> sh;
-  __shared__ uint32_t wcnt[2][4];
+  __shared__ uint32_t wcnt[2][W];
   extern __shared__ uint4 stage[];  // k ids, then k scores when asked for
   const int64_t qi = blockIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -381,7 +466,7 @@ __global__ __launch_bounds__(256) void token_topk_rows_kernel(
   __syncthreads();
   uint32_t gtb = 0, ties = 0, gta = 0, tia = 0;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < W; ++u) {
     gtb += u < wv ? wcnt[0][u] : 0u;
     ties += u < wv ? wcnt[1][u] : 0u;
     gta += wcnt[0][u];
@@ -448,6 +533,10 @@ __global__ __launch_bounds__(256) void token_topk_rows_kernel(
   }
 }
 
+// below this many queries the row top-k uses kWideW waves per query
+constexpr int64_t kFewQueries = 1024;
+constexpr int kWideW = 16;
+
 hipError_t launch_token_select(const uint16_t* qidx, Str3 qs, const uint16_t* kidx, Str3 ks,
                               const int32_t* q_pos, const int32_t* block_idx, int batch, int nq,
                               int L, int d, int B, int m, int k, int32_t* token_idx,
@@ -471,8 +560,12 @@ hipError_t launch_token_select(const uint16_t* qidx, Str3 qs, const uint16_t* ki
   else
     hipLaunchKernelGGL(count_pairs_direct_kernel, dim3(pg), dim3(256), 0, s, block_idx, nq, m,
                        nblk, npairs, w.cnt);
-  hipLaunchKernelGGL(scan_buckets_kernel, dim3(1), dim3(1024), 0, s, w.cnt, nkeys, w.offs,
-                     w.tile_off, w.total);
+  const int nchunks = (nkeys + kScanChunk - 1) / kScanChunk;
+  if (nchunks > 1)
+    hipLaunchKernelGGL(bucket_partials_kernel, dim3(nchunks), dim3(256), 0, s, w.cnt, nkeys,
+                       w.part);
+  hipLaunchKernelGGL(scan_buckets_kernel, dim3(nchunks), dim3(256), 0, s, w.cnt, nkeys,
+                     nchunks > 1 ? w.part : nullptr, nchunks, w.offs, w.tile_off, w.total);
   if (lds_hist)
     hipLaunchKernelGGL(scatter_pairs_kernel, hg, dim3(256), nblk * 8, s, block_idx, nq, m, nblk,
                        qpw, w.offs, w.cursor, w.pairs);
@@ -494,17 +587,26 @@ hipError_t launch_token_select(const uint16_t* qidx, Str3 qs, const uint16_t* ki
   const int64_t nq_total = static_cast<int64_t>(batch) * nq;
   const size_t stage_bytes = static_cast<size_t>(k) * 4 * (token_scores ? 2 : 1);
   if (B % 64 == 0 && m * B <= 8192 && stage_bytes <= 65536) {
-    const int rw = (m * B / 64 + 3) / 4;  // rows per wave
+    const int nrows = m * B / 64;
     const dim3 gr(static_cast<unsigned>(nq_total));
-#define HISA_TR(R_)                                                                           \
-  hipLaunchKernelGGL((token_topk_rows_kernel<R_>), gr, dim3(256), stage_bytes, s, w.scores,    \
-                     block_idx,                                                               \
-                     q_pos, m, B, k, L, token_idx, token_scores)
-    if (rw <= 2) HISA_TR(2);
-    else if (rw <= 4) HISA_TR(4);
-    else if (rw <= 8) HISA_TR(8);
-    else if (rw <= 16) HISA_TR(16);
-    else HISA_TR(32);
+#define HISA_TR(R_, W_)                                                                        \
+  hipLaunchKernelGGL((token_topk_rows_kernel<R_, W_>), gr, dim3(64 * W_), stage_bytes, s,       \
+                     w.scores, block_idx, q_pos, m, B, k, L, token_idx, token_scores)
+    if (nq_total < kFewQueries) {
+      // few queries (decode): WIDE waves per query, so that the CUs that get a
+      // workgroup hold enough waves to hide the latency of each step
+      const int rw = (nrows + kWideW - 1) / kWideW;  // rows per wave
+      if (rw <= 2) HISA_TR(2, kWideW);
+      else if (rw <= 4) HISA_TR(4, kWideW);
+      else HISA_TR(128 / kWideW, kWideW);
+    } else {
+      const int rw = (nrows + 3) / 4;
+      if (rw <= 2) HISA_TR(2, 4);
+      else if (rw <= 4) HISA_TR(4, 4);
+      else if (rw <= 8) HISA_TR(8, 4);
+      else if (rw <= 16) HISA_TR(16, 4);
+      else HISA_TR(32, 4);
+    }
 #undef HISA_TR
     return hipGetLastError();
   }

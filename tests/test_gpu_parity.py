@@ -44,6 +44,10 @@ SMALL = [
     # query (the block-parallel select instead of the row-parallel one)
     _mk("odd_k", L=1500, B=128, m=5, k=77, d_idx=64, Hq=2, Hkv=1),
     _mk("wide_10240", L=12288, nq=48, B=256, m=40, k=500, d_idx=64, Hq=1, Hkv=1),
+    # 3 x 4687 blocks: the bucket-count scan runs over four chunks of keys,
+    # the last one ragged
+    _mk("many_blocks_decode", kind="decode", batch=3, L=299963, B=64, m=8, k=256, d_idx=64, Hq=4,
+        Hkv=1),
 ]
 
 
