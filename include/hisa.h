@@ -148,12 +148,21 @@ size_t flat_indexer_topk_workspace_bytes(int batch, int nq, int L, int k);
  *   out  bf16 [batch][nq][Hq][Dv]   strides os.
  *   lse  optional fp32 [batch][nq][Hq]: natural-log sum of exp(scale*q.k)
  *        over the kept tokens (-inf for an empty set, whose output is 0).
+ *   workspace  optional device scratch of sparse_attn_fwd_workspace_bytes()
+ *        bytes, 256-byte aligned, contents on entry ignored. With it, few
+ *        (query, kv head) pairs with long token lists (decode) split each list
+ *        over several waves and merge the parts; NULL runs unsplit (same
+ *        result up to fp32 rounding, slower for such shapes). A non-NULL
+ *        workspace that is too small is HISA_ERR_WORKSPACE. The size is 0 when
+ *        the shape never splits.
  * Query head h reads kv head h / (Hq / Hkv). */
 hisa_status_t sparse_attn_fwd(const void* q, hisa_strides_t qs, const void* k, hisa_strides_t ks,
                               const void* v, hisa_strides_t vs, int batch, int nq, int L, int Hq,
                               int Hkv, int Dk, int Dv, const int32_t* token_idx, int topk,
                               float scale, void* out, hisa_strides_t os, float* lse,
-                              hisa_stream_t stream);
+                              void* workspace, size_t workspace_bytes, hisa_stream_t stream);
+size_t sparse_attn_fwd_workspace_bytes(int batch, int nq, int Hq, int Hkv, int Dk, int Dv,
+                                       int topk);
 
 /* Two-level (chunk x token) softmax decode at position t = L - 1 (HiLS
  * chapter, "hierarchical softmax decomposition"; HiLS-7B write-up, "what is

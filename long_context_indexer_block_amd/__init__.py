@@ -46,7 +46,8 @@ _SIGS = {
                                _P]),
     "flat_indexer_topk_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "sparse_attn_fwd": (_I, [_P, Strides, _P, Strides, _P, Strides, _I, _I, _I, _I, _I, _I, _I,
-                             _P, _I, _F, _P, Strides, _P, _P]),
+                             _P, _I, _F, _P, Strides, _P, _P, _S, _P]),
+    "sparse_attn_fwd_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I, _I]),
     "hils_two_level_attn_fwd": (_I, [_P, Strides, _P, Strides, _P, Strides, _P, _P, _I, _I, _I,
                                      _I, _I, _I, _I, _F, _F, _P, Strides, _P]),
 }
@@ -188,9 +189,20 @@ def flat_indexer_topk(qidx, kidx, q_pos, k, token_idx=None, token_scores=None, w
 
 
 # ----------------------------------------------------------------- attention
-def sparse_attn_fwd(q, k, v, token_idx, scale, out=None, lse=None, want_lse=False):
+def sparse_attn_workspace(q, k, v, token_idx):
+    """Workspace for sparse_attn_fwd on these shapes (None when it needs none)."""
+    b, nq, Hq, Dk = q.shape
+    n = lib().sparse_attn_fwd_workspace_bytes(b, nq, Hq, k.shape[2], Dk, v.shape[-1],
+                                              token_idx.shape[-1])
+    return torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+
+
+def sparse_attn_fwd(q, k, v, token_idx, scale, out=None, lse=None, want_lse=False,
+                    workspace="auto"):
     """q [b, nq, Hq, Dk], k [b, L, Hkv, Dk], v [b, L, Hkv, Dv] (may be a view of k),
-    token_idx [b, nq, topk] int32 -> out [b, nq, Hq, Dv] bf16 (, lse [b, nq, Hq])."""
+    token_idx [b, nq, topk] int32 -> out [b, nq, Hq, Dv] bf16 (, lse [b, nq, Hq]).
+    workspace: "auto" allocates what the shape asks for, None runs unsplit, or a
+    uint8 tensor from sparse_attn_workspace()."""
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, torch.bfloat16, nm)
     b, nq, Hq, Dk = q.shape
@@ -201,9 +213,13 @@ def sparse_attn_fwd(q, k, v, token_idx, scale, out=None, lse=None, want_lse=Fals
         out = torch.empty(b, nq, Hq, Dv, dtype=torch.bfloat16, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty(b, nq, Hq, dtype=torch.float32, device=q.device)
+    if isinstance(workspace, str):
+        workspace = sparse_attn_workspace(q, k, v, token_idx)
+    wsb = 0 if workspace is None else workspace.numel()
     _check(lib().sparse_attn_fwd(_ptr(q), _str3(q, "bth"), _ptr(k), _str3(k, "bth"), _ptr(v),
                                  _str3(v, "bth"), b, nq, L, Hq, Hkv, Dk, Dv, _ptr(token_idx), topk,
-                                 float(scale), _ptr(out), _str3(out, "bth"), _ptr(lse), _stream()))
+                                 float(scale), _ptr(out), _str3(out, "bth"), _ptr(lse),
+                                 _ptr(workspace), wsb, _stream()))
     return (out, lse) if want_lse else out
 
 

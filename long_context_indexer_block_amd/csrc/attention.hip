@@ -197,10 +197,19 @@ static hipError_t attn_launch(const uint16_t* q, Str3 qs, const uint16_t* k, Str
   return hipGetLastError();
 }
 
+// Only the head-width-128 kernel uses a workspace (the split of few long
+// token lists).
+size_t sparse_attn_workspace(int batch, int nq, int Hq, int Hkv, int Dk, int Dv, int topk) {
+  const int G = Hq / Hkv;
+  if (Dk == 128 && Dv == 128 && G <= 16) return attn_d128_workspace(batch, nq, Hkv, G, topk);
+  return 0;
+}
+
 hipError_t launch_sparse_attn(const uint16_t* q, Str3 qs, const uint16_t* k, Str3 ks,
                               const uint16_t* v, Str3 vs, int batch, int nq, int L, int Hq,
                               int Hkv, int Dk, int Dv, const int32_t* token_idx, int topk,
-                              float scale, uint16_t* out, Str3 os, float* lse, hipStream_t s) {
+                              float scale, uint16_t* out, Str3 os, float* lse, void* ws,
+                              hipStream_t s) {
   const int G = Hq / Hkv;
   const bool alias = (v == k) && vs.b == ks.b && vs.t == ks.t && vs.h == ks.h;
 #define HISA_ATT(GP_, DK_, DV_, AL_) \
@@ -210,7 +219,7 @@ hipError_t launch_sparse_attn(const uint16_t* q, Str3 qs, const uint16_t* k, Str
     return launch_mla_attn(q, qs, k, ks, batch, nq, L, Hkv, token_idx, topk, scale, out, os, lse, s);
   if (Dk == 128 && Dv == 128 && G <= 16)
     return launch_attn_d128(q, qs, k, ks, v, vs, batch, nq, L, Hkv, G, token_idx, topk, scale, out,
-                            os, lse, s);
+                            os, lse, ws, s);
   if (Dk == 576) {
     if (alias) {
       if (G <= 16) HISA_ATT(16, 576, 512, true);

@@ -22,6 +22,13 @@
 // exceeds R by more than kRaise raises R to it, rescaling the row sums and O
 // (rare). Numerators far below R underflow to zero, exact to fp32 since R
 // never exceeds the true maximum; no numerator exceeds 2^64.
+//
+// Few (query, kv head) pairs (decode) would leave most CUs idle, so their
+// token lists are split: each wave takes a run of tiles and writes its O, R
+// and row sums in fp32, and a second kernel rescales the splits to a common
+// maximum and sums them.
+#include <algorithm>
+
 #include "common.hpp"
 #include "internal.h"
 
@@ -33,6 +40,8 @@ constexpr int NT = 16;             // tokens per tile
 constexpr int TCH = NT * D / 8;    // 16-byte chunks per K or V tile (256)
 constexpr int WAVES = 2;           // independent waves per workgroup
 constexpr float kRaise = 64.0f;
+constexpr int64_t kSplitWaves = 2048;  // split the lists while fewer waves than this
+constexpr int kMinSplitTiles = 4;      // tiles per split, at least
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef __attribute__((address_space(1))) void* glb_ptr;
@@ -239,10 +248,14 @@ __global__ __launch_bounds__(128) void sparse_attn_d128_kernel(
     const uint16_t* __restrict__ q, Str3 qs, const uint16_t* __restrict__ k, Str3 ks,
     const uint16_t* __restrict__ v, Str3 vs, int nq, int L, int Hkv, int G,
     const int32_t* __restrict__ token_idx, int topk, float scale_log2, uint16_t* __restrict__ out,
-    Str3 os, float* __restrict__ lse, int64_t nitems) {
+    Str3 os, float* __restrict__ lse, int64_t nitems, int nsplit, int split_tiles,
+    float* __restrict__ part_o, float2* __restrict__ part_rl) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
-  const int64_t item = static_cast<int64_t>(blockIdx.x) * WAVES + w;
-  if (item >= nitems) return;
+  // x = item * nsplit + split; without a split (part_o null) nsplit is 1
+  const int64_t x = static_cast<int64_t>(blockIdx.x) * WAVES + w;
+  if (x >= nitems * nsplit) return;
+  const int64_t item = x / nsplit;
+  const int tok0 = static_cast<int>(x % nsplit) * split_tiles * NT;
   // item = (b * nq + qi) * Hkv + gk
   const int gk = static_cast<int>(item % Hkv);
   const int64_t qrow = item / Hkv;
@@ -252,11 +265,11 @@ __global__ __launch_bounds__(128) void sparse_attn_d128_kernel(
   it.vb = v + b * vs.b + gk * vs.h;
   it.kst = ks.t;
   it.vst = vs.t;
-  it.tix = token_idx + qrow * topk;
-  it.topk = topk;
+  it.tix = token_idx + qrow * topk + tok0;
+  it.topk = min(topk - tok0, split_tiles * NT);  // >= 1: no split is empty
   it.L = L;
   it.w = w;
-  const int ntiles = (topk + NT - 1) / NT;
+  const int ntiles = (it.topk + NT - 1) / NT;
   const int nt3 = (ntiles + 2) / 3 * 3;  // tiles processed: a multiple of 3, the extra ones masked
 
   State st;
@@ -291,6 +304,20 @@ __global__ __launch_bounds__(128) void sparse_attn_d128_kernel(
   // references sit in the lanes whose column is that head
   const float ltot = sum_x16_x32(st.lsum);
   const int g = l >> 4;
+  if (part_o != nullptr) {
+    // this split's unnormalised O (rows = heads), reference and row sum
+    float* po = part_o + x * (static_cast<int64_t>(G) * D);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int h = 4 * g + e;
+      if (h < G) {
+#pragma unroll
+        for (int dvb = 0; dvb < 8; ++dvb) po[h * D + 16 * dvb + (l & 15)] = st.o[dvb][e];
+      }
+    }
+    if (l < G) part_rl[x * G + l] = make_float2(st.R, ltot);
+    return;
+  }
   uint16_t* orow = out + b * os.b + qi * os.t + gk * G * os.h;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -308,15 +335,89 @@ __global__ __launch_bounds__(128) void sparse_attn_d128_kernel(
         ltot > 0.0f ? (st.R + log2f(ltot)) * 0.69314718055994530942f : -INFINITY;
 }
 
+// The splits of one item, rescaled to their largest reference and summed:
+// workgroup (item, head pair), thread = one output column of one head.
+__global__ __launch_bounds__(256) void attn_d128_combine_kernel(
+    const float* __restrict__ part_o, const float2* __restrict__ part_rl, int nsplit, int nq,
+    int Hkv, int G, uint16_t* __restrict__ out, Str3 os, float* __restrict__ lse) {
+  const int64_t item = blockIdx.x;
+  const int h = 2 * blockIdx.y + (threadIdx.x >> 7);
+  const int c = threadIdx.x & (D - 1);
+  if (h >= G) return;
+  const float2* rl = part_rl + item * nsplit * G + h;
+  const float* po = part_o + (item * nsplit * G + h) * D + c;
+  float M = -INFINITY;
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const float2 a = rl[sp * G];
+    if (a.y > 0.0f) M = fmaxf(M, a.x);
+  }
+  float lt = 0.0f, acc = 0.0f;
+#pragma unroll 4
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const float2 a = rl[sp * G];
+    const float o = po[static_cast<int64_t>(sp) * G * D];
+    if (a.y > 0.0f) {
+      const float f = exp2_ratio(a.x, M);
+      lt += a.y * f;
+      acc += o * f;
+    }
+  }
+  const int gk = static_cast<int>(item % Hkv);
+  const int64_t qrow = item / Hkv;
+  const int qi = static_cast<int>(qrow % nq), b = static_cast<int>(qrow / nq);
+  out[b * os.b + qi * os.t + (gk * G + h) * os.h + c] = f32_to_bf16(lt > 0.0f ? acc / lt : 0.0f);
+  if (lse != nullptr && c == 0)
+    lse[qrow * (static_cast<int64_t>(G) * Hkv) + gk * G + h] =
+        lt > 0.0f ? (M + log2f(lt)) * 0.69314718055994530942f : -INFINITY;
+}
+
+// Splits of each token list: enough waves to occupy the chip, at least
+// kMinSplitTiles tiles each, none empty.
+static int d128_splits(int64_t nitems, int topk, int* split_tiles) {
+  const int ntiles = (topk + NT - 1) / NT;
+  int64_t s = std::min<int64_t>((kSplitWaves + nitems - 1) / nitems, ntiles / kMinSplitTiles);
+  s = std::max<int64_t>(s, 1);
+  const int tps = static_cast<int>((ntiles + s - 1) / s);
+  *split_tiles = tps;
+  return (ntiles + tps - 1) / tps;
+}
+
+size_t attn_d128_workspace(int batch, int nq, int Hkv, int G, int topk) {
+  const int64_t nitems = static_cast<int64_t>(batch) * nq * Hkv;
+  int tps;
+  const int ns = d128_splits(nitems, topk, &tps);
+  if (ns <= 1) return 0;
+  const size_t n = static_cast<size_t>(nitems) * ns * G;
+  return align256(n * D * 4) + align256(n * 8);
+}
+
 hipError_t launch_attn_d128(const uint16_t* q, Str3 qs, const uint16_t* k, Str3 ks,
                             const uint16_t* v, Str3 vs, int batch, int nq, int L, int Hkv, int G,
                             const int32_t* token_idx, int topk, float scale, uint16_t* out,
-                            Str3 os, float* lse, hipStream_t s) {
+                            Str3 os, float* lse, void* ws, hipStream_t s) {
   const int64_t nitems = static_cast<int64_t>(batch) * nq * Hkv;
-  const unsigned blocks = static_cast<unsigned>((nitems + WAVES - 1) / WAVES);
+  int tps;
+  int ns = d128_splits(nitems, topk, &tps);
+  if (ws == nullptr || ns <= 1) {  // one wave per item
+    ns = 1;
+    tps = (topk + NT - 1) / NT;
+  }
+  float* part_o = nullptr;
+  float2* part_rl = nullptr;
+  if (ns > 1) {
+    const size_t n = static_cast<size_t>(nitems) * ns * G;
+    part_o = static_cast<float*>(ws);
+    part_rl = reinterpret_cast<float2*>(static_cast<char*>(ws) + align256(n * D * 4));
+  }
+  const int64_t waves = nitems * ns;
+  const unsigned blocks = static_cast<unsigned>((waves + WAVES - 1) / WAVES);
   hipLaunchKernelGGL(sparse_attn_d128_kernel, dim3(blocks), dim3(64 * WAVES), 0, s, q, qs, k, ks,
                      v, vs, nq, L, Hkv, G, token_idx, topk, scale * 1.44269504088896340736f, out,
-                     os, lse, nitems);
+                     os, lse, nitems, ns, tps, part_o, part_rl);
+  if (ns > 1)
+    hipLaunchKernelGGL(attn_d128_combine_kernel,
+                       dim3(static_cast<unsigned>(nitems), static_cast<unsigned>((G + 1) / 2)),
+                       dim3(256), 0, s, part_o, part_rl, ns, nq, Hkv, G, out, os, lse);
   return hipGetLastError();
 }
 

@@ -197,11 +197,17 @@ hisa_status_t flat_indexer_topk(const void* qidx, hisa_strides_t qs, const void*
                     "flat_indexer_topk");
 }
 
+size_t sparse_attn_fwd_workspace_bytes(int batch, int nq, int Hq, int Hkv, int Dk, int Dv,
+                                       int topk) {
+  if (batch < 1 || nq < 1 || Hq < 1 || Hkv < 1 || topk < 1 || Hq % Hkv != 0) return 0;
+  return hisa::sparse_attn_workspace(batch, nq, Hq, Hkv, Dk, Dv, topk);
+}
+
 hisa_status_t sparse_attn_fwd(const void* q, hisa_strides_t qs, const void* k, hisa_strides_t ks,
                               const void* v, hisa_strides_t vs, int batch, int nq, int L, int Hq,
                               int Hkv, int Dk, int Dv, const int32_t* token_idx, int topk,
                               float scale, void* out, hisa_strides_t os, float* lse,
-                              hisa_stream_t stream) {
+                              void* workspace, size_t workspace_bytes, hisa_stream_t stream) {
   CHECK(q && k && v && token_idx && out, HISA_ERR_NULL, "q, k, v, token_idx and out are required");
   CHECK(batch >= 1 && nq >= 1 && L >= 1 && topk >= 1 && Hq >= 1 && Hkv >= 1, HISA_ERR_SHAPE,
         "sizes must be >= 1");
@@ -216,11 +222,18 @@ hisa_status_t sparse_attn_fwd(const void* q, hisa_strides_t qs, const void* k, h
   if ((st = check_bf16(v, vs, "v")) != HISA_OK) return st;
   CHECK(nonneg(os), HISA_ERR_SHAPE, "out strides must be non-negative");
   CHECK(scale > 0.0f, HISA_ERR_SHAPE, "scale must be positive");
+  if (workspace != nullptr) {
+    CHECK((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, HISA_ERR_WORKSPACE,
+          "workspace must be 256-byte aligned");
+    const size_t need = hisa::sparse_attn_workspace(batch, nq, Hq, Hkv, Dk, Dv, topk);
+    CHECK(workspace_bytes >= need, HISA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu",
+          workspace_bytes, need);
+  }
   return hip_status(hisa::launch_sparse_attn(static_cast<const uint16_t*>(q), s3(qs),
                                              static_cast<const uint16_t*>(k), s3(ks),
                                              static_cast<const uint16_t*>(v), s3(vs), batch, nq,
                                              L, Hq, Hkv, Dk, Dv, token_idx, topk, scale,
-                                             static_cast<uint16_t*>(out), s3(os), lse,
+                                             static_cast<uint16_t*>(out), s3(os), lse, workspace,
                                              static_cast<hipStream_t>(stream)),
                     "sparse_attn_fwd");
 }

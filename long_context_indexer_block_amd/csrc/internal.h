@@ -33,17 +33,24 @@ hipError_t launch_flat_topk(const uint16_t* qidx, Str3 qs, const uint16_t* kidx,
                             const int32_t* q_pos, int batch, int nq, int L, int d, int k,
                             int32_t* token_idx, float* token_scores, void* ws, hipStream_t s);
 
-// attention.hip
+// attention.hip; ws (may be null) holds at least sparse_attn_workspace() bytes
+size_t sparse_attn_workspace(int batch, int nq, int Hq, int Hkv, int Dk, int Dv, int topk);
 hipError_t launch_sparse_attn(const uint16_t* q, Str3 qs, const uint16_t* k, Str3 ks,
                               const uint16_t* v, Str3 vs, int batch, int nq, int L, int Hq,
                               int Hkv, int Dk, int Dv, const int32_t* token_idx, int topk,
-                              float scale, uint16_t* out, Str3 os, float* lse, hipStream_t s);
+                              float scale, uint16_t* out, Str3 os, float* lse, void* ws,
+                              hipStream_t s);
 
-// attention_mla.hip: 64 query heads over one 576-wide latent row (V = first 512 columns)
+// attention_d128.hip: head width 128, at most 16 query heads per kv head;
+// with ws (attn_d128_workspace() bytes, 0 when it does not split) the token
+// lists of few items are split over several waves
+size_t attn_d128_workspace(int batch, int nq, int Hkv, int G, int topk);
 hipError_t launch_attn_d128(const uint16_t* q, Str3 qs, const uint16_t* k, Str3 ks,
                             const uint16_t* v, Str3 vs, int batch, int nq, int L, int Hkv, int G,
                             const int32_t* token_idx, int topk, float scale, uint16_t* out,
-                            Str3 os, float* lse, hipStream_t s);
+                            Str3 os, float* lse, void* ws, hipStream_t s);
+
+// attention_mla.hip: 64 query heads over one 576-wide latent row (V = first 512 columns)
 hipError_t launch_mla_attn(const uint16_t* q, Str3 qs, const uint16_t* kv, Str3 ks, int batch,
                            int nq, int L, int Hkv, const int32_t* token_idx, int topk, float scale,
                            uint16_t* out, Str3 os, float* lse, hipStream_t s);

@@ -12,7 +12,7 @@ import torch
 
 from . import (flat_indexer_topk, flat_indexer_topk_workspace_bytes, hils_two_level_attn_fwd,
                hisa_block_score, hisa_block_summary, hisa_select_blocks, hisa_token_select,
-               hisa_token_select_workspace_bytes, sparse_attn_fwd)
+               hisa_token_select_workspace_bytes, sparse_attn_fwd, sparse_attn_workspace)
 
 
 class HierPipeline:
@@ -36,6 +36,7 @@ class HierPipeline:
         Hq, Dv = q.shape[2], v.shape[-1]
         self.out = torch.empty(b, nq, Hq, Dv, dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty(b, nq, Hq, dtype=torch.float32, device=dev) if want_lse else None
+        self.attn_ws = sparse_attn_workspace(q, k, v, self.token_idx)
 
     def summarize(self):
         hisa_block_summary(self.kidx, self.B, summary=self.summary, split=self.split)
@@ -51,7 +52,7 @@ class HierPipeline:
 
     def attend(self):
         sparse_attn_fwd(self.q, self.k, self.v, self.token_idx, self.scale, out=self.out,
-                        lse=self.lse, want_lse=self.lse is not None)
+                        lse=self.lse, want_lse=self.lse is not None, workspace=self.attn_ws)
 
     def run(self, summarize=True):
         self.index(summarize)
@@ -75,6 +76,7 @@ class FlatPipeline:
         Hq, Dv = q.shape[2], v.shape[-1]
         self.out = torch.empty(b, nq, Hq, Dv, dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty(b, nq, Hq, dtype=torch.float32, device=dev) if want_lse else None
+        self.attn_ws = sparse_attn_workspace(q, k, v, self.token_idx)
 
     def index(self):
         flat_indexer_topk(self.qidx, self.kidx, self.q_pos, self.k_top, token_idx=self.token_idx,
@@ -83,7 +85,7 @@ class FlatPipeline:
 
     def attend(self):
         sparse_attn_fwd(self.q, self.k, self.v, self.token_idx, self.scale, out=self.out,
-                        lse=self.lse, want_lse=self.lse is not None)
+                        lse=self.lse, want_lse=self.lse is not None, workspace=self.attn_ws)
 
     def run(self):
         self.index()

@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_match_header():
     names = _declared()
-    assert len(names) == 11
+    assert len(names) == 12
     lib = ctypes.CDLL(H.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -80,7 +80,7 @@ def test_attention_validation():
     L = H.lib()
     s = S(0, 128, 128)
     base = [FAKE, s, FAKE, s, FAKE, s, 1, 4, 64, 6, 4, 128, 128, FAKE, 8, 0.1, FAKE, s, NULL,
-            NULL]
+            NULL, 0, NULL]
     assert L.sparse_attn_fwd(*base) == 2 and "multiple" in _err()     # Hq % Hkv
     b2 = list(base)
     b2[9], b2[10] = 128, 1
@@ -94,6 +94,24 @@ def test_attention_validation():
     b5 = list(base)
     b5[0] = NULL
     assert L.sparse_attn_fwd(*b5) == 1
+
+
+def test_attention_workspace():
+    L = H.lib()
+    # few (query, kv head) pairs with long lists split (decode: 64 x 16 heads
+    # over 2048 tokens); many pairs, short lists and the MLA shape do not
+    need = L.sparse_attn_fwd_workspace_bytes(64, 1, 16, 1, 128, 128, 2048)
+    assert need > 0 and need % 256 == 0
+    assert L.sparse_attn_fwd_workspace_bytes(1, 16384, 16, 1, 128, 128, 2048) == 0
+    assert L.sparse_attn_fwd_workspace_bytes(1, 1, 16, 1, 128, 128, 32) == 0
+    assert L.sparse_attn_fwd_workspace_bytes(1, 4, 64, 1, 576, 512, 2048) == 0
+    assert L.sparse_attn_fwd_workspace_bytes(1, 4, 6, 4, 128, 128, 2048) == 0   # Hq % Hkv
+    s = S(0, 128 * 16, 128)
+    args = [FAKE, s, FAKE, S(0, 128, 128), FAKE, S(0, 128, 128), 64, 1, 4096, 16, 1, 128, 128,
+            FAKE, 2048, 0.1, FAKE, s, NULL]
+    assert L.sparse_attn_fwd(*args, FAKE, need - 1, NULL) == 5 and "needs" in _err()
+    assert L.sparse_attn_fwd(*args, ctypes.c_void_p(0x10010), need, NULL) == 5
+    assert "aligned" in _err()
 
 
 def test_hils_validation():

@@ -6,7 +6,12 @@ accepts: ragged lengths (1, 33, 77 tokens), -1 holes in the middle, ids at
 or past L (skipped by contract, dropped for the oracle), repeated ids (a
 multiset: counted twice on both sides), a list with no valid token (zero
 output, log-sum-exp -inf), and logit ranges wide enough that the running
-reference of the online softmax must move or be redone."""
+reference of the online softmax must move or be redone.
+
+The d128_split cases have few (query, kv head) pairs and long lists, so the
+head-width-128 kernel splits each list over several waves and merges them;
+they run with the workspace that enables the split and without it (one wave
+per pair), including splits that hold no valid token."""
 import math
 import zlib
 
@@ -33,6 +38,14 @@ CASES = [
     ("mla_empty", 512, 3, 64, 64, 1, 576, 512, True, 1.0, 1 / 24, "empty"),
     ("mqa_holes", 1000, 8, 100, 16, 1, 128, 128, False, 1.0, 1.0, "holes"),
     ("gqa_dups_oob", 800, 8, 45, 8, 2, 64, 64, False, 1.0, 1.0, "dups_oob"),
+]
+SPLIT_CASES = [
+    ("d128_split_holes", 5000, 4, 2048, 16, 1, 128, 128, False, 1.0, 1.0, "holes"),
+    ("d128_split_short", 100, 3, 1024, 16, 1, 128, 128, False, 1.0, 1.0, "sorted"),
+    ("d128_split_empty", 512, 2, 256, 16, 1, 128, 128, False, 1.0, 1.0, "empty"),
+    # logits spread as with q, k ~ N(0, 64), N(0, 1); values O(1) like the output bar assumes
+    ("d128_split_late_peak", 3000, 2, 1500, 12, 1, 128, 128, False, 32.0, 0.25, "late_peak"),
+    ("d128_split_gqa", 4000, 2, 690, 12, 3, 128, 128, False, 1.0, 1.0, "dups_oob"),
 ]
 
 
@@ -64,8 +77,21 @@ def _lists(pattern, L, nq, topk, g):
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_sparse_attention_lists(case):
+    _run_case(case, "auto")
+
+
+@pytest.mark.parametrize("split", [True, False], ids=["split", "unsplit"])
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_sparse_attention_split(case, split):
+    name, L, nq, topk, Hq, Hkv, Dk, Dv = case[:8]
+    need = H.lib().sparse_attn_fwd_workspace_bytes(1, nq, Hq, Hkv, Dk, Dv, topk)
+    assert need > 0, f"{name} does not split"
+    _run_case(case, "auto" if split else None)
+
+
+def _run_case(case, workspace):
     name, L, nq, topk, Hq, Hkv, Dk, Dv, latent, qs, ks, pattern = case
-    log(f"case attention {name}")
+    log(f"case attention {name} workspace={workspace}")
     seed = zlib.crc32(name.encode())
     tg = torch.Generator(device="cpu").manual_seed(seed)
     g = np.random.default_rng(seed)
@@ -83,7 +109,7 @@ def test_sparse_attention_lists(case):
     qd, kd = q.to(DEV), kk.to(DEV)
     vd = kd[..., :Dv] if latent else vv.to(DEV)
     out, lse = H.sparse_attn_fwd(qd, kd, vd, torch.from_numpy(idx)[None].to(DEV), scale,
-                                 want_lse=True)
+                                 want_lse=True, workspace=workspace)
     torch.cuda.synchronize()
     go = out[0].float().cpu().numpy()
     gl = lse[0].cpu().numpy().astype(np.float64)

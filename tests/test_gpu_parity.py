@@ -169,6 +169,14 @@ def test_determinism_and_decode_matches_prefill_row():
     d.run()
     torch.cuda.synchronize()
     assert torch.equal(d.token_idx[:, 0], t1[:, -1])
+    # one query splits its token list over several waves (another fp32
+    # summation order); without the workspace it runs like a prefill row
+    assert d.attn_ws is not None
+    check_attention(d.out[:, 0].float().cpu().numpy(), o1[:, -1].float().cpu().numpy(),
+                    "decode split vs prefill row")
+    d.attn_ws = None
+    d.attend()
+    torch.cuda.synchronize()
     assert torch.equal(d.out[:, 0], o1[:, -1])
 
 
