@@ -40,7 +40,7 @@ constexpr int NT = 16;             // tokens per tile
 constexpr int TCH = NT * D / 8;    // 16-byte chunks per K or V tile (256)
 constexpr int WAVES = 2;           // independent waves per workgroup
 constexpr float kRaise = 64.0f;
-constexpr int64_t kSplitWaves = 2048;  // split the lists while fewer waves than this
+constexpr int64_t kSplitWaves = 512;  // split the lists while fewer waves than this
 constexpr int kMinSplitTiles = 4;      // tiles per split, at least
 
 typedef __attribute__((address_space(3))) void* lds_ptr;

@@ -279,22 +279,36 @@ __global__ void tile_table_kernel(const uint32_t* __restrict__ cnt,
 // all 64 pairs of the tile are the B operand (gathered query rows). The
 // accumulator lane layout (column = pair, 4 consecutive tokens) is stored
 // as one 16-byte write per pair.
-template <int D, int BS>
+// DIRECT (one query per sequence, so no key block has two pairs): workgroup
+// x scores pair x on its own, and the bucket tables are not used.
+template <int D, int BS, bool DIRECT>
 __global__ __launch_bounds__(256) void token_score_kernel(
     const uint16_t* __restrict__ qidx, int64_t qsb, int64_t qst, const uint16_t* __restrict__ kidx,
     int64_t ksb, int64_t kst, int L, int nq, int m, int nblk, const uint32_t* __restrict__ tiles,
     const uint32_t* __restrict__ total, const uint32_t* __restrict__ tile_off,
     const uint32_t* __restrict__ offs, const uint32_t* __restrict__ cnt,
-    const uint32_t* __restrict__ pairs, float* __restrict__ scores) {
+    const uint32_t* __restrict__ pairs, const int32_t* __restrict__ block_idx,
+    float* __restrict__ scores) {
   constexpr int KS = D / 32;
   constexpr int MT = BS / 64;  // 16-token tiles per wave
   const uint32_t tile = blockIdx.x;
-  if (tile >= total[1]) return;
-  const uint32_t key = tiles[tile];
-  const uint32_t sub = tile - tile_off[key];
-  const uint32_t p0 = offs[key] + sub * kTQ;
-  const uint32_t np = min(static_cast<uint32_t>(kTQ), cnt[key] - sub * kTQ);
-  const int b = key / nblk, c = key % nblk;
+  uint32_t p0, np;
+  int b, c;
+  if constexpr (DIRECT) {
+    c = block_idx[tile];
+    if (c < 0 || c >= nblk) return;  // empty slot: never a candidate
+    p0 = tile;
+    np = 1;
+    b = static_cast<int>(tile / (static_cast<uint32_t>(nq) * m));
+  } else {
+    if (tile >= total[1]) return;
+    const uint32_t key = tiles[tile];
+    const uint32_t sub = tile - tile_off[key];
+    p0 = offs[key] + sub * kTQ;
+    np = min(static_cast<uint32_t>(kTQ), cnt[key] - sub * kTQ);
+    b = key / nblk;
+    c = key % nblk;
+  }
   const int wave = threadIdx.x / kWave, lane = lane_id();
   const int g = lane / 16, r16 = lane % 16;
 
@@ -311,7 +325,7 @@ __global__ __launch_bounds__(256) void token_score_kernel(
   for (int nt = 0; nt < 4; ++nt) {
     if (nt * 16 >= static_cast<int>(np)) break;
     const uint32_t pl = min(static_cast<uint32_t>(nt * 16 + r16), np - 1);
-    const uint32_t pid = pairs[p0 + pl];
+    const uint32_t pid = DIRECT ? p0 : pairs[p0 + pl];
     const uint32_t qrow = pid / m;  // b*nq + q
     const int qq = qrow % nq;
     const uint16_t* qr = qidx + b * qsb + static_cast<int64_t>(qq) * qst + 8 * g;
@@ -546,38 +560,52 @@ hipError_t launch_token_select(const uint16_t* qidx, Str3 qs, const uint16_t* ki
   const size_t npairs = static_cast<size_t>(batch) * nq * m;
   const size_t max_tiles = (npairs + kTQ - 1) / kTQ + nkeys;
   TokWs w = carve(ws, batch, nq, L, B, m, nullptr);
-  // cnt and cursor are adjacent: clear both with one fill kernel
-  const size_t zero_n = (reinterpret_cast<char*>(w.offs) - reinterpret_cast<char*>(w.cnt)) / 4;
-  hipLaunchKernelGGL(zero_u32_kernel, dim3(std::min<size_t>((zero_n + 255) / 256, 4096)),
-                     dim3(256), 0, s, w.cnt, zero_n);
-  const unsigned pg = static_cast<unsigned>((npairs + 255) / 256);
-  const bool lds_hist = nblk <= kHistMax;
-  const int qpw = std::max(1, 4096 / m);
-  const dim3 hg((nq + qpw - 1) / qpw, batch);
-  if (lds_hist)
-    hipLaunchKernelGGL(count_pairs_kernel, hg, dim3(256), nblk * 4, s, block_idx, nq, m, nblk, qpw,
-                       w.cnt);
-  else
-    hipLaunchKernelGGL(count_pairs_direct_kernel, dim3(pg), dim3(256), 0, s, block_idx, nq, m,
-                       nblk, npairs, w.cnt);
-  const int nchunks = (nkeys + kScanChunk - 1) / kScanChunk;
-  if (nchunks > 1)
-    hipLaunchKernelGGL(bucket_partials_kernel, dim3(nchunks), dim3(256), 0, s, w.cnt, nkeys,
-                       w.part);
-  hipLaunchKernelGGL(scan_buckets_kernel, dim3(nchunks), dim3(256), 0, s, w.cnt, nkeys,
-                     nchunks > 1 ? w.part : nullptr, nchunks, w.offs, w.tile_off, w.total);
-  if (lds_hist)
-    hipLaunchKernelGGL(scatter_pairs_kernel, hg, dim3(256), nblk * 8, s, block_idx, nq, m, nblk,
-                       qpw, w.offs, w.cursor, w.pairs);
-  else
-    hipLaunchKernelGGL(scatter_pairs_direct_kernel, dim3(pg), dim3(256), 0, s, block_idx, nq, m,
-                       nblk, npairs, w.offs, w.cursor, w.pairs);
-  hipLaunchKernelGGL(tile_table_kernel, dim3((nkeys + 255) / 256), dim3(256), 0, s, w.cnt,
-                     w.tile_off, nkeys, w.tiles);
+  // one query per sequence: every key block has at most one pair, so the
+  // pairs are scored in place without bucketing them by block
+  const bool direct = nq == 1;
+  if (!direct) {
+    // cnt and cursor are adjacent: clear both with one fill kernel
+    const size_t zero_n = (reinterpret_cast<char*>(w.offs) - reinterpret_cast<char*>(w.cnt)) / 4;
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(std::min<size_t>((zero_n + 255) / 256, 4096)),
+                       dim3(256), 0, s, w.cnt, zero_n);
+    const unsigned pg = static_cast<unsigned>((npairs + 255) / 256);
+    const bool lds_hist = nblk <= kHistMax;
+    const int qpw = std::max(1, 4096 / m);
+    const dim3 hg((nq + qpw - 1) / qpw, batch);
+    if (lds_hist)
+      hipLaunchKernelGGL(count_pairs_kernel, hg, dim3(256), nblk * 4, s, block_idx, nq, m, nblk,
+                         qpw, w.cnt);
+    else
+      hipLaunchKernelGGL(count_pairs_direct_kernel, dim3(pg), dim3(256), 0, s, block_idx, nq, m,
+                         nblk, npairs, w.cnt);
+    const int nchunks = (nkeys + kScanChunk - 1) / kScanChunk;
+    if (nchunks > 1)
+      hipLaunchKernelGGL(bucket_partials_kernel, dim3(nchunks), dim3(256), 0, s, w.cnt, nkeys,
+                         w.part);
+    hipLaunchKernelGGL(scan_buckets_kernel, dim3(nchunks), dim3(256), 0, s, w.cnt, nkeys,
+                       nchunks > 1 ? w.part : nullptr, nchunks, w.offs, w.tile_off, w.total);
+    if (lds_hist)
+      hipLaunchKernelGGL(scatter_pairs_kernel, hg, dim3(256), nblk * 8, s, block_idx, nq, m,
+                         nblk, qpw, w.offs, w.cursor, w.pairs);
+    else
+      hipLaunchKernelGGL(scatter_pairs_direct_kernel, dim3(pg), dim3(256), 0, s, block_idx, nq, m,
+                         nblk, npairs, w.offs, w.cursor, w.pairs);
+    hipLaunchKernelGGL(tile_table_kernel, dim3((nkeys + 255) / 256), dim3(256), 0, s, w.cnt,
+                       w.tile_off, nkeys, w.tiles);
+  }
 #define HISA_TS(D_, B_)                                                                       \
-  hipLaunchKernelGGL((token_score_kernel<D_, B_>), dim3(static_cast<unsigned>(max_tiles)),   \
-                     dim3(256), 0, s, qidx, qs.b, qs.t, kidx, ks.b, ks.t, L, nq, m, nblk,     \
-                     w.tiles, w.total, w.tile_off, w.offs, w.cnt, w.pairs, w.scores)
+  do {                                                                                        \
+    if (direct)                                                                               \
+      hipLaunchKernelGGL((token_score_kernel<D_, B_, true>), dim3(static_cast<unsigned>(npairs)), \
+                         dim3(256), 0, s, qidx, qs.b, qs.t, kidx, ks.b, ks.t, L, nq, m, nblk, \
+                         w.tiles, w.total, w.tile_off, w.offs, w.cnt, w.pairs, block_idx,     \
+                         w.scores);                                                           \
+    else                                                                                      \
+      hipLaunchKernelGGL((token_score_kernel<D_, B_, false>),                                 \
+                         dim3(static_cast<unsigned>(max_tiles)), dim3(256), 0, s, qidx, qs.b,  \
+                         qs.t, kidx, ks.b, ks.t, L, nq, m, nblk, w.tiles, w.total, w.tile_off, \
+                         w.offs, w.cnt, w.pairs, block_idx, w.scores);                        \
+  } while (0)
   if (d == 64) {
     if (B == 64) HISA_TS(64, 64); else if (B == 128) HISA_TS(64, 128); else HISA_TS(64, 256);
   } else {
