@@ -8,6 +8,7 @@ launch stream), the dominant kernel's roofline, the flat-indexer comparison
 and the CPU oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-flat] [--no-cpu]
+       python bench.py --sweep [--workload NAME]   (block size / kept-block sweep)
 """
 from __future__ import annotations
 
@@ -42,6 +43,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only time the indexer (steps 1-4) for block sizes 64/128/256 and "
+                         "several m on this workload, one JSON line each, with the share of "
+                         "the flat indexer's tokens each keeps")
     ap.add_argument("--write-traffic", default="",
                     help="only summarise rocprofv3 byte counters found under this folder "
                          "(fetch/, write/, cfetch/, cwrite/) into the traffic record")
@@ -378,6 +383,71 @@ def bench_hils(w, a, inp):
     return res
 
 
+def recall_vs_flat(hier_idx, flat_idx, chunk=4096):
+    """Mean over queries of |hier ∩ flat| / |flat| for ascending, -1 padded
+    token lists [b, nq, k] (the flat indexer's exact top-k as the reference)."""
+    import torch
+    hit = tot = 0
+    h2 = hier_idx.reshape(-1, hier_idx.shape[-1])
+    f2 = flat_idx.reshape(-1, flat_idx.shape[-1])
+    for i in range(0, h2.shape[0], chunk):
+        h, f = h2[i:i + chunk], f2[i:i + chunk].contiguous()
+        # the -1 padding sits after the ids: map it past them to keep rows sorted
+        h = torch.where(h < 0, torch.iinfo(torch.int32).max, h).contiguous()
+        pos = torch.searchsorted(h, f).clamp_(max=h.shape[1] - 1)
+        found = (h.gather(1, pos) == f) & (f >= 0)
+        n = (f >= 0).sum(1).clamp_(min=1)
+        hit += (found.sum(1).double() / n.double()).sum().item()
+        tot += h.shape[0]
+    return hit / tot
+
+
+def bench_sweep(w, a, inp):
+    """Block size and kept-block sweep of the hierarchical indexer (steps 1-4,
+    the cost the two knobs move; the attention over k tokens is the same for
+    every setting), against the flat indexer on the same inputs."""
+    import torch
+
+    import long_context_indexer_block_amd as H
+    from long_context_indexer_block_amd.pipeline import FlatPipeline, HierPipeline
+
+    steps, warmup = max(2, a.steps // 2), max(1, a.warmup)
+    f = FlatPipeline(inp["kidx"], inp["qidx"], inp["q_pos"], inp["q"], inp["k"], inp["v"], w.k,
+                     w.scale)
+    fwall, _ = timed([f.index], steps, warmup)
+    flat_idx = f.token_idx.clone()
+    flat_ms = fwall * 1e3 / steps
+    del f
+    torch.cuda.empty_cache()
+    print(json.dumps({"sweep": w.name, "path": "flat", "index_ms": flat_ms}), flush=True)
+    auto_h, auto_m = H.hisa_auto_plan(w.L, w.B)
+    for B in (64, 128, 256):
+        for m in (32, 64, 128):
+            if m * B > 16384:
+                continue
+            p = HierPipeline(inp["kidx"], inp["qidx"], inp["q_pos"], inp["q"], inp["k"], inp["v"],
+                             B, m, w.k, w.scale)
+            calls = [
+                p.summarize,
+                lambda: H.hisa_block_score(p.qidx, p.q_pos, p.split, p.B, out=p.block_scores),
+                lambda: H.hisa_select_blocks(p.block_scores, p.q_pos, p.B, p.m, out=p.block_idx),
+                lambda: H.hisa_token_select(p.qidx, p.kidx, p.q_pos, p.block_idx, p.B, p.k_top,
+                                            token_idx=p.token_idx, want_scores=False,
+                                            workspace=p.ws),
+            ]
+            wall, stage = timed(calls, steps, warmup)
+            ms = wall * 1e3 / steps
+            rec = {"sweep": w.name, "path": "hierarchical", "B": B, "m": m,
+                   "auto_plan": bool(auto_h and B == w.B and m == auto_m), "index_ms": ms,
+                   "stage_ms": dict(zip(["summary", "block_score", "select_blocks",
+                                         "token_select"], stage)),
+                   "speedup_vs_flat": flat_ms / ms,
+                   "recall_vs_flat": recall_vs_flat(p.token_idx, flat_idx)}
+            print(json.dumps(rec), flush=True)
+            del p
+            torch.cuda.empty_cache()
+
+
 def main():
     a = parse()
     if a.write_traffic:
@@ -400,6 +470,9 @@ def main():
     log(f"generating {w.name} inputs on the GPU")
     inp = make_inputs(w, "cuda", seed=0)
     torch.cuda.synchronize()
+    if a.sweep:
+        bench_sweep(w, a, inp)
+        return
     if w.kind == "prefill":
         res = bench_prefill(w, a, inp)
     elif w.kind == "decode":

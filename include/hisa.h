@@ -128,6 +128,20 @@ hisa_status_t hisa_token_select(const void* qidx, hisa_strides_t qs, const void*
                                 size_t workspace_bytes, hisa_stream_t stream);
 size_t hisa_token_select_workspace_bytes(int batch, int nq, int L, int B, int m, int k);
 
+/* Runtime policy (HISA explainer 1.3 item 3, the adaptive mechanism, and
+ * 3.2 item 2, the dynamic number of kept blocks; HISA news article: short
+ * texts fall back to the original indexer). For a sequence of L keys and
+ * block size B:
+ *   *hierarchical  0 when L < 8192 (the caller runs flat_indexer_topk), else
+ *                  1 (hisa_block_score .. hisa_token_select); the pages leave
+ *                  8192 <= L <= 16384 open and this takes the hierarchical
+ *                  path there.
+ *   *m             max(64, L / 2000), clamped to 16384 / B (the largest
+ *                  supported m*B).
+ * Host-only: launches nothing. HISA_ERR_NULL for null outputs, HISA_ERR_SHAPE
+ * for L < 1, HISA_ERR_UNSUPPORTED for an unsupported B. */
+hisa_status_t hisa_auto_plan(int L, int B, int* hierarchical, int* m);
+
 /* Flat comparison indexer (HISA explainer 1.1 item 1; HISA news article: the
  * original indexer scores every earlier token). Candidates are all j <= t;
  * output format as hisa_token_select. */

@@ -45,6 +45,7 @@ _SIGS = {
     "flat_indexer_topk": (_I, [_P, Strides, _P, Strides, _P, _I, _I, _I, _I, _I, _P, _P, _P, _S,
                                _P]),
     "flat_indexer_topk_workspace_bytes": (_S, [_I, _I, _I, _I]),
+    "hisa_auto_plan": (_I, [_I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
     "sparse_attn_fwd": (_I, [_P, Strides, _P, Strides, _P, Strides, _I, _I, _I, _I, _I, _I, _I,
                              _P, _I, _F, _P, Strides, _P, _P, _S, _P]),
     "sparse_attn_fwd_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I, _I]),
@@ -186,6 +187,14 @@ def flat_indexer_topk(qidx, kidx, q_pos, k, token_idx=None, token_scores=None, w
                                    _ptr(q_pos), b, nq, L, d, k, _ptr(token_idx),
                                    _ptr(token_scores), _ptr(ws), ws.numel(), _stream()))
     return token_idx, token_scores
+
+
+def hisa_auto_plan(L, B):
+    """(hierarchical, m) for L keys and block size B: the flat indexer below
+    8192 keys, m = max(64, L // 2000) clamped to 16384 // B."""
+    h, m = _I(0), _I(0)
+    _check(lib().hisa_auto_plan(int(L), int(B), ctypes.byref(h), ctypes.byref(m)))
+    return bool(h.value), m.value
 
 
 # ----------------------------------------------------------------- attention

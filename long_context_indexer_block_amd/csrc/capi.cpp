@@ -3,6 +3,7 @@
 // check passes; a failed check leaves all outputs untouched.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -163,6 +164,16 @@ hisa_status_t hisa_token_select(const void* qidx, hisa_strides_t qs, const void*
                                               token_scores, workspace,
                                               static_cast<hipStream_t>(stream)),
                     "hisa_token_select");
+}
+
+hisa_status_t hisa_auto_plan(int L, int B, int* hierarchical, int* m) {
+  CHECK(hierarchical && m, HISA_ERR_NULL, "hierarchical and m are required");
+  CHECK(L >= 1, HISA_ERR_SHAPE, "L=%d must be >= 1", L);
+  hisa_status_t st;
+  if ((st = check_block(B)) != HISA_OK) return st;
+  *hierarchical = L >= 8192 ? 1 : 0;
+  *m = std::min(std::max(64, L / 2000), 16384 / B);
+  return HISA_OK;
 }
 
 size_t flat_indexer_topk_workspace_bytes(int batch, int nq, int L, int k) {

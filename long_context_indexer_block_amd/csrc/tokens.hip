@@ -436,15 +436,17 @@ token_topk_rows_kernel(const float* __restrict__ scores, const int32_t* __restri
   const int nrows = (m * B) >> 6;
   const float* row = scores + qi * static_cast<int64_t>(m) * B;
   const float qnan = __uint_as_float(0x7fc00000u);
-  // the slots' block ids, one per lane (m <= 128), read by row with readlane;
-  // a slot that is empty or past the end of the keys gets -1
-  int cv0 = -1, cv1 = -1;
-  if (l < m) cv0 = block_idx[qi * m + l];
-  if (64 + l < m) cv1 = block_idx[qi * m + 64 + l];
-  cv0 = cv0 >= 0 && cv0 < nblk ? cv0 : -1;
-  cv1 = cv1 >= 0 && cv1 < nblk ? cv1 : -1;
-  auto slot_block = [&](int sl) {
-    return __builtin_amdgcn_readlane(sl < 64 ? cv0 : cv1, sl & 63);
+  // the slots' block ids, one per lane in four registers (m <= 256), read by
+  // row with readlane; a slot that is empty or past the end of the keys gets -1
+  int cv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = 64 * j + l < m ? block_idx[qi * m + 64 * j + l] : -1;
+    cv[j] = c >= 0 && c < nblk ? c : -1;
+  }
+  auto slot_block = [&](int sl) {  // sl is wave-uniform
+    const int v = sl < 128 ? (sl < 64 ? cv[0] : cv[1]) : (sl < 192 ? cv[2] : cv[3]);
+    return __builtin_amdgcn_readlane(v, sl & 63);
   };
   float v[RW];
 #pragma unroll
@@ -614,19 +616,23 @@ hipError_t launch_token_select(const uint16_t* qidx, Str3 qs, const uint16_t* ki
 #undef HISA_TS
   const int64_t nq_total = static_cast<int64_t>(batch) * nq;
   const size_t stage_bytes = static_cast<size_t>(k) * 4 * (token_scores ? 2 : 1);
-  if (B % 64 == 0 && m * B <= 8192 && stage_bytes <= 65536) {
+  if (B % 64 == 0 && m * B <= 16384 && m <= 256 && stage_bytes <= 65536) {
     const int nrows = m * B / 64;
     const dim3 gr(static_cast<unsigned>(nq_total));
 #define HISA_TR(R_, W_)                                                                        \
   hipLaunchKernelGGL((token_topk_rows_kernel<R_, W_>), gr, dim3(64 * W_), stage_bytes, s,       \
                      w.scores, block_idx, q_pos, m, B, k, L, token_idx, token_scores)
     if (nq_total < kFewQueries) {
-      // few queries (decode): WIDE waves per query, so that the CUs that get a
-      // workgroup hold enough waves to hide the latency of each step
+      // few queries (decode): kWideW waves per query, so that the CUs that get
+      // a workgroup hold enough waves to hide the latency of each step
       const int rw = (nrows + kWideW - 1) / kWideW;  // rows per wave
       if (rw <= 2) HISA_TR(2, kWideW);
       else if (rw <= 4) HISA_TR(4, kWideW);
-      else HISA_TR(128 / kWideW, kWideW);
+      else if (rw <= 8) HISA_TR(8, kWideW);
+      else HISA_TR(16, kWideW);
+    } else if (nrows > 128) {
+      // more than 8192 candidates: 8 waves of up to 32 rows
+      HISA_TR(32, 8);
     } else {
       const int rw = (nrows + 3) / 4;
       if (rw <= 2) HISA_TR(2, 4);

@@ -3,6 +3,8 @@
 HierPipeline: block summary -> block score -> top-m blocks -> token top-k
               -> sparse attention (HISA explainer 1.2-1.3; HISA news article).
 FlatPipeline: flat indexer top-k -> sparse attention (the comparison path).
+AutoPipeline: one of the two by the runtime policy of hisa_auto_plan (flat
+              below 8192 keys, m = max(64, L // 2000)).
 HilsDecode:   chunk keys (once per cache) -> chunk scores -> top-m chunks
               -> two-level softmax attention (HiLS chapter).
 """
@@ -11,8 +13,9 @@ from __future__ import annotations
 import torch
 
 from . import (flat_indexer_topk, flat_indexer_topk_workspace_bytes, hils_two_level_attn_fwd,
-               hisa_block_score, hisa_block_summary, hisa_select_blocks, hisa_token_select,
-               hisa_token_select_workspace_bytes, sparse_attn_fwd, sparse_attn_workspace)
+               hisa_auto_plan, hisa_block_score, hisa_block_summary, hisa_select_blocks,
+               hisa_token_select, hisa_token_select_workspace_bytes, sparse_attn_fwd,
+               sparse_attn_workspace)
 
 
 class HierPipeline:
@@ -91,6 +94,28 @@ class FlatPipeline:
         self.index()
         self.attend()
         return self.out
+
+
+class AutoPipeline:
+    """The hierarchical or the flat path, chosen from L and B by
+    hisa_auto_plan (HISA explainer 1.3 item 3 and 3.2 item 2)."""
+
+    def __init__(self, kidx, qidx, q_pos, q, k, v, B, k_top, scale, want_scores=False,
+                 want_lse=False):
+        L = kidx.shape[1]
+        self.hierarchical, self.m = hisa_auto_plan(L, B)
+        if self.hierarchical:
+            self.path = HierPipeline(kidx, qidx, q_pos, q, k, v, B, self.m, k_top, scale,
+                                     want_scores=want_scores, want_lse=want_lse)
+        else:
+            self.path = FlatPipeline(kidx, qidx, q_pos, q, k, v, k_top, scale,
+                                     want_scores=want_scores, want_lse=want_lse)
+
+    def __getattr__(self, name):  # token_idx, token_scores, out, lse, ...
+        return getattr(self.__dict__["path"], name)
+
+    def run(self):
+        return self.path.run()
 
 
 class HilsDecode:

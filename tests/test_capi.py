@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_match_header():
     names = _declared()
-    assert len(names) == 12
+    assert len(names) == 13
     lib = ctypes.CDLL(H.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -135,3 +135,18 @@ def test_missing_library_raises(monkeypatch):
     monkeypatch.setattr(H, "LIB_PATH", "/nonexistent/libhisa.so")
     with pytest.raises(H.HisaError):
         H.lib()
+
+
+def test_auto_plan():
+    """The runtime policy (HISA explainer 1.3 item 3; 3.2 item 2): the flat
+    indexer below 8192 keys, m = max(64, L // 2000), clamped to m*B <= 16384."""
+    for L, B, hier, m in [(1, 128, False, 64), (8191, 128, False, 64), (8192, 128, True, 64),
+                          (16384, 64, True, 64), (65536, 128, True, 64), (131072, 128, True, 65),
+                          (200000, 128, True, 100), (1048576, 64, True, 256),
+                          (1048576, 128, True, 128), (1048576, 256, True, 64)]:
+        assert H.hisa_auto_plan(L, B) == (hier, m), (L, B)
+    L = H.lib()
+    x, y = ctypes.c_int(0), ctypes.c_int(0)
+    assert L.hisa_auto_plan(0, 128, ctypes.byref(x), ctypes.byref(y)) == 2
+    assert L.hisa_auto_plan(4096, 96, ctypes.byref(x), ctypes.byref(y)) == 3
+    assert L.hisa_auto_plan(4096, 128, None, ctypes.byref(y)) == 1

@@ -13,7 +13,8 @@ import torch
 
 import long_context_indexer_block_amd as H
 import oracle.hisa_oracle as O
-from long_context_indexer_block_amd.pipeline import FlatPipeline, HierPipeline, HilsDecode
+from long_context_indexer_block_amd.pipeline import (AutoPipeline, FlatPipeline, HierPipeline,
+                                                     HilsDecode)
 from parity import (SeqOracle, check_attention, check_index_rows, check_score_rows, f64, log)
 from workloads import WORKLOADS, Workload, make_inputs, sample_positions
 
@@ -152,6 +153,45 @@ def test_coverage_hier_equals_flat_gpu():
     torch.cuda.synchronize()
     assert torch.equal(p.token_idx, f.token_idx)
     assert torch.equal(p.out, f.out)
+
+
+@pytest.mark.parametrize("B,m", [(128, 128), (64, 256)])
+def test_token_select_16k_candidates(B, m):
+    # m*B = 16384 candidates per query (up to 256 slots) and enough queries
+    # for the 8-wave row select; sampled rows against the oracle
+    w = _mk(f"cand16k_B{B}_m{m}", L=20480, nq=1024, B=B, m=m, k=3000, d_idx=64, Hq=1, Hkv=1)
+    log(f"case {w}")
+    inp = make_inputs(w, DEV, seed=9)
+    p = _run_hier(w, inp)
+    rows = list(range(0, 1024, 97)) + [1022, 1023]
+    _check_hier(w, inp, p, rows, attn_rows=rows[-3:], what=w.name)
+
+
+@pytest.mark.parametrize("L,hier", [(4096, False), (12288, True)])
+def test_auto_pipeline(L, hier):
+    # the runtime policy: the flat indexer below 8192 keys, else the
+    # hierarchical one with m = max(64, L // 2000) = 64 here
+    w = _mk("auto", L=L, nq=96, B=128, m=64, k=256, d_idx=64, Hq=2, Hkv=1)
+    log(f"case auto {w}")
+    inp = make_inputs(w, DEV, seed=8)
+    a = AutoPipeline(inp["kidx"], inp["qidx"], inp["q_pos"], inp["q"], inp["k"], inp["v"], w.B,
+                     w.k, w.scale, want_scores=True)
+    assert a.hierarchical == hier and a.m == 64
+    a.run()
+    if hier:
+        r = HierPipeline(inp["kidx"], inp["qidx"], inp["q_pos"], inp["q"], inp["k"], inp["v"], w.B,
+                         64, w.k, w.scale)
+    else:
+        r = FlatPipeline(inp["kidx"], inp["qidx"], inp["q_pos"], inp["q"], inp["k"], inp["v"], w.k,
+                         w.scale)
+    r.run()
+    torch.cuda.synchronize()
+    assert torch.equal(a.token_idx, r.token_idx) and torch.equal(a.out, r.out)
+    so = SeqOracle(inp, 0, w.B, with_attention=False)
+    rows = [0, 47, 95]
+    ti = a.token_idx.cpu().numpy()
+    ref = [so.hier(x, 64, w.k)[2] if hier else so.flat(x, w.k)[0] for x in rows]
+    check_index_rows(ti[0, rows], np.stack(ref), "auto token_idx")
 
 
 def test_determinism_and_decode_matches_prefill_row():
