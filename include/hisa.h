@@ -90,6 +90,26 @@ hisa_status_t hisa_block_summary(const void* kidx, hisa_strides_t ks, int batch,
                                  int B, const void* proj, float* summary, void* split,
                                  hisa_stream_t stream);
 
+/* Step 1 for a growing cache (decode). A block's summary depends on its own
+ * tokens only (HISA explainer 1.2.1, mean pooling over fixed blocks), and the
+ * KV cache itself is left as it is (HISA news article, drop-in replacement),
+ * so after the cache of every sequence has grown to L tokens only the rows
+ * of the blocks that changed need recomputing. Recomputes rows
+ * first_row .. ceil(L/B) - 1 of tables laid out with n_rows_cap rows per
+ * sequence (summary fp32 [batch][n_rows_cap][d], split bf16
+ * [batch][n_rows_cap][3][d]); other rows are left untouched.
+ *   first_row = (L - 1) / B: the block holding the newest token (one decode
+ *                step: the block it starts, extends or completes);
+ *   first_row = 0: the whole table, built in this layout.
+ * hisa_block_score and hisa_select_blocks then take n_rows = n_rows_cap;
+ * rows past ceil(L/B) - 1 are never read. Other arguments and errors as
+ * hisa_block_summary; HISA_ERR_SHAPE if n_rows_cap < ceil(L/B) or first_row
+ * is outside [0, ceil(L/B)). */
+hisa_status_t hisa_block_summary_update(const void* kidx, hisa_strides_t ks, int batch, int L,
+                                        int d, int B, const void* proj, float* summary,
+                                        void* split, int n_rows_cap, int first_row,
+                                        hisa_stream_t stream);
+
 /* Step 2: block scores (HISA explainer 1.2.1 item 2; HISA news article,
  * block-level coarse filter: the indexer's own dot product against the
  * block features only).

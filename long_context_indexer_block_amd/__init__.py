@@ -37,6 +37,7 @@ _SIGS = {
     "hisa_last_error": (ctypes.c_char_p, []),
     "hisa_abi_version": (_I, []),
     "hisa_block_summary": (_I, [_P, Strides, _I, _I, _I, _I, _P, _P, _P, _P]),
+    "hisa_block_summary_update": (_I, [_P, Strides, _I, _I, _I, _I, _P, _P, _P, _I, _I, _P]),
     "hisa_block_score": (_I, [_P, Strides, _P, _I, _I, _P, _I, _I, _I, _P, _P]),
     "hisa_select_blocks": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "hisa_token_select": (_I, [_P, Strides, _P, Strides, _P, _P, _I, _I, _I, _I, _I, _I, _I,
@@ -111,6 +112,22 @@ def hisa_block_summary(kidx, B, proj=None, summary=None, split=None, want_split=
         split = torch.empty(b, n, 3, d, dtype=torch.bfloat16, device=kidx.device)
     _check(lib().hisa_block_summary(_ptr(kidx), _str3(kidx, "bt"), b, L, d, B, _ptr(proj),
                                     _ptr(summary), _ptr(split), _stream()))
+    return summary, split
+
+
+def hisa_block_summary_update(kidx, L, B, summary, split, first_row=None, proj=None):
+    """Recompute rows first_row .. ceil(L/B)-1 (default: the row of token L-1)
+    of summary [b, cap, d] / split [b, cap, 3, d] from the first L rows of
+    kidx [b, >=L, d] (a cache with room to grow)."""
+    _need(kidx, torch.bfloat16, "kidx")
+    b, _, d = kidx.shape
+    tab = summary if summary is not None else split
+    cap = tab.shape[1]
+    if first_row is None:
+        first_row = (L - 1) // B
+    _check(lib().hisa_block_summary_update(_ptr(kidx), _str3(kidx, "bt"), b, int(L), d, B,
+                                           _ptr(proj), _ptr(summary), _ptr(split), cap,
+                                           int(first_row), _stream()))
     return summary, split
 
 

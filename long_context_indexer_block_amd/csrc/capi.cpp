@@ -87,8 +87,37 @@ hisa_status_t hisa_block_summary(const void* kidx, hisa_strides_t ks, int batch,
   return hip_status(hisa::launch_block_summary(static_cast<const uint16_t*>(kidx), s3(ks), batch,
                                                L, d, B, static_cast<const uint16_t*>(proj),
                                                summary, static_cast<uint16_t*>(split),
+                                               (L + B - 1) / B, 0,
                                                static_cast<hipStream_t>(stream)),
                     "hisa_block_summary");
+}
+
+hisa_status_t hisa_block_summary_update(const void* kidx, hisa_strides_t ks, int batch, int L,
+                                        int d, int B, const void* proj, float* summary,
+                                        void* split, int n_rows_cap, int first_row,
+                                        hisa_stream_t stream) {
+  CHECK(kidx != nullptr, HISA_ERR_NULL, "kidx is NULL");
+  CHECK(summary != nullptr || split != nullptr, HISA_ERR_NULL, "summary and split both NULL");
+  CHECK(batch >= 1 && L >= 1, HISA_ERR_SHAPE, "batch=%d L=%d must be >= 1", batch, L);
+  hisa_status_t st;
+  if ((st = check_d(d)) != HISA_OK) return st;
+  if ((st = check_block(B)) != HISA_OK) return st;
+  if ((st = check_bf16(kidx, ks, "kidx")) != HISA_OK) return st;
+  CHECK(proj == nullptr || aligned16(proj), HISA_ERR_SHAPE, "proj must be 16-byte aligned");
+  CHECK(summary == nullptr || aligned16(summary), HISA_ERR_SHAPE, "summary must be 16-byte aligned");
+  CHECK(split == nullptr || aligned16(split), HISA_ERR_SHAPE, "split must be 16-byte aligned");
+  const int n_rows = (L + B - 1) / B;
+  CHECK(n_rows_cap >= n_rows, HISA_ERR_SHAPE, "n_rows_cap=%d below ceil(L/B)=%d", n_rows_cap,
+        n_rows);
+  CHECK(first_row >= 0 && first_row < n_rows, HISA_ERR_SHAPE,
+        "first_row=%d must be in [0, ceil(L/B)=%d)", first_row, n_rows);
+  CHECK(n_rows_cap <= 2147483647 / batch, HISA_ERR_SHAPE, "too many blocks");
+  return hip_status(hisa::launch_block_summary(static_cast<const uint16_t*>(kidx), s3(ks), batch,
+                                               L, d, B, static_cast<const uint16_t*>(proj),
+                                               summary, static_cast<uint16_t*>(split),
+                                               n_rows_cap, first_row,
+                                               static_cast<hipStream_t>(stream)),
+                    "hisa_block_summary_update");
 }
 
 hisa_status_t hisa_block_score(const void* qidx, hisa_strides_t qs, const int32_t* q_pos,

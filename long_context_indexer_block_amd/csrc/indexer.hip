@@ -19,14 +19,17 @@ namespace hisa {
 // sums through LDS, optionally project with proj (fp32, fixed order), and
 // write the mean plus the exact bf16 hi/mid/lo split of the (projected) sum.
 template <int D>
+// Row c = first_row + blockIdx.x of sequence blockIdx.y; tables hold n_rows
+// rows per sequence.
 __global__ __launch_bounds__(256) void block_summary_kernel(
     const uint16_t* __restrict__ kidx, int64_t ksb, int64_t kst, int L, int B, int n_rows,
-    const uint16_t* __restrict__ proj, float* __restrict__ summary, uint16_t* __restrict__ split) {
+    int first_row, const uint16_t* __restrict__ proj, float* __restrict__ summary,
+    uint16_t* __restrict__ split) {
   constexpr int TPR = D / 8;      // threads per row (8 columns each)
   constexpr int RP = 256 / TPR;   // rows summed in parallel
   __shared__ float part[RP][D + 1];
   __shared__ float sums[D];
-  const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int c = first_row + blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int col0 = (tid % TPR) * 8, r0 = tid / TPR;
   const int j0 = c * B, j1 = min(L, j0 + B);
   const uint16_t* base = kidx + b * ksb;
@@ -83,15 +86,15 @@ __global__ __launch_bounds__(256) void block_summary_kernel(
 
 hipError_t launch_block_summary(const uint16_t* kidx, Str3 ks, int batch, int L, int d, int B,
                                 const uint16_t* proj, float* summary, uint16_t* split,
-                                hipStream_t s) {
+                                int n_rows_cap, int first_row, hipStream_t s) {
   const int n_rows = (L + B - 1) / B;
-  dim3 grid(n_rows, batch);
+  dim3 grid(n_rows - first_row, batch);
   if (d == 64)
     hipLaunchKernelGGL(block_summary_kernel<64>, grid, dim3(256), 0, s, kidx, ks.b, ks.t, L, B,
-                       n_rows, proj, summary, split);
+                       n_rows_cap, first_row, proj, summary, split);
   else
     hipLaunchKernelGGL(block_summary_kernel<128>, grid, dim3(256), 0, s, kidx, ks.b, ks.t, L, B,
-                       n_rows, proj, summary, split);
+                       n_rows_cap, first_row, proj, summary, split);
   return hipGetLastError();
 }
 

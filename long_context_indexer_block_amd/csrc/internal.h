@@ -13,9 +13,10 @@ struct Str3 {
 };
 
 // indexer.hip
+// rows first_row .. ceil(L/B)-1 of tables with n_rows_cap rows per sequence
 hipError_t launch_block_summary(const uint16_t* kidx, Str3 ks, int batch, int L, int d, int B,
                                 const uint16_t* proj, float* summary, uint16_t* split,
-                                hipStream_t s);
+                                int n_rows_cap, int first_row, hipStream_t s);
 hipError_t launch_block_score(const uint16_t* qidx, Str3 qs, const int32_t* q_pos, int batch,
                               int nq, const uint16_t* split, int n_rows, int d, int B,
                               float* scores, hipStream_t s);

@@ -5,6 +5,8 @@ HierPipeline: block summary -> block score -> top-m blocks -> token top-k
 FlatPipeline: flat indexer top-k -> sparse attention (the comparison path).
 AutoPipeline: one of the two by the runtime policy of hisa_auto_plan (flat
               below 8192 keys, m = max(64, L // 2000)).
+DecodeSession: batched decode over caches that grow in place; appending
+              tokens recomputes only the summary rows of the blocks they touch.
 HilsDecode:   chunk keys (once per cache) -> chunk scores -> top-m chunks
               -> two-level softmax attention (HiLS chapter).
 """
@@ -13,7 +15,8 @@ from __future__ import annotations
 import torch
 
 from . import (flat_indexer_topk, flat_indexer_topk_workspace_bytes, hils_two_level_attn_fwd,
-               hisa_auto_plan, hisa_block_score, hisa_block_summary, hisa_select_blocks,
+               hisa_auto_plan, hisa_block_score, hisa_block_summary, hisa_block_summary_update,
+               hisa_select_blocks,
                hisa_token_select, hisa_token_select_workspace_bytes, sparse_attn_fwd,
                sparse_attn_workspace)
 
@@ -116,6 +119,67 @@ class AutoPipeline:
 
     def run(self):
         return self.path.run()
+
+
+class DecodeSession:
+    """One new query per sequence per step over caches with room to grow.
+
+    kidx [b, Lmax, d], k [b, Lmax, Hkv, Dk], v [b, Lmax, Hkv, Dv] are the
+    caller's caches; the first L tokens are valid. The summary table keeps a
+    row for every block the caches can reach. After the caller writes new
+    tokens behind the valid ones, grow(L_new) recomputes only the rows of the
+    blocks those tokens fall in; step(q, qidx) runs block scores, top-m blocks,
+    token top-k and attention for the queries at position L-1."""
+
+    def __init__(self, kidx, k, v, L, Hq, B, m, k_top, scale):
+        from . import lib, sparse_attn_workspace  # noqa: F401
+        self.kidx, self.kc, self.vc = kidx, k, v
+        self.B, self.m, self.k_top, self.scale = B, m, k_top, scale
+        b, Lmax, d = kidx.shape
+        dev = kidx.device
+        cap = -(-Lmax // B)
+        self.split = torch.empty(b, cap, 3, d, dtype=torch.bfloat16, device=dev)
+        self.q_pos = torch.empty(b, 1, dtype=torch.int32, device=dev)
+        self.block_scores = torch.empty(b, 1, cap, dtype=torch.float32, device=dev)
+        self.block_idx = torch.empty(b, 1, m, dtype=torch.int32, device=dev)
+        self.token_idx = torch.empty(b, 1, k_top, dtype=torch.int32, device=dev)
+        nbytes = hisa_token_select_workspace_bytes(b, 1, Lmax, B, m, k_top)
+        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        Hkv, Dk, Dv = k.shape[2], k.shape[3], v.shape[3]
+        n = lib().sparse_attn_fwd_workspace_bytes(b, 1, Hq, Hkv, Dk, Dv, k_top)
+        self.attn_ws = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
+        self.out = torch.empty(b, 1, Hq, Dv, dtype=torch.bfloat16, device=dev)
+        self.L = 0
+        self.grow(L)
+
+    def grow(self, L_new):
+        """The caches now hold L_new tokens: refresh the rows of the blocks
+        from the one holding the first new token on."""
+        assert self.L < L_new <= self.kidx.shape[1]
+        hisa_block_summary_update(self.kidx, L_new, self.B, None, self.split,
+                                  first_row=self.L // self.B)
+        self.L = L_new
+        self.q_pos.fill_(L_new - 1)
+
+    def step(self, q, qidx):
+        """q [b, 1, Hq, Dk], qidx [b, 1, d]: the queries at position L-1."""
+        L = self.L
+        hisa_block_score(qidx, self.q_pos, self.split, self.B, out=self.block_scores)
+        hisa_select_blocks(self.block_scores, self.q_pos, self.B, self.m, out=self.block_idx)
+        hisa_token_select(qidx, self.kidx[:, :L], self.q_pos, self.block_idx, self.B, self.k_top,
+                          token_idx=self.token_idx, want_scores=False, workspace=self.ws)
+        sparse_attn_fwd(q, self.kc[:, :L], self.vc[:, :L], self.token_idx, self.scale,
+                        out=self.out, workspace=self.attn_ws)
+        return self.out
+
+    def capture(self, q, qidx):
+        """step(q, qidx) at the current length as a HIP graph: copy the next
+        queries into q and qidx, then replay() (the step enqueues kernel
+        launches only, no allocation and no memset). Valid until grow()."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step(q, qidx)
+        return g
 
 
 class HilsDecode:

@@ -13,8 +13,8 @@ import torch
 
 import long_context_indexer_block_amd as H
 import oracle.hisa_oracle as O
-from long_context_indexer_block_amd.pipeline import (AutoPipeline, FlatPipeline, HierPipeline,
-                                                     HilsDecode)
+from long_context_indexer_block_amd.pipeline import (AutoPipeline, DecodeSession, FlatPipeline,
+                                                     HierPipeline, HilsDecode)
 from parity import (SeqOracle, check_attention, check_index_rows, check_score_rows, f64, log)
 from workloads import WORKLOADS, Workload, make_inputs, sample_positions
 
@@ -192,6 +192,56 @@ def test_auto_pipeline(L, hier):
     ti = a.token_idx.cpu().numpy()
     ref = [so.hier(x, 64, w.k)[2] if hier else so.flat(x, w.k)[0] for x in rows]
     check_index_rows(ti[0, rows], np.stack(ref), "auto token_idx")
+
+
+def test_decode_session_grows_like_a_rebuild():
+    # caches with room to grow: each grow() recomputes only the summary rows
+    # of the blocks the new tokens fall in; every step must equal a pipeline
+    # built from scratch at that length (same kernels: bit-exact)
+    w = _mk("grow", kind="decode", batch=3, L=1000, B=64, m=4, k=100, d_idx=64, Hq=4, Hkv=1)
+    log(f"case decode session {w}")
+    inp = make_inputs(w, DEV, seed=10)
+    kidx, k, v, q, qidx = inp["kidx"], inp["k"], inp["v"], inp["q"], inp["qidx"]
+    s = DecodeSession(kidx, k, v, 700, w.Hq, w.B, w.m, w.k, w.scale)
+    for L in (700, 701, 703, 704, 705, 735, 768, 769, 1000):
+        if L != s.L:
+            s.grow(L)
+        s.step(q, qidx)
+        pos = torch.full((w.batch, 1), L - 1, dtype=torch.int32, device=DEV)
+        r = HierPipeline(kidx[:, :L], qidx, pos, q, k[:, :L], v[:, :L], w.B, w.m, w.k, w.scale)
+        r.run()
+        torch.cuda.synchronize()
+        n = -(-L // w.B)
+        assert torch.equal(s.split[:, :n], r.split), L
+        assert torch.equal(s.block_idx, r.block_idx) and torch.equal(s.token_idx, r.token_idx), L
+        assert torch.equal(s.out, r.out), L
+    # the incrementally built rows against the oracle (integer keys: exact)
+    for b in range(w.batch):
+        ref = O.block_summary(f64(kidx[b]), w.B)
+        cnt = np.array([min(1000, (c + 1) * w.B) - c * w.B for c in range(ref.shape[0])])
+        np.testing.assert_array_equal(f64(s.split[b]).sum(axis=1), np.rint(ref * cnt[:, None]))
+
+
+def test_decode_graph_replays_match_eager():
+    # the decode step as a HIP graph; each replay (with eager work and a
+    # synchronisation in between) must equal the eager step on the same queries
+    w = _mk("graph", kind="decode", batch=4, L=6000, B=128, m=8, k=512, d_idx=128, Hq=16, Hkv=1)
+    log(f"case decode graph {w}")
+    inp = make_inputs(w, DEV, seed=11)
+    s = DecodeSession(inp["kidx"], inp["k"], inp["v"], w.L, w.Hq, w.B, w.m, w.k, w.scale)
+    q, qidx = inp["q"].clone(), inp["qidx"].clone()
+    g = s.capture(q, qidx)
+    gen = torch.Generator(device=DEV).manual_seed(12)
+    for rep in range(4):
+        q.copy_(torch.randn(q.shape, generator=gen, device=DEV).to(torch.bfloat16))
+        qidx.copy_(torch.randint(-8, 9, qidx.shape, generator=gen, device=DEV).to(torch.bfloat16))
+        g.replay()
+        torch.cuda.synchronize()
+        got_idx, got_out = s.token_idx.clone(), s.out.clone()
+        s.step(q, qidx)  # eager, on the same queries
+        torch.cuda.synchronize()
+        assert torch.equal(got_idx, s.token_idx), rep
+        assert torch.equal(got_out, s.out), rep
 
 
 def test_determinism_and_decode_matches_prefill_row():
