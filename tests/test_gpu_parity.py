@@ -328,34 +328,62 @@ def _hils_check(w, exact):
     torch.cuda.synchronize()
     t = w.L - 1
     Wp = f64(inp["w_proj"])
-    got_idx = hd.chunk_idx.view(w.Hq, m).cpu().numpy()
-    out = hd.out[0].float().cpu().numpy()
+    got_idx = hd.chunk_idx.view(w.batch, w.Hq, m).cpu().numpy()
+    outs = hd.out.float().cpu().numpy()
     excluded = 0
-    for h in range(w.Hq):
-        K = f64(inp["k"][0, :, h])
-        V = f64(inp["v"][0, :, h])
-        q = f64(inp["q"][0, h])
-        khat = O.block_summary(K, C, proj=Wp)
-        ref_out, ref_idx = O.hils_decode_head(q, K, V, khat, t, C, m, sc, sc)
-        if exact:
-            check_index_rows(got_idx[h:h + 1], ref_idx[None], f"hils int chunk_idx h={h}")
-            check_score_rows(hd.khat[h].cpu().numpy(), khat, f"hils int khat h={h}")
-        elif not np.array_equal(got_idx[h], ref_idx):
-            # N(0,1) chunk scores are not exact in fp32: accept a different set
-            # only when the oracle's last kept and first dropped free scores are
-            # closer than an fp32 error bound of the two dot products.
-            raw = khat @ q
-            b = t // C
-            cand = np.arange(1, b)
-            order = cand[np.lexsort((cand, -raw[cand]))]
-            gap = raw[order[m - 3]] - raw[order[m - 2]]
-            bound = 4 * 2.0 ** -24 * w.Dk * 2 * np.abs(khat[order[m - 3:m - 1]] * q).sum()
-            assert gap <= bound, f"hils h={h}: chunk sets differ with gap {gap} > {bound}"
-            excluded += 1
-            continue
-        mx, mean, rel = check_attention(out[h:h + 1], ref_out[None], f"hils out h={h}")
+    for b in range(w.batch):
+        for h in range(w.Hq):
+            K = f64(inp["k"][b, :, h])
+            V = f64(inp["v"][b, :, h])
+            q = f64(inp["q"][b, h])
+            khat = O.block_summary(K, C, proj=Wp)
+            ref_out, ref_idx = O.hils_decode_head(q, K, V, khat, t, C, m, sc, sc)
+            if exact:
+                check_index_rows(got_idx[b, h:h + 1], ref_idx[None],
+                                 f"hils int chunk_idx b={b} h={h}")
+                # complete chunks: a mean over a power-of-two count, exact; a
+                # partial last chunk: one division by its token count
+                full = w.L // C
+                gk = hd.khat[b * w.Hq + h].cpu().numpy()
+                check_score_rows(gk[:full], khat[:full], f"hils int khat b={b} h={h}")
+                if full < khat.shape[0]:
+                    np.testing.assert_allclose(gk[full:], khat[full:], rtol=2e-7, atol=1e-5)
+            elif not np.array_equal(got_idx[b, h], ref_idx):
+                # N(0,1) chunk scores are not exact in fp32: accept a different
+                # set only when the oracle's last kept and first dropped free
+                # scores are closer than an fp32 error bound of the two dot
+                # products.
+                raw = khat @ q
+                bt = t // C
+                cand = np.arange(1, bt)
+                order = cand[np.lexsort((cand, -raw[cand]))]
+                gap = raw[order[m - 3]] - raw[order[m - 2]]
+                bound = 4 * 2.0 ** -24 * w.Dk * 2 * np.abs(khat[order[m - 3:m - 1]] * q).sum()
+                assert gap <= bound, f"hils b={b} h={h}: chunk sets differ with gap {gap} > {bound}"
+                excluded += 1
+                continue
+            check_attention(outs[b, h:h + 1], ref_out[None], f"hils out b={b} h={h}")
     log(f"  hils exact={exact}: heads excluded as near-ties: {excluded}")
     return excluded
+
+
+# small two-level decodes in the integer twin (exact routing): head width 128,
+# chunks of 128 and 256 tokens (several 64-token groups each), a partial local
+# chunk, m = 64 (four chunks per wave), two sequences
+HILS_SMALL = [
+    WORKLOADS["hils_decode_1m"].with_(name="hils_d128_c128", batch=2, L=5000, B=128, m=8, Hq=4,
+                                      Hkv=4, Dk=128, Dv=128, d_idx=128, int_mode=True),
+    WORKLOADS["hils_decode_1m"].with_(name="hils_c256", batch=1, L=3000, B=256, m=6, Hq=3, Hkv=3,
+                                      int_mode=True),
+    WORKLOADS["hils_decode_1m"].with_(name="hils_c64_m64", batch=2, L=4100, B=64, m=64, Hq=2,
+                                      Hkv=2, int_mode=True),
+]
+
+
+@pytest.mark.parametrize("w", HILS_SMALL, ids=[w.name for w in HILS_SMALL])
+def test_hils_small(w):
+    log(f"case hils small {w}")
+    assert _hils_check(w, exact=True) == 0
 
 
 def test_workload_hils_decode_int_twin():
