@@ -224,12 +224,165 @@ __global__ __launch_bounds__(NT) void select_blocks_kernel(
   }
 }
 
+// The same selection without workgroup barriers. A wave holds its candidates
+// item-major (item i of lane l is position base + 64i + l) as order-preserving
+// 32-bit keys (0, below every finite score's key, for no candidate), finds the
+// K-th largest by bisection on the key (each step one comparison per item,
+// counted on the scalar unit from the comparison's lane mask), and writes the kept ones
+// in position order with ballots: those above the threshold and the first
+// `need` equal to it. With W > 1 waves, wave w keeps the best K of its slice
+// of 64*IT candidates (each of the K best overall is among the K best of its
+// slice under the same order), the kept keys and positions meet in LDS in
+// position order, and wave 0 selects the best K of those.
+struct WaveSel {
+  uint32_t T;     // threshold key: keys > T kept
+  uint32_t need;  // plus the first `need` keys == T
+};
+
+template <int IT>
+__device__ __forceinline__ WaveSel wave_select(const uint32_t (&key)[IT], uint32_t okm,
+                                               uint32_t K) {
+  float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    if ((okm >> i) & 1u) {
+      const float f = key_value(key[i]);
+      mn = fminf(mn, f);
+      mx = fmaxf(mx, f);
+    }
+  }
+  uint32_t lo = order_key(wave_ext_dpp<false>(mn)), hi = order_key(wave_ext_dpp<true>(mx));
+  // the largest key x with count(key >= x) >= K (keys of no candidate are 0 < lo)
+  while (lo < hi) {
+    const uint32_t mid = lo + ((hi - lo + 1u) >> 1);
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) c += static_cast<uint32_t>(__popcll(__ballot(key[i] >= mid)));
+    if (c >= K) lo = mid; else hi = mid - 1u;
+  }
+  uint32_t gt = 0;
+#pragma unroll
+  for (int i = 0; i < IT; ++i) gt += static_cast<uint32_t>(__popcll(__ballot(key[i] > lo)));
+  return WaveSel{lo, K - gt};
+}
+
+template <int IT, class Emit>
+__device__ __forceinline__ void wave_compact(const uint32_t (&key)[IT], uint32_t okm,
+                                             const WaveSel s, Emit emit) {
+  uint32_t kept = 0, ties = 0;
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const bool ok = (okm >> i) & 1u;
+    const bool eq = ok && key[i] == s.T;
+    const uint64_t em = __ballot(eq);
+    const bool keep = ok && (key[i] > s.T || (eq && ties + lanes_below(em) < s.need));
+    const uint64_t km = __ballot(keep);
+    if (keep) emit(i, kept + lanes_below(km));
+    ties += static_cast<uint32_t>(__popcll(em));
+    kept += static_cast<uint32_t>(__popcll(km));
+  }
+}
+
+constexpr int kSelUnion = 1024;  // LDS entries for the waves' kept candidates
+
+template <int W, int IT>
+__global__ __launch_bounds__(64 * W) void select_blocks_wave_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ q_pos, int nq, int n_rows,
+    int B, int m, int32_t* __restrict__ block_idx) {
+  constexpr int S = 64 * IT;  // candidates per wave
+  constexpr int CAP = W > 1 ? kSelUnion : 1;
+  __shared__ uint32_t ckey[CAP];
+  __shared__ int cpos[CAP];
+  __shared__ int ccnt[W];
+  const int64_t qi = static_cast<int64_t>(blockIdx.y) * nq + blockIdx.x;
+  const float* row = scores + qi * n_rows;
+  int32_t* out = block_idx + qi * m;
+  const int t = min(max(q_pos[qi], 0), n_rows * B - 1);
+  const int bt = t / B;
+  const int n = max(bt - 1, 0);
+  const int K = m - (bt == 0 ? 1 : 2);  // free slots
+  if (n <= K) {
+    for (int i = threadIdx.x; i < m; i += 64 * W) out[i] = i <= bt ? i : -1;
+    return;
+  }
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = lane_id();
+  const int base = w * S;
+  uint32_t key[IT];
+  uint32_t okm = 0;
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int p = base + 64 * i + l;
+    key[i] = p < n ? order_key(row[1 + p]) : 0u;
+    okm |= p < n ? (1u << i) : 0u;
+  }
+  if constexpr (W == 1) {
+    if (K > 0) {
+      const WaveSel sel = wave_select(key, okm, static_cast<uint32_t>(K));
+      wave_compact(key, okm, sel, [&](int i, uint32_t pos) { out[1 + pos] = 64 * i + l + 1; });
+    }
+  } else {
+    const int kw = min(K, max(0, min(S, n - base)));  // kept by this wave
+    if (kw > 0) {
+      const WaveSel sel = wave_select(key, okm, static_cast<uint32_t>(kw));
+      wave_compact(key, okm, sel, [&](int i, uint32_t pos) {
+        ckey[w * K + pos] = key[i];
+        cpos[w * K + pos] = base + 64 * i + l;
+      });
+    }
+    if (l == 0) ccnt[w] = kw;
+    __syncthreads();
+    if (w == 0 && K > 0) {
+      // entry e = u*K + j is the j-th kept candidate of wave u: position order
+      constexpr int IB = CAP / 64;
+      uint32_t k2[IB];
+      uint32_t ok2 = 0;
+#pragma unroll
+      for (int i = 0; i < IB; ++i) {
+        const int e = 64 * i + l;
+        const int u = e / K;
+        const bool ok = u < W && e - u * K < ccnt[min(u, W - 1)];
+        k2[i] = ok ? ckey[e] : 0u;
+        ok2 |= ok ? (1u << i) : 0u;
+      }
+      const WaveSel sel = wave_select(k2, ok2, static_cast<uint32_t>(K));
+      wave_compact(k2, ok2, sel, [&](int i, uint32_t pos) { out[1 + pos] = cpos[64 * i + l] + 1; });
+    }
+  }
+  if (threadIdx.x == 0) {
+    out[0] = 0;
+    out[1 + K] = bt;
+  }
+}
+
 hipError_t launch_select_blocks(const float* scores, const int32_t* q_pos, int batch, int nq,
                                 int n_rows, int B, int m, int32_t* block_idx, hipStream_t s) {
   dim3 grid(nq, batch);
-  if (n_rows <= 64 * 16)
-    hipLaunchKernelGGL((select_blocks_kernel<64, 16, true>), grid, dim3(64), 0, s, scores, q_pos,
-                       nq, n_rows, B, m, block_idx);
+#define HISA_SW(W_, IT_)                                                                        \
+  hipLaunchKernelGGL((select_blocks_wave_kernel<W_, IT_>), grid, dim3(64 * W_), 0, s, scores,   \
+                     q_pos, nq, n_rows, B, m, block_idx)
+  // The wave select trades latency for throughput: a wave's ~32 dependent
+  // bisection steps are slower than the histogram select's few levels when
+  // only a few queries run, and faster once many queries fill the chip.
+  const bool many = static_cast<int64_t>(batch) * nq >= 1024;
+  // candidates are blocks 1 .. n_rows-2 at most
+  if (!many) {
+    if (n_rows <= 64 * 16)
+      hipLaunchKernelGGL((select_blocks_kernel<64, 16, true>), grid, dim3(64), 0, s, scores,
+                         q_pos, nq, n_rows, B, m, block_idx);
+    else if (n_rows <= 1024 * 16)
+      hipLaunchKernelGGL((select_blocks_kernel<1024, 16, true>), grid, dim3(1024), 0, s, scores,
+                         q_pos, nq, n_rows, B, m, block_idx);
+    else
+      hipLaunchKernelGGL((select_blocks_kernel<1024, 16, false>), grid, dim3(1024), 0, s, scores,
+                         q_pos, nq, n_rows, B, m, block_idx);
+  } else if (n_rows <= 64 + 2) HISA_SW(1, 1);
+  else if (n_rows <= 128 + 2) HISA_SW(1, 2);
+  else if (n_rows <= 256 + 2) HISA_SW(1, 4);
+  else if (n_rows <= 512 + 2) HISA_SW(1, 8);
+  else if (n_rows <= 1024 + 2) HISA_SW(1, 16);
+  else if (n_rows <= 16 * 1024 && (m - 2) * 16 <= kSelUnion) HISA_SW(16, 16);
+#undef HISA_SW
+  // many kept blocks: the workgroup-wide histogram select
   else if (n_rows <= 1024 * 16)
     hipLaunchKernelGGL((select_blocks_kernel<1024, 16, true>), grid, dim3(1024), 0, s, scores,
                        q_pos, nq, n_rows, B, m, block_idx);

@@ -116,6 +116,34 @@ def test_block_summary_exact(L, B, d, proj):
         np.testing.assert_array_equal(tot, np.rint(ref * cnt[:, None]))
 
 
+@pytest.mark.parametrize("nq", [24, 512], ids=["few_queries", "many_queries"])
+@pytest.mark.parametrize("n_rows,m", [(40, 8), (130, 12), (1026, 64), (5000, 40), (16384, 32),
+                                      (3000, 70)])
+def test_select_blocks_ties(n_rows, m, nq):
+    # integer scores from a narrow range (many ties at the threshold, +0.0 and
+    # -0.0 among them). Few queries take the workgroup histogram select; from
+    # 1024 queries on, one wave per query up to 1024 candidates, 16 waves and
+    # a union of their kept candidates beyond (the histogram select when the
+    # union would not fit). Exact sets against the oracle.
+    B = 64
+    log(f"case select_blocks n_rows={n_rows} m={m} nq={nq}")
+    g = torch.Generator(device="cpu").manual_seed(n_rows * 131 + m)
+    sc = torch.randint(-5, 6, (2, nq, n_rows), generator=g).float()
+    neg0 = (sc == 0) & (torch.rand(sc.shape, generator=g) < 0.5)
+    sc = torch.where(neg0, torch.tensor(-0.0), sc)
+    pos = torch.randint(0, n_rows * B, (2, nq), generator=g, dtype=torch.int32)
+    pos[:, 0] = n_rows * B - 1          # the most candidates
+    pos[:, 1] = 0                       # block 0 only
+    pos[:, 2] = B * (m - 1)             # exactly enough blocks for all of them
+    pos[:, 3] = B * m                   # one candidate too many
+    out = H.hisa_select_blocks(sc.to(DEV), pos.to(DEV), B, m).cpu().numpy()
+    rows = list(range(nq)) if nq <= 64 else list(range(8)) + list(range(8, nq, 13))
+    for b in range(2):
+        ref = np.stack([O.select_blocks_for_query(sc[b, i].double().numpy(), int(pos[b, i]), B, m)
+                        for i in rows])
+        check_index_rows(out[b, rows], ref, f"select_blocks b={b}")
+
+
 @pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
 def test_hier_pipeline_small(w):
     log(f"case hier {w}")
