@@ -418,7 +418,7 @@ __device__ __forceinline__ float r_load(const float* row, int r, int nrows, int 
 }
 // The register budget allows 5 waves per SIMD: the kernel is latency bound
 // (barriers, LDS atomics), so more resident workgroups hide more of it.
-template <int RW, int W>
+template <int RW, int W, int NS>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(5, 8))) void
 token_topk_rows_kernel(const float* __restrict__ scores, const int32_t* __restrict__ block_idx,
                        const int32_t* __restrict__ q_pos, int m, int B, int k, int L,
@@ -436,16 +436,18 @@ token_topk_rows_kernel(const float* __restrict__ scores, const int32_t* __restri
   const int nrows = (m * B) >> 6;
   const float* row = scores + qi * static_cast<int64_t>(m) * B;
   const float qnan = __uint_as_float(0x7fc00000u);
-  // the slots' block ids, one per lane in four registers (m <= 256), read by
+  // the slots' block ids, one per lane in NS registers (m <= 64*NS), read by
   // row with readlane; a slot that is empty or past the end of the keys gets -1
-  int cv[4];
+  int cv[NS];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NS; ++j) {
     const int c = 64 * j + l < m ? block_idx[qi * m + 64 * j + l] : -1;
     cv[j] = c >= 0 && c < nblk ? c : -1;
   }
   auto slot_block = [&](int sl) {  // sl is wave-uniform
-    const int v = sl < 128 ? (sl < 64 ? cv[0] : cv[1]) : (sl < 192 ? cv[2] : cv[3]);
+    int v = cv[0];
+#pragma unroll
+    for (int j = 1; j < NS; ++j) v = sl >= 64 * j ? cv[j] : v;
     return __builtin_amdgcn_readlane(v, sl & 63);
   };
   float v[RW];
@@ -620,8 +622,14 @@ hipError_t launch_token_select(const uint16_t* qidx, Str3 qs, const uint16_t* ki
     const int nrows = m * B / 64;
     const dim3 gr(static_cast<unsigned>(nq_total));
 #define HISA_TR(R_, W_)                                                                        \
-  hipLaunchKernelGGL((token_topk_rows_kernel<R_, W_>), gr, dim3(64 * W_), stage_bytes, s,       \
-                     w.scores, block_idx, q_pos, m, B, k, L, token_idx, token_scores)
+  do {                                                                                        \
+    if (m <= 128)                                                                             \
+      hipLaunchKernelGGL((token_topk_rows_kernel<R_, W_, 2>), gr, dim3(64 * W_), stage_bytes,   \
+                         s, w.scores, block_idx, q_pos, m, B, k, L, token_idx, token_scores);  \
+    else                                                                                      \
+      hipLaunchKernelGGL((token_topk_rows_kernel<R_, W_, 4>), gr, dim3(64 * W_), stage_bytes,   \
+                         s, w.scores, block_idx, q_pos, m, B, k, L, token_idx, token_scores);  \
+  } while (0)
     if (nq_total < kFewQueries) {
       // few queries (decode): kWideW waves per query, so that the CUs that get
       // a workgroup hold enough waves to hide the latency of each step
