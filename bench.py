@@ -227,6 +227,28 @@ def timed(calls, steps, warmup):
     return wall, stage
 
 
+def graph_ms(call_groups, steps):
+    """Capture each list of calls as one HIP graph (the calls enqueue kernel
+    launches only) and time `steps` replays, round-robin over the graphs,
+    with the host clock between synchronisations. Returns ms per replay."""
+    import torch
+    graphs = []
+    for calls in call_groups:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in calls:
+                c()
+        graphs.append(g)
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        graphs[s % len(graphs)].replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
 def base_record(w, a, nq, wall, dtype="bf16"):
     ms_step = wall * 1e3 / a.steps
     return {
@@ -269,6 +291,9 @@ def bench_prefill(w, a, inp):
     res["config"]["kv"] = ("MLA latent, V = first 512 columns of K" if w.mla else
                            f"{w.Hkv} kv head(s)")
     res["stage_ms"] = stage_ms
+    # the same step replayed as one HIP graph (no per-launch host cost)
+    g_ms = graph_ms([calls], a.steps)
+    res["graph"] = {"ms_per_step": g_ms, "queries_per_s": nq / (g_ms * 1e-3)}
     traffic = measured_traffic() if (w.mla and w.name == "prefill_64k_mla") else None
     res["roofline"] = {"kernel": f"sparse_attn ({w.Hq} heads, Dk {w.Dk}, Dv {w.Dv})",
                        "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
@@ -338,24 +363,11 @@ def bench_decode(w, a, inp):
     res["stage_ms"] = dict(zip(stages, stage))
     res["summary_build_ms"] = summary_ms
     # the same step captured as HIP graphs, one per query set, and replayed:
-    # the launch cost of the eight kernels goes away
-    graphs = []
-    for i in range(4):
+    # the per-launch host cost goes away
+    def use(i):
         p.qidx, p.q = qsets[i], qs[i]
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for c in calls[1:]:
-                c()
-        graphs.append(g)
-    for g in graphs:
-        g.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s_ in range(a.steps):
-        graphs[s_ % 4].replay()
-    torch.cuda.synchronize()
-    gwall = time.perf_counter() - t0
-    res["graph"] = {"ms_per_step": gwall * 1e3 / a.steps, "queries_per_s": nq * a.steps / gwall}
+    g_ms = graph_ms([[lambda i=i: use(i)] + calls[1:] for i in range(4)], a.steps)
+    res["graph"] = {"ms_per_step": g_ms, "queries_per_s": nq / (g_ms * 1e-3)}
     # per-step compulsory HBM bytes: summaries (hi/mid/lo), the kept blocks'
     # keys, the kept tokens' K and V rows
     n_sel = int((p.token_idx >= 0).sum().item())
