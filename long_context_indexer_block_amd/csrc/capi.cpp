@@ -127,7 +127,7 @@ hisa_status_t hisa_block_score(const void* qidx, hisa_strides_t qs, const int32_
         "qidx, q_pos, split and block_scores are required");
   CHECK(batch >= 1 && nq >= 1 && n_rows >= 1, HISA_ERR_SHAPE,
         "batch=%d nq=%d n_rows=%d must be >= 1", batch, nq, n_rows);
-  CHECK(nq <= 65535 * 64 && batch <= 65535, HISA_ERR_UNSUPPORTED, "grid too large");
+  CHECK(n_rows <= 65535 * 64 && batch <= 65535, HISA_ERR_UNSUPPORTED, "grid too large");
   hisa_status_t st;
   if ((st = check_d(d)) != HISA_OK) return st;
   if ((st = check_block(B)) != HISA_OK) return st;

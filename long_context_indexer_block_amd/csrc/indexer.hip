@@ -100,10 +100,13 @@ hipError_t launch_block_summary(const uint16_t* kidx, Str3 ks, int batch, int L,
 
 // ------------------------------------------------------------------ scores
 // Tile: 64 queries x 64 blocks per workgroup, 16 queries per wave. The
-// contraction q . (hi + mid + lo) runs on the bf16 matrix cores with fp32
+// contraction (hi + mid + lo) . q runs on the bf16 matrix cores with fp32
 // accumulation (K = 3*D); for integer-valued keys every partial sum is an
 // integer below 2^24, so the score is exact, then scaled by 1/B (exact for
-// a power-of-two B).
+// a power-of-two B). The summaries are the A operand (rows = blocks) and the
+// queries the B operand, so each lane ends with four consecutive blocks of
+// one query and stores them with one 16-byte write. The twelve fragments of
+// a 16-block step are loaded together.
 template <int D>
 __global__ __launch_bounds__(256) void block_score_kernel(
     const uint16_t* __restrict__ qidx, int64_t qsb, int64_t qst, const int32_t* __restrict__ q_pos,
@@ -112,49 +115,55 @@ __global__ __launch_bounds__(256) void block_score_kernel(
   constexpr int KS = D / 32;
   const int wave = threadIdx.x / kWave, lane = lane_id();
   const int b = blockIdx.z;
-  const int q0 = blockIdx.y * 64 + wave * 16;
-  const int c0 = blockIdx.x * 64;
+  // query tiles vary fastest: consecutive workgroups go to the XCDs in turn,
+  // so each XCD gets every eighth query tile with all its block tiles, and
+  // the causal work (more blocks for later queries) is spread evenly
+  const int q0 = blockIdx.x * 64 + wave * 16;
+  const int c0 = blockIdx.y * 64;
   const int g = lane / 16, r16 = lane % 16;
   if (q0 >= nq) return;
-  // positions of the four output rows this lane stores, and the wave's max
-  int bt_row[4];
+  // this lane's query (column r16 of the products) and its local block
+  const int qq = q0 + r16;
+  const int qc = min(qq, nq - 1);
+  const int bt = qq < nq ? min(max(q_pos[static_cast<int64_t>(b) * nq + qc], 0), n_rows * B - 1) / B
+                         : -1;
+  const int btmax = static_cast<int>(wave_max(static_cast<float>(bt)));
+  // B fragments: the query row of this lane, 8 values per k step
+  const uint16_t* qrow = qidx + b * qsb + static_cast<int64_t>(qc) * qst + 8 * g;
+  bf16x8 qf[KS];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int qq = q0 + 4 * g + r;
-    bt_row[r] = qq < nq ? min(max(q_pos[static_cast<int64_t>(b) * nq + qq], 0), n_rows * B - 1) / B
-                        : -1;
-  }
-  int btmax = max(max(bt_row[0], bt_row[1]), max(bt_row[2], bt_row[3]));
-  btmax = static_cast<int>(wave_max(static_cast<float>(btmax)));
-  // A fragments: the query row of this lane, 8 values per k step.
-  const int qa = min(q0 + r16, nq - 1);
-  const uint16_t* qrow = qidx + b * qsb + static_cast<int64_t>(qa) * qst + 8 * g;
-  bf16x8 a[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) a[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 32 * s));
+  for (int s = 0; s < KS; ++s) qf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 32 * s));
+  float* orow = out + (static_cast<int64_t>(b) * nq + qc) * n_rows;
+  const bool vec = (n_rows & 3) == 0;
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     const int cb = c0 + nt * 16;
     if (cb >= n_rows) break;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     if (cb < btmax) {
+      // A fragments: block cb + r16 of the summary table (hi, mid, lo terms)
       const int cc = min(cb + r16, n_rows - 1);
       const uint16_t* srow = split + (static_cast<int64_t>(b) * n_rows + cc) * 3 * D + 8 * g;
+      uint4 sf[3 * KS];
 #pragma unroll
-      for (int term = 0; term < 3; ++term)
+      for (int x = 0; x < 3 * KS; ++x)
+        sf[x] = *reinterpret_cast<const uint4*>(srow + (x / KS) * D + 32 * (x % KS));
+      __builtin_amdgcn_sched_barrier(0);  // all of them in flight before the first product
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-          acc = mfma16(a[s], as_bf16x8(*reinterpret_cast<const uint4*>(srow + term * D + 32 * s)),
-                       acc);
+      for (int x = 0; x < 3 * KS; ++x) acc = mfma16(as_bf16x8(sf[x]), qf[x % KS], acc);
     }
-    const int c = cb + r16;
-    if (c < n_rows) {
+    // lane: blocks cb + 4g + (0..3) of query qq
+    if (qq < nq) {
+      const int c = cb + 4 * g;
+      float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int qq = q0 + 4 * g + r;
-        if (qq < nq)
-          out[(static_cast<int64_t>(b) * nq + qq) * n_rows + c] =
-              c < bt_row[r] ? acc[r] * invB : -INFINITY;
+      for (int r = 0; r < 4; ++r) v[r] = c + r < bt ? acc[r] * invB : -INFINITY;
+      if (vec && c + 3 < n_rows) {
+        *reinterpret_cast<float4*>(orow + c) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (c + r < n_rows) orow[c + r] = v[r];
       }
     }
   }
@@ -163,7 +172,7 @@ __global__ __launch_bounds__(256) void block_score_kernel(
 hipError_t launch_block_score(const uint16_t* qidx, Str3 qs, const int32_t* q_pos, int batch,
                               int nq, const uint16_t* split, int n_rows, int d, int B,
                               float* scores, hipStream_t s) {
-  dim3 grid((n_rows + 63) / 64, (nq + 63) / 64, batch);
+  dim3 grid((nq + 63) / 64, (n_rows + 63) / 64, batch);
   const float invB = 1.0f / static_cast<float>(B);
   if (d == 64)
     hipLaunchKernelGGL(block_score_kernel<64>, grid, dim3(256), 0, s, qidx, qs.b, qs.t, q_pos, nq,
