@@ -209,13 +209,22 @@ size_t sparse_attn_fwd_workspace_bytes(int batch, int nq, int Hq, int Hkv, int D
  *             run with batch*H sequences (row b*H + h).
  *   chunk_idx int32 [batch*H][m]: chosen chunks (from hisa_select_blocks),
  *             ascending, -1 padded.
- *   out       bf16 [batch][H][D], strides os (batch, head). */
+ *   out       bf16 [batch][H][D], strides os (batch, head).
+ *   workspace optional device scratch of hils_two_level_attn_fwd_workspace_bytes()
+ *             bytes, 256-byte aligned, contents on entry ignored. With it, few
+ *             (sequence, head) pairs spread their chosen chunks over many
+ *             workgroups and merge the chunk results in a second kernel; NULL
+ *             runs one workgroup per pair (same result up to fp32 rounding).
+ *             A non-NULL workspace that is too small is HISA_ERR_WORKSPACE;
+ *             the size is 0 when the shape never splits. */
 hisa_status_t hils_two_level_attn_fwd(const void* q, hisa_strides_t qs, const void* k,
                                       hisa_strides_t ks, const void* v, hisa_strides_t vs,
                                       const float* khat, const int32_t* chunk_idx, int batch,
                                       int L, int H, int D, int C, int n_rows, int m,
                                       float scale_chunk, float scale_token, void* out,
-                                      hisa_strides_t os, hisa_stream_t stream);
+                                      hisa_strides_t os, void* workspace, size_t workspace_bytes,
+                                      hisa_stream_t stream);
+size_t hils_two_level_attn_fwd_workspace_bytes(int batch, int H, int D, int m);
 
 #ifdef __cplusplus
 }

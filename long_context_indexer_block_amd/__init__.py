@@ -51,7 +51,8 @@ _SIGS = {
                              _P, _I, _F, _P, Strides, _P, _P, _S, _P]),
     "sparse_attn_fwd_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I, _I]),
     "hils_two_level_attn_fwd": (_I, [_P, Strides, _P, Strides, _P, Strides, _P, _P, _I, _I, _I,
-                                     _I, _I, _I, _I, _F, _F, _P, Strides, _P]),
+                                     _I, _I, _I, _I, _F, _F, _P, Strides, _P, _S, _P]),
+    "hils_two_level_attn_fwd_workspace_bytes": (_S, [_I, _I, _I, _I]),
 }
 EXPORTS = [n for n in _SIGS]
 
@@ -249,8 +250,17 @@ def sparse_attn_fwd(q, k, v, token_idx, scale, out=None, lse=None, want_lse=Fals
     return (out, lse) if want_lse else out
 
 
-def hils_two_level_attn_fwd(q, k, v, khat, chunk_idx, C, scale_chunk, scale_token, out=None):
-    """q [b, H, D], k/v [b, L, H, D], khat [b*H, n, D] fp32, chunk_idx [b*H, m] -> out [b, H, D]."""
+def hils_workspace(b, H, D, m, device):
+    """Workspace for hils_two_level_attn_fwd on these shapes (None when it needs none)."""
+    n = lib().hils_two_level_attn_fwd_workspace_bytes(b, H, D, m)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def hils_two_level_attn_fwd(q, k, v, khat, chunk_idx, C, scale_chunk, scale_token, out=None,
+                            workspace="auto"):
+    """q [b, H, D], k/v [b, L, H, D], khat [b*H, n, D] fp32, chunk_idx [b*H, m] -> out [b, H, D].
+    workspace: "auto" allocates what the shape asks for, None runs one workgroup per
+    (sequence, head), or a uint8 tensor from hils_workspace()."""
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, torch.bfloat16, nm)
     b, H, D = q.shape
@@ -259,10 +269,14 @@ def hils_two_level_attn_fwd(q, k, v, khat, chunk_idx, C, scale_chunk, scale_toke
     m = chunk_idx.shape[-1]
     if out is None:
         out = torch.empty(b, H, D, dtype=torch.bfloat16, device=q.device)
+    if isinstance(workspace, str):
+        workspace = hils_workspace(b, H, D, m, q.device)
+    wsb = 0 if workspace is None else workspace.numel()
     _check(lib().hils_two_level_attn_fwd(_ptr(q), _str3(q, "bh"), _ptr(k), _str3(k, "bth"),
                                          _ptr(v), _str3(v, "bth"), _ptr(khat), _ptr(chunk_idx), b,
                                          L, H, D, C, n, m, float(scale_chunk), float(scale_token),
-                                         _ptr(out), _str3(out, "bh"), _stream()))
+                                         _ptr(out), _str3(out, "bh"), _ptr(workspace), wsb,
+                                         _stream()))
     return out
 
 

@@ -346,20 +346,34 @@ __global__ __launch_bounds__(256) void attn_d128_combine_kernel(
   if (h >= G) return;
   const float2* rl = part_rl + item * nsplit * G + h;
   const float* po = part_o + (item * nsplit * G + h) * D + c;
+  // the splits in groups of 8 whose loads are all issued before they are used
   float M = -INFINITY;
-  for (int sp = 0; sp < nsplit; ++sp) {
-    const float2 a = rl[sp * G];
-    if (a.y > 0.0f) M = fmaxf(M, a.x);
+  for (int s0 = 0; s0 < nsplit; s0 += 8) {
+    float2 a[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      a[u] = s0 + u < nsplit ? rl[(s0 + u) * G] : make_float2(-INFINITY, 0.0f);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (a[u].y > 0.0f) M = fmaxf(M, a[u].x);
   }
   float lt = 0.0f, acc = 0.0f;
-#pragma unroll 4
-  for (int sp = 0; sp < nsplit; ++sp) {
-    const float2 a = rl[sp * G];
-    const float o = po[static_cast<int64_t>(sp) * G * D];
-    if (a.y > 0.0f) {
-      const float f = exp2_ratio(a.x, M);
-      lt += a.y * f;
-      acc += o * f;
+  for (int s0 = 0; s0 < nsplit; s0 += 8) {
+    float2 a[8];
+    float o[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool ok = s0 + u < nsplit;
+      a[u] = ok ? rl[(s0 + u) * G] : make_float2(-INFINITY, 0.0f);
+      o[u] = ok ? po[static_cast<int64_t>(s0 + u) * G * D] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (a[u].y > 0.0f) {
+        const float f = exp2_ratio(a[u].x, M);
+        lt += a[u].y * f;
+        acc += o[u] * f;
+      }
     }
   }
   const int gk = static_cast<int>(item % Hkv);

@@ -278,12 +278,18 @@ hisa_status_t sparse_attn_fwd(const void* q, hisa_strides_t qs, const void* k, h
                     "sparse_attn_fwd");
 }
 
+size_t hils_two_level_attn_fwd_workspace_bytes(int batch, int H, int D, int m) {
+  if (batch < 1 || H < 1 || (D != 64 && D != 128) || m < 2 || m > 64) return 0;
+  return hisa::hils_workspace(batch, H, D, m);
+}
+
 hisa_status_t hils_two_level_attn_fwd(const void* q, hisa_strides_t qs, const void* k,
                                       hisa_strides_t ks, const void* v, hisa_strides_t vs,
                                       const float* khat, const int32_t* chunk_idx, int batch,
                                       int L, int H, int D, int C, int n_rows, int m,
                                       float scale_chunk, float scale_token, void* out,
-                                      hisa_strides_t os, hisa_stream_t stream) {
+                                      hisa_strides_t os, void* workspace, size_t workspace_bytes,
+                                      hisa_stream_t stream) {
   CHECK(q && k && v && khat && chunk_idx && out, HISA_ERR_NULL,
         "q, k, v, khat, chunk_idx and out are required");
   CHECK(batch >= 1 && L >= 1 && H >= 1, HISA_ERR_SHAPE, "sizes must be >= 1");
@@ -296,11 +302,18 @@ hisa_status_t hils_two_level_attn_fwd(const void* q, hisa_strides_t qs, const vo
   if ((st = check_bf16(k, ks, "k")) != HISA_OK) return st;
   if ((st = check_bf16(v, vs, "v")) != HISA_OK) return st;
   CHECK(nonneg(qs) && nonneg(os), HISA_ERR_SHAPE, "q/out strides must be non-negative");
+  if (workspace != nullptr) {
+    CHECK((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, HISA_ERR_WORKSPACE,
+          "workspace must be 256-byte aligned");
+    const size_t need = hisa::hils_workspace(batch, H, D, m);
+    CHECK(workspace_bytes >= need, HISA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu",
+          workspace_bytes, need);
+  }
   return hip_status(hisa::launch_hils(static_cast<const uint16_t*>(q), s3(qs),
                                       static_cast<const uint16_t*>(k), s3(ks),
                                       static_cast<const uint16_t*>(v), s3(vs), khat, chunk_idx,
                                       batch, L, H, D, C, n_rows, m, scale_chunk, scale_token,
-                                      static_cast<uint16_t*>(out), s3(os),
+                                      static_cast<uint16_t*>(out), s3(os), workspace,
                                       static_cast<hipStream_t>(stream)),
                     "hils_two_level_attn_fwd");
 }

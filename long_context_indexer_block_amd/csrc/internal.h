@@ -56,11 +56,13 @@ hipError_t launch_mla_attn(const uint16_t* q, Str3 qs, const uint16_t* kv, Str3 
                            int nq, int L, int Hkv, const int32_t* token_idx, int topk, float scale,
                            uint16_t* out, Str3 os, float* lse, hipStream_t s);
 
-// hils.hip
+// hils.hip; ws (may be null) holds at least hils_workspace() bytes (0 when the
+// shape never splits its chunks over workgroups)
+size_t hils_workspace(int batch, int H, int D, int m);
 hipError_t launch_hils(const uint16_t* q, Str3 qs, const uint16_t* k, Str3 ks, const uint16_t* v,
                        Str3 vs, const float* khat, const int32_t* chunk_idx, int batch, int L,
                        int H, int D, int C, int n_rows, int m, float scale_chunk,
-                       float scale_token, uint16_t* out, Str3 os, hipStream_t s);
+                       float scale_token, uint16_t* out, Str3 os, void* ws, hipStream_t s);
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 

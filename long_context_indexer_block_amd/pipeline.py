@@ -15,6 +15,7 @@ from __future__ import annotations
 import torch
 
 from . import (flat_indexer_topk, flat_indexer_topk_workspace_bytes, hils_two_level_attn_fwd,
+               hils_workspace,
                hisa_auto_plan, hisa_block_score, hisa_block_summary, hisa_block_summary_update,
                hisa_select_blocks,
                hisa_token_select, hisa_token_select_workspace_bytes, sparse_attn_fwd,
@@ -198,6 +199,7 @@ class HilsDecode:
         self.scores = torch.empty(b * H, 1, n, dtype=torch.float32, device=dev)
         self.chunk_idx = torch.empty(b * H, 1, m, dtype=torch.int32, device=dev)
         self.out = torch.empty(b, H, D, dtype=torch.bfloat16, device=dev)
+        self.ws = hils_workspace(b, H, D, m, dev)
 
     def build_keys(self):
         # every (sequence, head) pair is one routed sequence: x[bi] viewed as
@@ -216,7 +218,8 @@ class HilsDecode:
 
     def attend(self):
         hils_two_level_attn_fwd(self.q, self.k, self.v, self.khat, self.chunk_idx.view(-1, self.m),
-                                self.C, self.scale_chunk, self.scale_token, out=self.out)
+                                self.C, self.scale_chunk, self.scale_token, out=self.out,
+                                workspace=self.ws)
 
     def run(self, build=False):
         if build:

@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_match_header():
     names = _declared()
-    assert len(names) == 14
+    assert len(names) == 15
     lib = ctypes.CDLL(H.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -118,7 +118,7 @@ def test_hils_validation():
     L = H.lib()
     s = S(0, 64, 64)
     args = [FAKE, s, FAKE, s, FAKE, s, FAKE, FAKE, 1, 4096, 16, 64, 64, 64, 32, 0.125, 0.125,
-            FAKE, s, NULL]
+            FAKE, s, NULL, 0, NULL]
     a = list(args)
     a[13] = 63                                                       # n_rows != ceil(L/C)
     assert L.hils_two_level_attn_fwd(*a) == 2
@@ -128,6 +128,13 @@ def test_hils_validation():
     a = list(args)
     a[11] = 32                                                       # D unsupported
     assert L.hils_two_level_attn_fwd(*a) == 3
+    # few (sequence, head) pairs split their chunks; many do not
+    need = L.hils_two_level_attn_fwd_workspace_bytes(1, 16, 64, 32)
+    assert need > 0 and need % 256 == 0
+    assert L.hils_two_level_attn_fwd_workspace_bytes(64, 16, 64, 32) == 0
+    a = list(args)
+    a[19], a[20] = FAKE, need - 1                                    # too small
+    assert L.hils_two_level_attn_fwd(*a) == 5 and "needs" in _err()
 
 
 def test_missing_library_raises(monkeypatch):

@@ -347,11 +347,16 @@ def test_workload_decode_128k_b64():
             check_attention(p.out[b, 0].float().cpu().numpy(), ro, f"decode attention b={b}")
 
 
-def _hils_check(w, exact):
+def _hils_check(w, exact, split=True):
     inp = make_inputs(w, DEV, seed=0)
     C, m = w.B, w.m
     sc = 1.0 / math.sqrt(w.Dk)
     hd = HilsDecode(inp["q"], inp["k"], inp["v"], inp["w_proj"], C, m, sc, sc)
+    # few (sequence, head) pairs: the chunks are spread over workgroups and
+    # merged, unless the workspace is withheld
+    assert hd.ws is not None
+    if not split:
+        hd.ws = None
     hd.run(build=True)
     torch.cuda.synchronize()
     t = w.L - 1
@@ -408,10 +413,11 @@ HILS_SMALL = [
 ]
 
 
+@pytest.mark.parametrize("split", [True, False], ids=["split", "one_workgroup_per_pair"])
 @pytest.mark.parametrize("w", HILS_SMALL, ids=[w.name for w in HILS_SMALL])
-def test_hils_small(w):
-    log(f"case hils small {w}")
-    assert _hils_check(w, exact=True) == 0
+def test_hils_small(w, split):
+    log(f"case hils small {w} split={split}")
+    assert _hils_check(w, exact=True, split=split) == 0
 
 
 def test_workload_hils_decode_int_twin():
