@@ -401,6 +401,8 @@ def bench_hils(w, a, inp):
     res["config"]["queries"] = w.batch
     res["value"] = w.batch * a.steps / wall
     res["stage_ms"] = {"route": stage[0], "two_level_attention": stage[1]}
+    g_ms = graph_ms([[hd.route, hd.attend]], a.steps)
+    res["graph"] = {"ms_per_step": g_ms, "queries_per_s": w.batch / (g_ms * 1e-3)}
     res["chunk_key_build_ms"] = e0.elapsed_time(e1)
     n = hd.n
     # fp32 chunk keys of every chunk, then the chosen chunks' K and V rows
