@@ -40,6 +40,10 @@ SMALL = [
         sigma=1.0 / 24.0),
     _mk("mla_unit", L=640, B=64, m=3, k=160, d_idx=64, Hq=64, Hkv=1, Dk=576, Dv=512, mla=True,
         sigma=1.0),
+    # two sequences and 13 queries each (not a multiple of the 8 XCDs the
+    # latent kernel deals its queries to)
+    _mk("mla_batch2", batch=2, L=900, nq=13, B=64, m=4, k=200, d_idx=64, Hq=64, Hkv=1, Dk=576,
+        Dv=512, mla=True, sigma=1.0 / 24.0),
     _mk("k1_decode", kind="decode", batch=3, L=3000, B=128, m=6, k=1, d_idx=128, Hq=16, Hkv=1),
     # an odd k (ids written one by one), and more than 8192 candidates per
     # query (the block-parallel select instead of the row-parallel one)
