@@ -564,9 +564,13 @@ hipError_t launch_token_select(const uint16_t* qidx, Str3 qs, const uint16_t* ki
   const size_t npairs = static_cast<size_t>(batch) * nq * m;
   const size_t max_tiles = (npairs + kTQ - 1) / kTQ + nkeys;
   TokWs w = carve(ws, batch, nq, L, B, m, nullptr);
-  // one query per sequence: every key block has at most one pair, so the
-  // pairs are scored in place without bucketing them by block
-  const bool direct = nq == 1;
+  // Pairs are scored in place, without bucketing them by key block, when
+  // there is one query per sequence (no key block has two pairs) or when
+  // reading every pair's block directly gathers little (<= 256 MB, served
+  // from L2 and the Infinity Cache): the bucketing's launches then cost more
+  // than the reads they save.
+  const bool direct =
+      nq == 1 || npairs * static_cast<size_t>(B) * d * 2 <= (static_cast<size_t>(256) << 20);
   if (!direct) {
     // cnt and cursor are adjacent: clear both with one fill kernel
     const size_t zero_n = (reinterpret_cast<char*>(w.offs) - reinterpret_cast<char*>(w.cnt)) / 4;

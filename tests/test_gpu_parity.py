@@ -187,6 +187,21 @@ def test_coverage_hier_equals_flat_gpu():
     assert torch.equal(p.out, f.out)
 
 
+def test_token_select_bucketed_many_keys():
+    # enough pairs that they are bucketed by key block (over 256 MB of direct
+    # reads) and more than 4096 key blocks, so the bucket-count scan runs over
+    # several chunks of keys with a ragged last one: 2 x 2100 blocks of 64
+    w = _mk("bucketed_4200_keys", batch=2, L=2100 * 64 - 5, nq=512, B=64, m=40, k=300, d_idx=64,
+            Hq=1, Hkv=1)
+    assert w.batch * w.queries * w.m * w.B * w.d_idx * 2 > 256 << 20
+    assert w.batch * w.n_blocks > 4096
+    log(f"case {w}")
+    inp = make_inputs(w, DEV, seed=13)
+    p = _run_hier(w, inp)
+    rows = list(range(0, 512, 61)) + [510, 511]
+    _check_hier(w, inp, p, rows, attn_rows=rows[-2:], what=w.name)
+
+
 @pytest.mark.parametrize("B,m", [(128, 128), (64, 256)])
 def test_token_select_16k_candidates(B, m):
     # m*B = 16384 candidates per query (up to 256 slots) and enough queries
