@@ -68,7 +68,7 @@ extern "C" {
 
 const char* hisa_last_error(void) { return g_err.c_str(); }
 
-int hisa_abi_version(void) { return 1; }
+int hisa_abi_version(void) { return 2; }
 
 hisa_status_t hisa_block_summary(const void* kidx, hisa_strides_t ks, int batch, int L, int d,
                                  int B, const void* proj, float* summary, void* split,

@@ -32,7 +32,7 @@ def test_exports_match_header():
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(H.EXPORTS) == names
-    assert H.lib().hisa_abi_version() == 1
+    assert H.lib().hisa_abi_version() == 2
 
 
 def _err():
