@@ -488,7 +488,7 @@ def main():
         return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the path has no "
-              "multi-GPU form in this build", file=sys.stderr)
+              "multi-GPU form", file=sys.stderr)
         sys.exit(2)
     import torch
 
