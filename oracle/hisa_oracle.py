@@ -303,3 +303,16 @@ def hils_decode_head(q, K, V, khat, t, C, m, scale_chunk, scale_token):
     chosen = select_blocks_for_query(raw, t, C, m)
     logits = [scale_chunk * float(khat[c] @ q) if c >= 0 else 0.0 for c in chosen]
     return hils_combine(q, K, V, chosen, logits, t, C, scale_token), chosen
+
+
+def hils_prefill_query(q, K, V, W, khat, t, C, m, scale_chunk, scale_token):
+    """One head, the query at position t of a causal two-level prefill: the
+    decode of the first t+1 tokens.  Complete chunks keep their keys (rows of
+    khat, the projected means of all their tokens); the local chunk t // C
+    takes the projected mean of its tokens <= t only, as the decode's local
+    chunk does at t = L-1.  Returns (out [D], chosen chunk ids [m])."""
+    b = t // C
+    rows = _f64(K)[b * C: t + 1]
+    kh = _f64(khat)[: b + 1].copy()
+    kh[b] = _f64(W) @ (rows.sum(axis=0) / rows.shape[0])
+    return hils_decode_head(q, K, V, kh, t, C, m, scale_chunk, scale_token)

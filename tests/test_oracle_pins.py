@@ -323,3 +323,35 @@ def test_hils_routing_forced_and_count():
         dropped = [c for c in range(1, b) if c not in kept]
         if free and dropped:
             assert min(khat[c] @ q for c in free) >= max(khat[c] @ q for c in dropped)
+
+
+def test_hils_prefill_is_decode_of_the_prefix():
+    # a prefill query at t equals the decode of the cache cut after t: its
+    # chunk keys rebuilt from the first t+1 tokens, so the local chunk's key
+    # covers only the tokens up to the query; tokens after t change nothing
+    rng = np.random.default_rng(21)
+    L, C, D, m = 300, 16, 8, 6
+    K = rng.standard_normal((L, D))
+    V = rng.standard_normal((L, D))
+    W = rng.standard_normal((D, D)) / 3
+    khat = O.block_summary(K, C, proj=W)
+    for t in [0, 5, 15, 16, 17, 100, 159, 160, 299]:
+        q = rng.standard_normal(D)
+        out, chosen = O.hils_prefill_query(q, K, V, W, khat, t, C, m, 0.3, 0.4)
+        kp = O.block_summary(K[: t + 1], C, proj=W)
+        ref, ref_chosen = O.hils_decode_head(q, K[: t + 1], V[: t + 1], kp, t, C, m, 0.3, 0.4)
+        np.testing.assert_array_equal(chosen, ref_chosen)
+        np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+        K2, V2 = K.copy(), V.copy()
+        K2[t + 1:] = rng.standard_normal(K2[t + 1:].shape)
+        V2[t + 1:] = rng.standard_normal(V2[t + 1:].shape)
+        out2, chosen2 = O.hils_prefill_query(q, K2, V2, W, O.block_summary(K2, C, proj=W), t, C,
+                                             m, 0.3, 0.4)
+        np.testing.assert_array_equal(chosen, chosen2)
+        np.testing.assert_allclose(out, out2, rtol=1e-12, atol=1e-12)
+    # at the last position it is the decode itself
+    q = rng.standard_normal(D)
+    a, ca = O.hils_prefill_query(q, K, V, W, khat, L - 1, C, m, 0.3, 0.4)
+    b_, cb = O.hils_decode_head(q, K, V, khat, L - 1, C, m, 0.3, 0.4)
+    np.testing.assert_array_equal(ca, cb)
+    np.testing.assert_allclose(a, b_, rtol=1e-12, atol=1e-12)
