@@ -416,6 +416,85 @@ def bench_hils(w, a, inp):
     return res
 
 
+PEAK_FP32_VEC_TFLOPS = 157.3   # MI355X fp32 vector peak (256 CUs x 2.4 GHz x 256 flop/clk)
+
+
+def hils_prefill_flop(w):
+    """Algorithmic vector work of one causal two-level prefill: per (query,
+    head), 4*D flop per attended token (its score and its share of the value
+    sum), 2*D per chosen chunk (the chunk logit) and 2*D*D for the local
+    chunk's projected key. A query at t keeps min(t//C + 1, m) chunks: the
+    complete ones hold C tokens, the local one t - (t//C)*C + 1."""
+    import numpy as np
+    t = np.arange(w.L - w.queries, w.L, dtype=np.int64)
+    bt = t // w.B
+    chunks = np.minimum(bt + 1, w.m)
+    tokens = (chunks - 1) * w.B + (t - bt * w.B + 1)
+    D = w.Dk
+    per_head = 4 * D * tokens.sum() + 2 * D * chunks.sum() + 2 * D * D * t.size
+    return float(per_head * w.Hq * w.batch)
+
+
+def bench_hils_prefill(w, a, inp):
+    from long_context_indexer_block_amd.pipeline import HilsPrefill
+
+    sc = 1.0 / math.sqrt(w.Dk)
+    hp = HilsPrefill(inp["q"], inp["k"], inp["v"], inp["w_proj"], inp["q_pos"], w.B, w.m, sc, sc)
+    wall, stage = timed([hp.build_keys, hp.route, hp.attend], a.steps, a.warmup)
+    res = base_record(w, a, w.batch * w.queries, wall)
+    res["stage_ms"] = {"chunk_keys": stage[0], "route": stage[1], "two_level_attention": stage[2]}
+    flop = hils_prefill_flop(w)
+    ach = flop / (stage[2] * 1e-3) / 1e12
+    res["roofline"] = {"kernel": "hils_prefill_kernel", "bound": "alu", "achieved": ach,
+                       "peak": PEAK_FP32_VEC_TFLOPS, "unit": "TFLOP/s",
+                       "frac": ach / PEAK_FP32_VEC_TFLOPS, "traffic": None,
+                       "alg_flop_per_launch": flop}
+    return res
+
+
+def cpu_baseline_hils_prefill(w, inp, budget_s):
+    """The CPU oracle on a bounded sample of the two-level prefill: seeded
+    (position, head) queries until the time budget is spent; the chunk keys
+    of the sampled heads are built once beforehand and not timed."""
+    import numpy as np
+    import torch
+
+    import oracle.hisa_oracle as O
+    from workloads import sample_positions
+
+    Wp = inp["w_proj"].to("cpu", torch.float64).numpy()
+    heads = [0, w.Hq // 2, w.Hq - 1]
+    kv = {}
+    for h in heads:
+        K = inp["k"][0, :, h].to("cpu", torch.float64).numpy()
+        V = inp["v"][0, :, h].to("cpu", torch.float64).numpy()
+        kv[h] = (K, V, O.block_summary(K, w.B, proj=Wp))
+    pos = sample_positions(w, 20000)
+    rng = np.random.default_rng(0)
+    rng.shuffle(pos)
+    first = w.L - w.queries
+    sc = 1.0 / math.sqrt(w.Dk)
+    done = 0
+    t0 = time.perf_counter()
+    for i, t in enumerate(pos):
+        h = heads[i % len(heads)]
+        K, V, khat = kv[h]
+        q = inp["q"][0, t - first, h].to("cpu", torch.float64).numpy()
+        O.hils_prefill_query(q, K, V, Wp, khat, int(t), w.B, w.m, sc, sc)
+        done += 1
+        if time.perf_counter() - t0 > budget_s and done >= 4:
+            break
+    el = time.perf_counter() - t0
+    aff = len(os.sched_getaffinity(0))
+    threads = int(os.environ.get("OMP_NUM_THREADS", aff))
+    # one query position covers all Hq heads
+    return {"value": done / el / w.Hq, "unit": "queries/s", "cores": min(threads, aff),
+            "kind": "oracle",
+            "sample": f"{done} seeded (position, head) queries of the {w.name} prefill in numpy "
+                      f"float64 (routing and two-level softmax), scaled to positions of all "
+                      f"{w.Hq} heads; chunk keys built beforehand, not timed"}
+
+
 def recall_vs_flat(hier_idx, flat_idx, chunk=4096):
     """Mean over queries of |hier ∩ flat| / |flat| for ascending, -1 padded
     token lists [b, nq, k] (the flat indexer's exact top-k as the reference)."""
@@ -510,11 +589,16 @@ def main():
         res = bench_prefill(w, a, inp)
     elif w.kind == "decode":
         res = bench_decode(w, a, inp)
+    elif w.kind == "hils_prefill":
+        res = bench_hils_prefill(w, a, inp)
     else:
         res = bench_hils(w, a, inp)
     if not a.no_cpu and w.kind == "prefill":
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_seconds)
+    elif not a.no_cpu and w.kind == "hils_prefill":
+        log("cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline_hils_prefill(w, inp, a.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

@@ -226,6 +226,35 @@ hisa_status_t hils_two_level_attn_fwd(const void* q, hisa_strides_t qs, const vo
                                       hisa_stream_t stream);
 size_t hils_two_level_attn_fwd_workspace_bytes(int batch, int H, int D, int m);
 
+/* Causal two-level prefill (HiLS chapter, "hierarchical softmax
+ * decomposition" applied at every position, as the decode of the tokens up to
+ * the query). The query of sequence b at position t = q_pos[b][i] gets, per
+ * head, the two-level output of the decode over tokens 0 .. t: complete chunks
+ * c < t / C keep their keys khat_c, the local chunk t / C is keyed by
+ *   proj @ (mean of its tokens t/C*C .. t)
+ * (formed in the kernel), and its token softmax stops at t.
+ *   q         bf16 [batch][nq][H][D], strides qs (batch, token, head).
+ *   k, v      bf16 [batch][L][H][D], strides (batch, token, head).
+ *   khat      fp32 [batch*H][n_rows][D]: chunk keys of the whole cache from
+ *             hisa_block_summary with the same proj, batch*H sequences (row
+ *             b*H + h); the local chunk's row is not read.
+ *   chunk_idx int32 [batch*H][nq][m]: chosen chunks of each query (from
+ *             hisa_block_score / hisa_select_blocks over sequence b*H + h
+ *             with q_pos[b]), ascending, -1 padded; ids above t / C are
+ *             ignored.
+ *   proj      bf16 [D][D] row-major, the projection khat was made with, or
+ *             NULL when khat is the plain mean.
+ *   q_pos     int32 [batch][nq]: each query's position, clamped to [0, L-1].
+ *   out       bf16 [batch][nq][H][D], strides os (batch, token, head).
+ * batch*H <= 65535; sizes must be >= 1. */
+hisa_status_t hils_two_level_prefill_fwd(const void* q, hisa_strides_t qs, const void* k,
+                                         hisa_strides_t ks, const void* v, hisa_strides_t vs,
+                                         const float* khat, const int32_t* chunk_idx,
+                                         const void* proj, const int32_t* q_pos, int batch,
+                                         int nq, int L, int H, int D, int C, int n_rows, int m,
+                                         float scale_chunk, float scale_token, void* out,
+                                         hisa_strides_t os, hisa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -53,6 +53,8 @@ _SIGS = {
     "hils_two_level_attn_fwd": (_I, [_P, Strides, _P, Strides, _P, Strides, _P, _P, _I, _I, _I,
                                      _I, _I, _I, _I, _F, _F, _P, Strides, _P, _S, _P]),
     "hils_two_level_attn_fwd_workspace_bytes": (_S, [_I, _I, _I, _I]),
+    "hils_two_level_prefill_fwd": (_I, [_P, Strides, _P, Strides, _P, Strides, _P, _P, _P, _P,
+                                        _I, _I, _I, _I, _I, _I, _I, _I, _F, _F, _P, Strides, _P]),
 }
 EXPORTS = [n for n in _SIGS]
 
@@ -280,5 +282,25 @@ def hils_two_level_attn_fwd(q, k, v, khat, chunk_idx, C, scale_chunk, scale_toke
     return out
 
 
+def hils_two_level_prefill_fwd(q, k, v, khat, chunk_idx, q_pos, C, scale_chunk, scale_token,
+                               proj=None, out=None):
+    """q [b, nq, H, D], k/v [b, L, H, D], khat [b*H, n, D] fp32, chunk_idx [b*H, nq, m],
+    q_pos [b, nq] int32, proj [D, D] bf16 or None -> out [b, nq, H, D]."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, nm)
+    b, nq, H, D = q.shape
+    L = k.shape[1]
+    n = khat.shape[1]
+    m = chunk_idx.shape[-1]
+    if out is None:
+        out = torch.empty(b, nq, H, D, dtype=torch.bfloat16, device=q.device)
+    _check(lib().hils_two_level_prefill_fwd(_ptr(q), _str3(q, "bth"), _ptr(k), _str3(k, "bth"),
+                                            _ptr(v), _str3(v, "bth"), _ptr(khat),
+                                            _ptr(chunk_idx), _ptr(proj), _ptr(q_pos), b, nq, L, H,
+                                            D, C, n, m, float(scale_chunk), float(scale_token),
+                                            _ptr(out), _str3(out, "bth"), _stream()))
+    return out
+
+
 # ----------------------------------------------------------------- pipelines
-from .pipeline import HierPipeline, FlatPipeline, HilsDecode  # noqa: E402,F401
+from .pipeline import HierPipeline, FlatPipeline, HilsDecode, HilsPrefill  # noqa: E402,F401

@@ -318,4 +318,34 @@ hisa_status_t hils_two_level_attn_fwd(const void* q, hisa_strides_t qs, const vo
                     "hils_two_level_attn_fwd");
 }
 
+hisa_status_t hils_two_level_prefill_fwd(const void* q, hisa_strides_t qs, const void* k,
+                                         hisa_strides_t ks, const void* v, hisa_strides_t vs,
+                                         const float* khat, const int32_t* chunk_idx,
+                                         const void* proj, const int32_t* q_pos, int batch,
+                                         int nq, int L, int H, int D, int C, int n_rows, int m,
+                                         float scale_chunk, float scale_token, void* out,
+                                         hisa_strides_t os, hisa_stream_t stream) {
+  CHECK(q && k && v && khat && chunk_idx && q_pos && out, HISA_ERR_NULL,
+        "q, k, v, khat, chunk_idx, q_pos and out are required");
+  CHECK(batch >= 1 && nq >= 1 && L >= 1 && H >= 1, HISA_ERR_SHAPE, "sizes must be >= 1");
+  CHECK(D == 64 || D == 128, HISA_ERR_UNSUPPORTED, "D=%d unsupported (64 or 128)", D);
+  hisa_status_t st;
+  if ((st = check_block(C)) != HISA_OK) return st;
+  CHECK(m >= 2 && m <= 64, HISA_ERR_UNSUPPORTED, "m=%d must be in [2, 64]", m);
+  CHECK(n_rows == (L + C - 1) / C, HISA_ERR_SHAPE, "n_rows=%d must be ceil(L/C)", n_rows);
+  CHECK(static_cast<long long>(batch) * H <= 65535LL, HISA_ERR_UNSUPPORTED,
+        "batch*H=%lld exceeds 65535", static_cast<long long>(batch) * H);
+  if ((st = check_bf16(k, ks, "k")) != HISA_OK) return st;
+  if ((st = check_bf16(v, vs, "v")) != HISA_OK) return st;
+  CHECK(nonneg(qs) && nonneg(os), HISA_ERR_SHAPE, "q/out strides must be non-negative");
+  return hip_status(
+      hisa::launch_hils_prefill(static_cast<const uint16_t*>(q), s3(qs),
+                                static_cast<const uint16_t*>(k), s3(ks),
+                                static_cast<const uint16_t*>(v), s3(vs), khat, chunk_idx,
+                                static_cast<const uint16_t*>(proj), q_pos, batch, nq, L, H, D, C,
+                                n_rows, m, scale_chunk, scale_token, static_cast<uint16_t*>(out),
+                                s3(os), static_cast<hipStream_t>(stream)),
+      "hils_two_level_prefill_fwd");
+}
+
 }  // extern "C"

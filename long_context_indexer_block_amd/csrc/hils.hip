@@ -180,6 +180,105 @@ __global__ __launch_bounds__(64 * W) void hils_kernel(
     out[b * os.b + h * os.h + e] = f32_to_bf16(hils_mix<D>(logit, ac, m, e));
 }
 
+// Causal two-level prefill: one workgroup of W waves per (sequence, head,
+// query). The query at position t routes and attends as the decode of the
+// first t+1 tokens: complete chunks keep their table keys, and the local
+// chunk t / C is keyed by the projected mean of its tokens <= t, formed here
+// (column sums split over the waves, then the projection).
+template <int D, int W>
+__global__ __launch_bounds__(64 * W) void hils_prefill_kernel(
+    const uint16_t* __restrict__ q, Str3 qs, const uint16_t* __restrict__ k, Str3 ks,
+    const uint16_t* __restrict__ v, Str3 vs, const float* __restrict__ khat,
+    const int32_t* __restrict__ chunk_idx, const uint16_t* __restrict__ proj,
+    const int32_t* __restrict__ q_pos, int nq, int L, int H, int C, int n_rows, int m,
+    float scale_chunk, float scale_token, uint16_t* __restrict__ out, Str3 os) {
+  constexpr int MAXM = 64;
+  constexpr int NP = D / 2;
+  __shared__ float ac[MAXM * D];
+  __shared__ float logit[MAXM];
+  __shared__ __align__(16) float qf[D];
+  __shared__ float kloc[D];        // the local chunk's key
+  __shared__ float psum[W][D];     // per-wave column sums of the local chunk
+  __shared__ __align__(16) float pw[W][64];
+  const int qi = blockIdx.x;       // query of the sequence
+  const int bh = blockIdx.y;       // b*H + h
+  const int b = bh / H, h = bh % H;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+  const int t = min(max(q_pos[static_cast<int64_t>(b) * nq + qi], 0), L - 1);
+  const int bt = t / C;
+  const uint16_t* kb = k + b * ks.b + h * ks.h;
+  const uint16_t* vb = v + b * vs.b + h * vs.h;
+  for (int e = tid; e < D; e += 64 * W)
+    qf[e] = bf16_to_f32(q[b * qs.b + static_cast<int64_t>(qi) * qs.t + h * qs.h + e]);
+#pragma unroll
+  for (int x = 0; x < D / 64; ++x) {
+    float acc = 0.0f;
+    for (int j = bt * C + wave; j <= t; j += W)
+      acc += bf16_to_f32(kb[static_cast<int64_t>(j) * ks.t + lane + 64 * x]);
+    psum[wave][lane + 64 * x] = acc;
+  }
+  __syncthreads();
+  for (int e = tid; e < D; e += 64 * W) {
+    float pr = 0.0f;
+    if (proj == nullptr) {
+#pragma unroll
+      for (int w = 0; w < W; ++w) pr += psum[w][e];
+    } else {
+      for (int d = 0; d < D; ++d) {
+        float sd = 0.0f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) sd += psum[w][d];
+        pr = fmaf(bf16_to_f32(proj[e * D + d]), sd, pr);
+      }
+    }
+    kloc[e] = pr / static_cast<float>(t - bt * C + 1);
+  }
+  __syncthreads();
+  const int32_t* cidx = chunk_idx + (static_cast<int64_t>(bh) * nq + qi) * m;
+  const int nmine = (m - wave + W - 1) / W;
+  const int cid = lane < nmine ? cidx[wave + W * lane] : -1;
+  for (int it = 0; it < nmine; ++it) {
+    const int ci = wave + W * it;
+    const int c = __builtin_amdgcn_readlane(cid, it);
+    if (c < 0 || c > bt) {
+      if (lane == 0) logit[ci] = -INFINITY;
+      continue;
+    }
+    const float* kh = c == bt ? kloc : khat + (static_cast<int64_t>(bh) * n_rows + c) * D;
+    const ChunkOut<D> co = hils_chunk<D>(qf, kb, ks.t, vb, vs.t, kh, c, C, L, t, scale_chunk,
+                                         scale_token, pw[wave], lane);
+    if (lane < NP) {
+      ac[ci * D + 2 * lane] = co.a0;
+      ac[ci * D + 2 * lane + 1] = co.a1;
+    }
+    if (lane == 0) logit[ci] = co.r;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  }
+  __syncthreads();
+  for (int e = tid; e < D; e += 64 * W)
+    out[b * os.b + static_cast<int64_t>(qi) * os.t + h * os.h + e] =
+        f32_to_bf16(hils_mix<D>(logit, ac, m, e));
+}
+
+hipError_t launch_hils_prefill(const uint16_t* q, Str3 qs, const uint16_t* k, Str3 ks,
+                               const uint16_t* v, Str3 vs, const float* khat,
+                               const int32_t* chunk_idx, const uint16_t* proj,
+                               const int32_t* q_pos, int batch, int nq, int L, int H, int D,
+                               int C, int n_rows, int m, float scale_chunk, float scale_token,
+                               uint16_t* out, Str3 os, hipStream_t s) {
+  const dim3 grid(nq, batch * H);
+  if (D == 64)
+    hipLaunchKernelGGL((hils_prefill_kernel<64, 16>), grid, dim3(64 * 16), 0, s, q, qs, k, ks, v,
+                       vs, khat, chunk_idx, proj, q_pos, nq, L, H, C, n_rows, m, scale_chunk,
+                       scale_token, out, os);
+  else
+    hipLaunchKernelGGL((hils_prefill_kernel<128, 8>), grid, dim3(64 * 8), 0, s, q, qs, k, ks, v,
+                       vs, khat, chunk_idx, proj, q_pos, nq, L, H, C, n_rows, m, scale_chunk,
+                       scale_token, out, os);
+  return hipGetLastError();
+}
+
 // Split form, first kernel: workgroup (pair bh, chunks 4y .. 4y+3), one wave
 // per chosen chunk; a_c into ws_a [pairs][m][D], the logit into ws_r [pairs][m].
 template <int D>

@@ -64,6 +64,13 @@ hipError_t launch_hils(const uint16_t* q, Str3 qs, const uint16_t* k, Str3 ks, c
                        int H, int D, int C, int n_rows, int m, float scale_chunk,
                        float scale_token, uint16_t* out, Str3 os, void* ws, hipStream_t s);
 
+hipError_t launch_hils_prefill(const uint16_t* q, Str3 qs, const uint16_t* k, Str3 ks,
+                               const uint16_t* v, Str3 vs, const float* khat,
+                               const int32_t* chunk_idx, const uint16_t* proj,
+                               const int32_t* q_pos, int batch, int nq, int L, int H, int D,
+                               int C, int n_rows, int m, float scale_chunk, float scale_token,
+                               uint16_t* out, Str3 os, hipStream_t s);
+
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace hisa

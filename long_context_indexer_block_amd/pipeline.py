@@ -15,7 +15,7 @@ from __future__ import annotations
 import torch
 
 from . import (flat_indexer_topk, flat_indexer_topk_workspace_bytes, hils_two_level_attn_fwd,
-               hils_workspace,
+               hils_two_level_prefill_fwd, hils_workspace,
                hisa_auto_plan, hisa_block_score, hisa_block_summary, hisa_block_summary_update,
                hisa_select_blocks,
                hisa_token_select, hisa_token_select_workspace_bytes, sparse_attn_fwd,
@@ -222,6 +222,61 @@ class HilsDecode:
                                 workspace=self.ws)
 
     def run(self, build=False):
+        if build:
+            self.build_keys()
+        self.route()
+        self.attend()
+        return self.out
+
+
+class HilsPrefill:
+    """Causal two-level prefill: the query at position q_pos[b, i] of every
+    head routes over the chunk keys before it (chunk 0 and its own chunk
+    forced) and attends within its chosen chunks, as the decode of the tokens
+    up to it would.
+
+    q [b, nq, H, D], k/v [b, L, H, D] bf16, w_proj [D, D] bf16 (or None for
+    plain-mean chunk keys), q_pos [b, nq] int32."""
+
+    def __init__(self, q, k, v, w_proj, q_pos, C, m, scale_chunk, scale_token):
+        self.q, self.k, self.v, self.w_proj, self.q_pos = q, k, v, w_proj, q_pos
+        self.C, self.m, self.scale_chunk, self.scale_token = C, m, scale_chunk, scale_token
+        b, nq, H, D = q.shape
+        L = k.shape[1]
+        dev = k.device
+        n = -(-L // C)
+        self.n = n
+        self.khat = torch.empty(b * H, n, D, dtype=torch.float32, device=dev)
+        self.split = torch.empty(b * H, n, 3, D, dtype=torch.bfloat16, device=dev)
+        # routed sequence b*H + h reads the positions of sequence b
+        self.q_pos_h = q_pos.repeat_interleave(H, dim=0).contiguous()
+        self.scores = torch.empty(b * H, nq, n, dtype=torch.float32, device=dev)
+        self.chunk_idx = torch.empty(b * H, nq, m, dtype=torch.int32, device=dev)
+        self.out = torch.empty(b, nq, H, D, dtype=torch.bfloat16, device=dev)
+
+    def build_keys(self):
+        b, L, H, D = self.k.shape
+        for bi in range(b):
+            kv = self.k[bi].permute(1, 0, 2)
+            hisa_block_summary(kv, self.C, proj=self.w_proj, summary=self.khat[bi * H:(bi + 1) * H],
+                               split=self.split[bi * H:(bi + 1) * H])
+
+    def route(self):
+        # q[bi] viewed as [H, nq, D] (no copy): head h is routed sequence bi*H + h
+        b, nq, H, D = self.q.shape
+        for bi in range(b):
+            rows = slice(bi * H, (bi + 1) * H)
+            hisa_block_score(self.q[bi].permute(1, 0, 2), self.q_pos_h[rows], self.split[rows],
+                             self.C, out=self.scores[rows])
+            hisa_select_blocks(self.scores[rows], self.q_pos_h[rows], self.C, self.m,
+                               out=self.chunk_idx[rows])
+
+    def attend(self):
+        hils_two_level_prefill_fwd(self.q, self.k, self.v, self.khat, self.chunk_idx, self.q_pos,
+                                   self.C, self.scale_chunk, self.scale_token, proj=self.w_proj,
+                                   out=self.out)
+
+    def run(self, build=True):
         if build:
             self.build_keys()
         self.route()

@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_match_header():
     names = _declared()
-    assert len(names) == 15
+    assert len(names) == 16
     lib = ctypes.CDLL(H.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -135,6 +135,35 @@ def test_hils_validation():
     a = list(args)
     a[19], a[20] = FAKE, need - 1                                    # too small
     assert L.hils_two_level_attn_fwd(*a) == 5 and "needs" in _err()
+
+
+def test_hils_prefill_validation():
+    L = H.lib()
+    s = S(0, 1024, 64)
+    args = [FAKE, s, FAKE, s, FAKE, s, FAKE, FAKE, FAKE, FAKE, 1, 4096, 4096, 16, 64, 64, 64, 32,
+            0.125, 0.125, FAKE, s, NULL]
+    a = list(args)
+    a[9] = NULL                                                      # q_pos missing
+    assert L.hils_two_level_prefill_fwd(*a) == 1
+    a = list(args)
+    a[8] = NULL                                                      # no proj: plain means, valid
+    a[16] = 63                                                       # but n_rows != ceil(L/C)
+    assert L.hils_two_level_prefill_fwd(*a) == 2 and "n_rows" in _err()
+    a = list(args)
+    a[11] = 0                                                        # nq < 1
+    assert L.hils_two_level_prefill_fwd(*a) == 2
+    a = list(args)
+    a[17] = 1                                                        # m < 2
+    assert L.hils_two_level_prefill_fwd(*a) == 3
+    a = list(args)
+    a[14] = 96                                                       # D unsupported
+    assert L.hils_two_level_prefill_fwd(*a) == 3
+    a = list(args)
+    a[10], a[13] = 4097, 16                                          # batch*H > 65535
+    assert L.hils_two_level_prefill_fwd(*a) == 3 and "65535" in _err()
+    a = list(args)
+    a[2] = ctypes.c_void_p(0x10002)                                  # k not 16-byte aligned
+    assert L.hils_two_level_prefill_fwd(*a) == 2
 
 
 def test_missing_library_raises(monkeypatch):

@@ -14,7 +14,7 @@ import torch
 import long_context_indexer_block_amd as H
 import oracle.hisa_oracle as O
 from long_context_indexer_block_amd.pipeline import (AutoPipeline, DecodeSession, FlatPipeline,
-                                                     HierPipeline, HilsDecode)
+                                                     HierPipeline, HilsDecode, HilsPrefill)
 from parity import (SeqOracle, check_attention, check_index_rows, check_score_rows, f64, log)
 from workloads import WORKLOADS, Workload, make_inputs, sample_positions
 
@@ -449,3 +449,107 @@ def test_workload_hils_decode_1m():
     w = WORKLOADS["hils_decode_1m"]
     log(f"case hils N(0,1) {w}")
     assert _hils_check(w, exact=False) <= 2
+
+
+# ---------------------------------------------------------------- two-level prefill
+def _hils_prefill_check(w, exact, positions=None, heads=None):
+    """Run the causal two-level prefill of workload w on the GPU and check the
+    queries at `positions` (default: all) of `heads` (default: all) against
+    the oracle's decode of the tokens up to each query."""
+    inp = make_inputs(w, DEV, seed=0)
+    C, m, nq = w.B, w.m, w.queries
+    sc = 1.0 / math.sqrt(w.Dk)
+    hp = HilsPrefill(inp["q"], inp["k"], inp["v"], inp["w_proj"], inp["q_pos"], C, m, sc, sc)
+    hp.run()
+    torch.cuda.synchronize()
+    Wp = f64(inp["w_proj"])
+    qpos = inp["q_pos"].cpu().numpy()
+    first = w.L - nq
+    rows = list(range(nq)) if positions is None else [t - first for t in positions]
+    ridx = torch.tensor(rows, dtype=torch.long, device=DEV)
+    got_idx = hp.chunk_idx.view(w.batch, w.Hq, nq, m)[:, :, ridx].cpu().numpy()
+    outs = hp.out[:, ridx].float().cpu().numpy()      # [b, rows, H, D]
+    qs = inp["q"][:, ridx].cpu()
+    excluded = 0
+    for b in range(w.batch):
+        for h in (range(w.Hq) if heads is None else heads):
+            K = f64(inp["k"][b, :, h])
+            V = f64(inp["v"][b, :, h])
+            khat = O.block_summary(K, C, proj=Wp)
+            keep, refs = [], []
+            for r, i in enumerate(rows):
+                t = int(qpos[b, i])
+                q = f64(qs[b, r, h])
+                ref_out, ref_idx = O.hils_prefill_query(q, K, V, Wp, khat, t, C, m, sc, sc)
+                if not np.array_equal(got_idx[b, h, r], ref_idx):
+                    assert not exact, (f"hils prefill chunk_idx b={b} h={h} t={t}: gpu "
+                                       f"{got_idx[b, h, r].tolist()} ref {ref_idx.tolist()}")
+                    # N(0,1) chunk scores: a different set is accepted only at a
+                    # near tie of the last kept and first dropped free chunk
+                    raw = khat @ q
+                    bt = t // C
+                    cand = np.arange(1, bt)
+                    order = cand[np.lexsort((cand, -raw[cand]))]
+                    gap = raw[order[m - 3]] - raw[order[m - 2]]
+                    bound = 4 * 2.0 ** -24 * w.Dk * 2 * np.abs(khat[order[m - 3:m - 1]] * q).sum()
+                    assert gap <= bound, f"b={b} h={h} t={t}: chunk sets differ, gap {gap}"
+                    excluded += 1
+                    continue
+                keep.append(r)
+                refs.append(ref_out)
+            if keep:
+                check_attention(outs[b, keep, h], np.stack(refs), f"hils prefill out b={b} h={h}")
+    log(f"  hils prefill exact={exact}: queries excluded as near-ties: {excluded}")
+    return excluded
+
+
+# every position of small causal prefills in the integer twin (exact
+# routing): queries inside the first chunk (only chunk 0), across chunk
+# boundaries, a partial last chunk, head width 128, chunks of 128 tokens,
+# m = 64 (four chunks per wave), two sequences
+HILS_PREFILL_SMALL = [
+    WORKLOADS["hils_prefill_64k"].with_(name="hilsp_c64", batch=2, L=700, m=8, Hq=3, Hkv=3,
+                                        int_mode=True),
+    WORKLOADS["hils_prefill_64k"].with_(name="hilsp_d128_c128", batch=1, L=1500, B=128, m=6,
+                                        Hq=2, Hkv=2, Dk=128, Dv=128, d_idx=128, nq=700,
+                                        int_mode=True),
+    WORKLOADS["hils_prefill_64k"].with_(name="hilsp_c64_m64", batch=1, L=4480, m=64, Hq=1,
+                                        Hkv=1, nq=400, int_mode=True),
+]
+
+
+@pytest.mark.parametrize("w", HILS_PREFILL_SMALL, ids=[w.name for w in HILS_PREFILL_SMALL])
+def test_hils_prefill_small(w):
+    log(f"case hils prefill small {w}")
+    assert _hils_prefill_check(w, exact=True) == 0
+
+
+def test_hils_prefill_matches_decode_at_last_position():
+    # the last query of a prefill is the decode at L-1 over the same cache
+    w = HILS_PREFILL_SMALL[0]
+    inp = make_inputs(w, DEV, seed=0)
+    sc = 1.0 / math.sqrt(w.Dk)
+    hp = HilsPrefill(inp["q"], inp["k"], inp["v"], inp["w_proj"], inp["q_pos"], w.B, w.m, sc, sc)
+    hp.run()
+    q_last = inp["q"][:, -1].contiguous()
+    hd = HilsDecode(q_last, inp["k"], inp["v"], inp["w_proj"], w.B, w.m, sc, sc)
+    hd.ws = None
+    hd.run(build=True)
+    torch.cuda.synchronize()
+    assert torch.equal(hp.chunk_idx[:, -1], hd.chunk_idx.view(-1, w.m))
+    check_attention(hp.out[:, -1].float().cpu().numpy(), hd.out.float().cpu().numpy(),
+                    "prefill last query vs decode")
+
+
+def test_workload_hils_prefill_64k_int_twin_sampled():
+    w = WORKLOADS["hils_prefill_64k"].with_(int_mode=True)
+    log(f"case hils prefill 64K int twin, sampled {w}")
+    assert _hils_prefill_check(w, exact=True, positions=sample_positions(w, 24),
+                               heads=[0, 7, 15]) == 0
+
+
+def test_workload_hils_prefill_64k_sampled():
+    w = WORKLOADS["hils_prefill_64k"]
+    log(f"case hils prefill 64K N(0,1), sampled {w}")
+    assert _hils_prefill_check(w, exact=False, positions=sample_positions(w, 24),
+                               heads=[0, 5, 10, 15]) <= 4

@@ -31,7 +31,7 @@ SLAB_ROWS = 65536
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "prefill", "decode" or "hils"
+    kind: str            # "prefill", "decode", "hils" or "hils_prefill"
     batch: int           # independent sequences
     L: int               # cached tokens per sequence
     B: int               # block (chunk) size
@@ -51,7 +51,7 @@ class Workload:
     def queries(self) -> int:
         if self.nq is not None:
             return self.nq
-        return self.L if self.kind == "prefill" else 1
+        return self.L if self.kind in ("prefill", "hils_prefill") else 1
 
     @property
     def n_blocks(self) -> int:
@@ -79,6 +79,8 @@ WORKLOADS = {
                                 16, 1, 128, 128),
     "hils_decode_1m": Workload("hils_decode_1m", "hils", 1, 1048576, 64, 32, 0, 64,
                                16, 16, 64, 64),
+    "hils_prefill_64k": Workload("hils_prefill_64k", "hils_prefill", 1, 65536, 64, 32, 0, 64,
+                                 16, 16, 64, 64),
 }
 HEADLINE = "prefill_64k_mla"
 
@@ -121,25 +123,32 @@ def make_inputs(w: Workload, device="cpu", seed: int = 0) -> dict:
         k [b, L, Hkv, Dk], v [b, L, Hkv, Dv] (a strided view of k when mla),
         q_pos [b, nq] int32.
       hils: k, v [b, L, H, D], q [b, H, D], w_proj [D, D], q_pos [b] (= L-1).
+      hils_prefill: as hils with q [b, nq, H, D] and q_pos [b, nq] (the
+        last nq positions).
     """
     g = _gen(device, seed)
     nq = w.queries
     out = {}
-    if w.kind == "hils":
+    if w.kind in ("hils", "hils_prefill"):
         H, D = w.Hq, w.Dk
+        qshape = (w.batch, H, D) if w.kind == "hils" else (w.batch, nq, H, D)
         if w.int_mode:
             out["k"] = _randint_bf16((w.batch, w.L, H, D), g, device)
             out["v"] = _randn_bf16((w.batch, w.L, H, D), g, device, 1.0)
-            out["q"] = _randint_bf16((w.batch, H, D), g, device)
+            out["q"] = _randint_bf16(qshape, g, device)
             wp = torch.randint(-1, 2, (D, D), generator=g, device=device, dtype=torch.int32)
             out["w_proj"] = wp.to(torch.bfloat16)
         else:
             out["k"] = _randn_bf16((w.batch, w.L, H, D), g, device, w.sigma)
             out["v"] = _randn_bf16((w.batch, w.L, H, D), g, device, w.sigma)
-            out["q"] = _randn_bf16((w.batch, H, D), g, device, w.sigma)
+            out["q"] = _randn_bf16(qshape, g, device, w.sigma)
             wp = torch.randn((D, D), generator=g, device=device, dtype=torch.float32)
             out["w_proj"] = (wp / math.sqrt(D)).to(torch.bfloat16)
-        out["q_pos"] = torch.full((w.batch,), w.L - 1, dtype=torch.int32, device=device)
+        if w.kind == "hils":
+            out["q_pos"] = torch.full((w.batch,), w.L - 1, dtype=torch.int32, device=device)
+        else:
+            pos = torch.arange(w.L - nq, w.L, dtype=torch.int32, device=device)
+            out["q_pos"] = pos.unsqueeze(0).expand(w.batch, nq).contiguous()
         return out
 
     out["kidx"] = _randint_bf16((w.batch, w.L, w.d_idx), g, device)
