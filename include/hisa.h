@@ -246,14 +246,27 @@ size_t hils_two_level_attn_fwd_workspace_bytes(int batch, int H, int D, int m);
  *             NULL when khat is the plain mean.
  *   q_pos     int32 [batch][nq]: each query's position, clamped to [0, L-1].
  *   out       bf16 [batch][nq][H][D], strides os (batch, token, head).
- * batch*H <= 65535; sizes must be >= 1. */
+ *   workspace optional device scratch of hils_two_level_prefill_fwd_workspace_bytes()
+ *             bytes, 256-byte aligned, contents on entry ignored. With it, the
+ *             (query, slot) entries are bucketed by chunk and each chunk's K
+ *             and V rows are read once per 64 entries (matrix cores), with a
+ *             per-entry partial result merged per query; NULL runs one
+ *             workgroup per (query, head) gathering its own chunks (same
+ *             result up to fp32 rounding; for few queries). Too small is
+ *             HISA_ERR_WORKSPACE. Its size grows as batch*H*nq*m*D*4 bytes.
+ * q, k, v 16-byte aligned with strides in multiples of 8 elements; khat and
+ * proj 16-byte aligned. batch*H <= 65535, batch*H*nq*m < 2^32; sizes must be
+ * >= 1. */
 hisa_status_t hils_two_level_prefill_fwd(const void* q, hisa_strides_t qs, const void* k,
                                          hisa_strides_t ks, const void* v, hisa_strides_t vs,
                                          const float* khat, const int32_t* chunk_idx,
                                          const void* proj, const int32_t* q_pos, int batch,
                                          int nq, int L, int H, int D, int C, int n_rows, int m,
                                          float scale_chunk, float scale_token, void* out,
-                                         hisa_strides_t os, hisa_stream_t stream);
+                                         hisa_strides_t os, void* workspace,
+                                         size_t workspace_bytes, hisa_stream_t stream);
+size_t hils_two_level_prefill_fwd_workspace_bytes(int batch, int nq, int L, int H, int D, int C,
+                                                  int m);
 
 #ifdef __cplusplus
 }

@@ -54,7 +54,9 @@ _SIGS = {
                                      _I, _I, _I, _I, _F, _F, _P, Strides, _P, _S, _P]),
     "hils_two_level_attn_fwd_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "hils_two_level_prefill_fwd": (_I, [_P, Strides, _P, Strides, _P, Strides, _P, _P, _P, _P,
-                                        _I, _I, _I, _I, _I, _I, _I, _I, _F, _F, _P, Strides, _P]),
+                                        _I, _I, _I, _I, _I, _I, _I, _I, _F, _F, _P, Strides, _P,
+                                        _S, _P]),
+    "hils_two_level_prefill_fwd_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I, _I]),
 }
 EXPORTS = [n for n in _SIGS]
 
@@ -282,23 +284,38 @@ def hils_two_level_attn_fwd(q, k, v, khat, chunk_idx, C, scale_chunk, scale_toke
     return out
 
 
+def hils_prefill_workspace(b, nq, L, H, D, C, m, device):
+    """Workspace for the bucketed hils_two_level_prefill_fwd on these shapes."""
+    n = lib().hils_two_level_prefill_fwd_workspace_bytes(b, nq, L, H, D, C, m)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
 def hils_two_level_prefill_fwd(q, k, v, khat, chunk_idx, q_pos, C, scale_chunk, scale_token,
-                               proj=None, out=None):
+                               proj=None, out=None, workspace="auto"):
     """q [b, nq, H, D], k/v [b, L, H, D], khat [b*H, n, D] fp32, chunk_idx [b*H, nq, m],
-    q_pos [b, nq] int32, proj [D, D] bf16 or None -> out [b, nq, H, D]."""
+    q_pos [b, nq] int32, proj [D, D] bf16 or None -> out [b, nq, H, D].
+    workspace: "auto" allocates the bucketed path's scratch, None runs one
+    workgroup per (query, head), or a uint8 tensor from hils_prefill_workspace()."""
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, torch.bfloat16, nm)
+    for t, nm in ((khat, "khat"), (chunk_idx, "chunk_idx"), (q_pos, "q_pos")):
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
     b, nq, H, D = q.shape
     L = k.shape[1]
     n = khat.shape[1]
     m = chunk_idx.shape[-1]
     if out is None:
         out = torch.empty(b, nq, H, D, dtype=torch.bfloat16, device=q.device)
+    if isinstance(workspace, str):
+        workspace = hils_prefill_workspace(b, nq, L, H, D, C, m, q.device)
+    wsb = 0 if workspace is None else workspace.numel()
     _check(lib().hils_two_level_prefill_fwd(_ptr(q), _str3(q, "bth"), _ptr(k), _str3(k, "bth"),
                                             _ptr(v), _str3(v, "bth"), _ptr(khat),
                                             _ptr(chunk_idx), _ptr(proj), _ptr(q_pos), b, nq, L, H,
                                             D, C, n, m, float(scale_chunk), float(scale_token),
-                                            _ptr(out), _str3(out, "bth"), _stream()))
+                                            _ptr(out), _str3(out, "bth"), _ptr(workspace), wsb,
+                                            _stream()))
     return out
 
 

@@ -318,13 +318,22 @@ hisa_status_t hils_two_level_attn_fwd(const void* q, hisa_strides_t qs, const vo
                     "hils_two_level_attn_fwd");
 }
 
+size_t hils_two_level_prefill_fwd_workspace_bytes(int batch, int nq, int L, int H, int D, int C,
+                                                  int m) {
+  if (batch < 1 || nq < 1 || L < 1 || H < 1 || (D != 64 && D != 128) || m < 2 || m > 64 ||
+      (C != 64 && C != 128 && C != 256))
+    return 0;
+  return hisa::hils_prefill_workspace(batch, nq, L, H, D, C, m);
+}
+
 hisa_status_t hils_two_level_prefill_fwd(const void* q, hisa_strides_t qs, const void* k,
                                          hisa_strides_t ks, const void* v, hisa_strides_t vs,
                                          const float* khat, const int32_t* chunk_idx,
                                          const void* proj, const int32_t* q_pos, int batch,
                                          int nq, int L, int H, int D, int C, int n_rows, int m,
                                          float scale_chunk, float scale_token, void* out,
-                                         hisa_strides_t os, hisa_stream_t stream) {
+                                         hisa_strides_t os, void* workspace,
+                                         size_t workspace_bytes, hisa_stream_t stream) {
   CHECK(q && k && v && khat && chunk_idx && q_pos && out, HISA_ERR_NULL,
         "q, k, v, khat, chunk_idx, q_pos and out are required");
   CHECK(batch >= 1 && nq >= 1 && L >= 1 && H >= 1, HISA_ERR_SHAPE, "sizes must be >= 1");
@@ -335,16 +344,28 @@ hisa_status_t hils_two_level_prefill_fwd(const void* q, hisa_strides_t qs, const
   CHECK(n_rows == (L + C - 1) / C, HISA_ERR_SHAPE, "n_rows=%d must be ceil(L/C)", n_rows);
   CHECK(static_cast<long long>(batch) * H <= 65535LL, HISA_ERR_UNSUPPORTED,
         "batch*H=%lld exceeds 65535", static_cast<long long>(batch) * H);
+  CHECK(static_cast<long long>(batch) * H * nq * m < (1LL << 32), HISA_ERR_UNSUPPORTED,
+        "batch*H*nq*m must be below 2^32");
+  if ((st = check_bf16(q, qs, "q")) != HISA_OK) return st;
   if ((st = check_bf16(k, ks, "k")) != HISA_OK) return st;
   if ((st = check_bf16(v, vs, "v")) != HISA_OK) return st;
-  CHECK(nonneg(qs) && nonneg(os), HISA_ERR_SHAPE, "q/out strides must be non-negative");
+  CHECK(aligned16(khat), HISA_ERR_SHAPE, "khat must be 16-byte aligned");
+  CHECK(proj == nullptr || aligned16(proj), HISA_ERR_SHAPE, "proj must be 16-byte aligned");
+  CHECK(nonneg(os), HISA_ERR_SHAPE, "out strides must be non-negative");
+  if (workspace != nullptr) {
+    CHECK((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, HISA_ERR_WORKSPACE,
+          "workspace must be 256-byte aligned");
+    const size_t need = hisa::hils_prefill_workspace(batch, nq, L, H, D, C, m);
+    CHECK(workspace_bytes >= need, HISA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu",
+          workspace_bytes, need);
+  }
   return hip_status(
       hisa::launch_hils_prefill(static_cast<const uint16_t*>(q), s3(qs),
                                 static_cast<const uint16_t*>(k), s3(ks),
                                 static_cast<const uint16_t*>(v), s3(vs), khat, chunk_idx,
                                 static_cast<const uint16_t*>(proj), q_pos, batch, nq, L, H, D, C,
                                 n_rows, m, scale_chunk, scale_token, static_cast<uint16_t*>(out),
-                                s3(os), static_cast<hipStream_t>(stream)),
+                                s3(os), workspace, static_cast<hipStream_t>(stream)),
       "hils_two_level_prefill_fwd");
 }
 

@@ -261,21 +261,396 @@ __global__ __launch_bounds__(64 * W) void hils_prefill_kernel(
         f32_to_bf16(hils_mix<D>(logit, ac, m, e));
 }
 
+// ---------------------------------------------------------------------------
+// Bucketed prefill. Many queries share each chunk, so rather than every
+// query gathering its chosen chunks, the (query, slot) entries of chunk_idx
+// are bucketed by (sequence*head, chunk) and each chunk's K and V rows are
+// read once per tile of 64 entries:
+//   1. local keys: kloc[bh][j] = proj @ (mean of tokens j/C*C .. j), every j;
+//   2. per tile, on matrix cores: the chunk's token softmax for the tile's
+//      queries (causal within the local chunk) times V, normalised, into
+//      partial[e][:], and the chunk logit (scale_chunk * q . key) into
+//      logit[e], key = khat of the chunk or kloc of the query's position when
+//      it is the query's local chunk;
+//   3. per query, the softmax over its chosen chunks' logits mixes the
+//      partials.
+// ---------------------------------------------------------------------------
+struct PrefillWs {
+  PairBuckets pb;
+  float* kloc;      // [batch*H][L][D]
+  float* logit;     // [batch*H*nq*m]
+  float* partial;   // [batch*H*nq*m][D]
+};
+
+static PrefillWs carve_prefill(void* ws, int batch, int nq, int L, int H, int D, int C, int m,
+                               size_t* bytes) {
+  const int bh = batch * H, nblk = (L + C - 1) / C;
+  const size_t npairs = static_cast<size_t>(bh) * nq * m;
+  size_t off = 0;
+  PrefillWs w;
+  w.pb = carve_pair_buckets(ws, bh, nq, m, nblk, &off);
+  char* p = static_cast<char*>(ws);
+  auto take = [&](size_t n) { char* r = p ? p + off : nullptr; off += align256(n); return r; };
+  w.kloc = reinterpret_cast<float*>(take(static_cast<size_t>(bh) * L * D * 4));
+  w.logit = reinterpret_cast<float*>(take(npairs * 4));
+  w.partial = reinterpret_cast<float*>(take(npairs * D * 4));
+  if (bytes) *bytes = off;
+  return w;
+}
+
+size_t hils_prefill_workspace(int batch, int nq, int L, int H, int D, int C, int m) {
+  size_t bytes = 0;
+  carve_prefill(nullptr, batch, nq, L, H, D, C, m, &bytes);
+  return bytes;
+}
+
+// Workgroup (chunk c, pair bh): 64-token groups of the chunk. Thread (rg, d)
+// sums column d over its rows of the group (a prefix within them), the row
+// groups are joined with the running carry, then thread (jg, e) projects the
+// prefixes of rows jg, jg + RG, ... onto output column e.
+template <int D>
+__global__ __launch_bounds__(256) void hils_local_keys_kernel(
+    const uint16_t* __restrict__ k, Str3 ks, int H, int L, int C,
+    const uint16_t* __restrict__ proj, float* __restrict__ kloc) {
+  constexpr int RG = 256 / D;      // row groups of the scan
+  constexpr int RPG = 64 / RG;     // rows per group
+  __shared__ float pre[64][D];
+  __shared__ float tot[RG][D];
+  __shared__ float carry[D];
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / H, h = bh % H;
+  const int tid = threadIdx.x, d = tid % D, rg = tid / D;
+  const uint16_t* kb = k + b * ks.b + h * ks.h;
+  float* out = kloc + static_cast<int64_t>(bh) * L * D;
+  if (tid < D) carry[tid] = 0.0f;
+  const int j_end = min(L, (c + 1) * C);
+  for (int g0 = c * C; g0 < j_end; g0 += 64) {
+    float run = 0.0f;
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      const int j = g0 + rg * RPG + i;
+      run += j < j_end ? bf16_to_f32(kb[static_cast<int64_t>(j) * ks.t + d]) : 0.0f;
+      pre[rg * RPG + i][d] = run;
+    }
+    tot[rg][d] = run;
+    __syncthreads();
+    float base = carry[d];
+    for (int r = 0; r < rg; ++r) base += tot[r][d];
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) pre[rg * RPG + i][d] += base;
+    __syncthreads();
+    if (tid < D) {
+      float all = carry[tid];
+      for (int r = 0; r < RG; ++r) all += tot[r][tid];
+      carry[tid] = all;
+    }
+    // rows jg + RG*i of the group; column e = d of this thread
+    constexpr int NJ = 64 / RG;
+    float acc[NJ];
+    if (proj == nullptr) {
+#pragma unroll
+      for (int i = 0; i < NJ; ++i) acc[i] = pre[rg + RG * i][d];
+    } else {
+#pragma unroll
+      for (int i = 0; i < NJ; ++i) acc[i] = 0.0f;
+      const uint16_t* wr = proj + d * D;
+      for (int x = 0; x < D; x += 8) {
+        const uint4 wv = *reinterpret_cast<const uint4*>(wr + x);
+        const float wf[8] = {bf16_lo(wv.x), bf16_hi(wv.x), bf16_lo(wv.y), bf16_hi(wv.y),
+                             bf16_lo(wv.z), bf16_hi(wv.z), bf16_lo(wv.w), bf16_hi(wv.w)};
+#pragma unroll
+        for (int i = 0; i < NJ; ++i) {
+          const float* pr = &pre[rg + RG * i][x];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) acc[i] = fmaf(wf[u], pr[u], acc[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NJ; ++i) {
+      const int j = g0 + rg + RG * i;
+      if (j < j_end)
+        out[static_cast<int64_t>(j) * D + d] = acc[i] / static_cast<float>(j - c * C + 1);
+    }
+    __syncthreads();
+  }
+}
+
+// Tile kernel: 4 waves, wave w takes entries 16w .. 16w+15 of the tile (one
+// per lane column r = l%16). Per 64-token group of the chunk, V is staged in
+// LDS (rows padded by 16 bytes) and K fragments come straight from global.
+// S^T = K Q^T on 16x16x32 bf16 MFMA leaves in lane l the entry l%16 and the
+// tokens 4(l/16)..+3 of each 16-token tile: the A operand of the 16x16x16
+// P V product, with V^T fragments from ds_read_tr16_b64. Online softmax over
+// the chunk's groups (one group for C = 64).
+struct TileTabs {
+  const uint32_t* cnt;
+  const uint32_t* offs;
+  const uint32_t* tile_off;
+  const uint32_t* total;
+  const uint32_t* pairs;
+  const uint32_t* tiles;
+};
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short v4s_t;
+
+__device__ __forceinline__ float max_x4_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_x4_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+template <int D, int C>
+__global__ __launch_bounds__(256) void hils_pair_chunk_kernel(
+    const uint16_t* __restrict__ q, Str3 qs, const uint16_t* __restrict__ k, Str3 ks,
+    const uint16_t* __restrict__ v, Str3 vs, const float* __restrict__ khat,
+    const float* __restrict__ kloc, const int32_t* __restrict__ q_pos, int H, int nq, int L,
+    int n_rows, int m, TileTabs tt, unsigned grid_tiles, float scale_chunk,
+    float scale_token_log2, float* __restrict__ partial, float* __restrict__ logit) {
+  constexpr int NKS = D / 32;     // k-steps of S^T
+  constexpr int NDB = D / 16;     // 16-column blocks of O
+  constexpr int RS = 2 * D + 16;  // LDS bytes per staged V row
+  __shared__ __align__(16) unsigned char vt[64 * RS];
+  // the chip deals workgroups round-robin to its 8 XCDs: give each XCD a
+  // contiguous run of tiles, so that the tiles of one chunk share an L2
+  const unsigned per = grid_tiles / 8;
+  const unsigned tile = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (tile >= tt.total[1]) return;
+  const uint32_t key = tt.tiles[tile];
+  const int bh = static_cast<int>(key / n_rows), c = static_cast<int>(key % n_rows);
+  const int b = bh / H, h = bh % H;
+  const uint32_t first = tt.offs[key] + (tile - tt.tile_off[key]) * kPairTile;
+  const uint32_t end = tt.offs[key] + tt.cnt[key];
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, r = l & 15;
+  const uint32_t pi = first + 16 * w + r;
+  const bool pv = pi < end;
+  const uint32_t e = pv ? tt.pairs[pi] : 0u;
+  const int qi = pv ? static_cast<int>(e / m - static_cast<uint32_t>(bh) * nq) : 0;
+  const int t = min(max(q_pos[static_cast<int64_t>(b) * nq + qi], 0), L - 1);
+  const int bt = t / C;
+  const uint16_t* qrow = q + b * qs.b + static_cast<int64_t>(qi) * qs.t + h * qs.h;
+  bf16x8 qf[NKS];
+#pragma unroll
+  for (int x = 0; x < NKS; ++x)
+    qf[x] = as_bf16x8(pv ? *reinterpret_cast<const uint4*>(qrow + 32 * x + 8 * g)
+                         : make_uint4(0u, 0u, 0u, 0u));
+  // chunk logit: q . key over this lane's columns 32x + 8g .. +7
+  {
+    const float* kr = c == bt ? kloc + (static_cast<int64_t>(bh) * L + t) * D
+                              : khat + (static_cast<int64_t>(bh) * n_rows + c) * D;
+    float part = 0.0f;
+    if (pv) {
+#pragma unroll
+      for (int x = 0; x < NKS; ++x) {
+        const float4 k0 = *reinterpret_cast<const float4*>(kr + 32 * x + 8 * g);
+        const float4 k1 = *reinterpret_cast<const float4*>(kr + 32 * x + 8 * g + 4);
+        const uint4 qw = __builtin_bit_cast(uint4, qf[x]);
+        part = fmaf(bf16_lo(qw.x), k0.x, part); part = fmaf(bf16_hi(qw.x), k0.y, part);
+        part = fmaf(bf16_lo(qw.y), k0.z, part); part = fmaf(bf16_hi(qw.y), k0.w, part);
+        part = fmaf(bf16_lo(qw.z), k1.x, part); part = fmaf(bf16_hi(qw.z), k1.y, part);
+        part = fmaf(bf16_lo(qw.w), k1.z, part); part = fmaf(bf16_hi(qw.w), k1.w, part);
+      }
+    }
+    part = sum_x4_groups(part);
+    if (pv && g == 0) logit[e] = c <= bt ? part * scale_chunk : -INFINITY;
+  }
+  const uint16_t* kb = k + b * ks.b + h * ks.h;
+  const uint16_t* vb = v + b * vs.b + h * vs.h;
+  float mrun = -INFINITY, lsum = 0.0f;
+  f32x4 o[NDB];
+#pragma unroll
+  for (int x = 0; x < NDB; ++x) o[x] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  const int j_end = min(L, (c + 1) * C);
+  for (int j0 = c * C; j0 < j_end; j0 += 64) {
+    if (j0 != c * C) __syncthreads();  // the previous group's V reads are done
+    for (int x = threadIdx.x; x < 64 * D / 8; x += 256) {
+      const int row = x / (D / 8), ch = x % (D / 8);
+      const int j = min(j0 + row, L - 1);
+      *reinterpret_cast<uint4*>(vt + row * RS + 16 * ch) =
+          *reinterpret_cast<const uint4*>(vb + static_cast<int64_t>(j) * vs.t + 8 * ch);
+    }
+    uint4 kf[4][NKS];
+#pragma unroll
+    for (int tau = 0; tau < 4; ++tau) {
+      const int j = min(j0 + 16 * tau + r, L - 1);
+#pragma unroll
+      for (int x = 0; x < NKS; ++x)
+        kf[tau][x] = *reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(j) * ks.t +
+                                                     32 * x + 8 * g);
+    }
+    __syncthreads();  // V staged
+    float sv[4][4];
+    float gmax = -INFINITY;
+#pragma unroll
+    for (int tau = 0; tau < 4; ++tau) {
+      f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int x = 0; x < NKS; ++x) sacc = mfma16(as_bf16x8(kf[tau][x]), qf[x], sacc);
+#pragma unroll
+      for (int ee = 0; ee < 4; ++ee) {
+        const int j = j0 + 16 * tau + 4 * g + ee;
+        sv[tau][ee] = pv && j <= t ? sacc[ee] * scale_token_log2 : -INFINITY;
+        gmax = fmaxf(gmax, sv[tau][ee]);
+      }
+    }
+    gmax = max_x4_groups(gmax);
+    const float mnew = fmaxf(mrun, gmax);
+    if (j0 != c * C) {
+      const float alpha = mrun == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mrun - mnew);
+      lsum *= alpha;
+#pragma unroll
+      for (int ee = 0; ee < 4; ++ee) {
+        const float ae = __shfl(alpha, 4 * g + ee, 64);
+#pragma unroll
+        for (int x = 0; x < NDB; ++x) o[x][ee] *= ae;
+      }
+    }
+    mrun = mnew;
+    const float moff = mnew == -INFINITY ? 0.0f : -mnew;
+    const int sl = l & 15;
+#pragma unroll
+    for (int tau = 0; tau < 4; ++tau) {
+      v4s_t pa;
+#pragma unroll
+      for (int ee = 0; ee < 4; ++ee) {
+        const float p = __builtin_amdgcn_exp2f(sv[tau][ee] + moff);
+        lsum += p;
+        pa[ee] = static_cast<short>(f32_to_bf16(p));
+      }
+      const unsigned char* vrow = vt + (16 * tau + 4 * g + (sl >> 2)) * RS + 8 * (sl & 3);
+#pragma unroll
+      for (int x = 0; x < NDB; ++x) {
+        const v4s_t vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s_t*)(vrow + 32 * x));
+        o[x] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vf, o[x], 0, 0, 0);
+      }
+    }
+  }
+  lsum = sum_x4_groups(lsum);
+  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+  // O row 4g + ee is the entry of lane 4g + ee; column 16x + r
+#pragma unroll
+  for (int ee = 0; ee < 4; ++ee) {
+    const int src = 4 * g + ee;
+    const uint32_t er = __shfl(e, src, 64);
+    const float ir = __shfl(inv, src, 64);
+    const int vr = __shfl(pv ? 1 : 0, src, 64);
+    if (vr) {
+      float* pr = partial + static_cast<int64_t>(er) * D + r;
+#pragma unroll
+      for (int x = 0; x < NDB; ++x) pr[16 * x] = o[x][ee] * ir;
+    }
+  }
+}
+
+// One wave per (bh, query): the softmax over the chosen chunks' logits
+// (lane s holds slot s) mixes the partials; lane l owns columns l + 64x.
+template <int D>
+__global__ __launch_bounds__(256) void hils_prefill_combine_kernel(
+    const int32_t* __restrict__ chunk_idx, const int32_t* __restrict__ q_pos, int H, int nq,
+    int L, int C, int m, const float* __restrict__ partial, const float* __restrict__ logit,
+    uint16_t* __restrict__ out, Str3 os, int64_t nitems) {
+  constexpr int NX = D / 64;
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (item >= nitems) return;
+  const int l = threadIdx.x & 63;
+  const int bh = static_cast<int>(item / nq), qi = static_cast<int>(item % nq);
+  const int b = bh / H, h = bh % H;
+  const int t = min(max(q_pos[static_cast<int64_t>(b) * nq + qi], 0), L - 1);
+  const int bt = t / C;
+  const int64_t e0 = item * m;
+  const int c = l < m ? chunk_idx[e0 + l] : -1;
+  const bool ok = c >= 0 && c <= bt;
+  const float lg = ok ? logit[e0 + l] : -INFINITY;
+  const float mx = wave_max(lg);
+  const float wgt = ok && mx != -INFINITY ? __expf(lg - mx) : 0.0f;
+  const float z = wave_sum(wgt);
+  float acc[NX];
+#pragma unroll
+  for (int x = 0; x < NX; ++x) acc[x] = 0.0f;
+  for (int s0 = 0; s0 < m; s0 += 8) {
+    float val[8][NX], ws[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = s0 + u;
+      ws[u] = s < m ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), s)) : 0.0f;
+#pragma unroll
+      for (int x = 0; x < NX; ++x)
+        val[u][x] = ws[u] != 0.0f ? partial[(e0 + s) * D + l + 64 * x] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int x = 0; x < NX; ++x) acc[x] = fmaf(ws[u], val[u][x], acc[x]);
+  }
+  const float iz = z > 0.0f ? 1.0f / z : 0.0f;
+  uint16_t* orow = out + b * os.b + static_cast<int64_t>(qi) * os.t + h * os.h;
+#pragma unroll
+  for (int x = 0; x < NX; ++x) orow[l + 64 * x] = f32_to_bf16(acc[x] * iz);
+}
+
 hipError_t launch_hils_prefill(const uint16_t* q, Str3 qs, const uint16_t* k, Str3 ks,
                                const uint16_t* v, Str3 vs, const float* khat,
                                const int32_t* chunk_idx, const uint16_t* proj,
                                const int32_t* q_pos, int batch, int nq, int L, int H, int D,
                                int C, int n_rows, int m, float scale_chunk, float scale_token,
-                               uint16_t* out, Str3 os, hipStream_t s) {
-  const dim3 grid(nq, batch * H);
+                               uint16_t* out, Str3 os, void* ws, hipStream_t s) {
+  if (ws == nullptr) {
+    const dim3 grid(nq, batch * H);
+    if (D == 64)
+      hipLaunchKernelGGL((hils_prefill_kernel<64, 16>), grid, dim3(64 * 16), 0, s, q, qs, k, ks,
+                         v, vs, khat, chunk_idx, proj, q_pos, nq, L, H, C, n_rows, m, scale_chunk,
+                         scale_token, out, os);
+    else
+      hipLaunchKernelGGL((hils_prefill_kernel<128, 8>), grid, dim3(64 * 8), 0, s, q, qs, k, ks,
+                         v, vs, khat, chunk_idx, proj, q_pos, nq, L, H, C, n_rows, m, scale_chunk,
+                         scale_token, out, os);
+    return hipGetLastError();
+  }
+  const int bh = batch * H;
+  PrefillWs w = carve_prefill(ws, batch, nq, L, H, D, C, m, nullptr);
+  hipError_t err = launch_pair_buckets(chunk_idx, bh, nq, m, n_rows, w.pb, s);
+  if (err != hipSuccess) return err;
   if (D == 64)
-    hipLaunchKernelGGL((hils_prefill_kernel<64, 16>), grid, dim3(64 * 16), 0, s, q, qs, k, ks, v,
-                       vs, khat, chunk_idx, proj, q_pos, nq, L, H, C, n_rows, m, scale_chunk,
-                       scale_token, out, os);
+    hipLaunchKernelGGL((hils_local_keys_kernel<64>), dim3(n_rows, bh), dim3(256), 0, s, k, ks, H,
+                       L, C, proj, w.kloc);
   else
-    hipLaunchKernelGGL((hils_prefill_kernel<128, 8>), grid, dim3(64 * 8), 0, s, q, qs, k, ks, v,
-                       vs, khat, chunk_idx, proj, q_pos, nq, L, H, C, n_rows, m, scale_chunk,
-                       scale_token, out, os);
+    hipLaunchKernelGGL((hils_local_keys_kernel<128>), dim3(n_rows, bh), dim3(256), 0, s, k, ks, H,
+                       L, C, proj, w.kloc);
+  const size_t npairs = static_cast<size_t>(bh) * nq * m;
+  const size_t max_tiles = (npairs + kPairTile - 1) / kPairTile + static_cast<size_t>(bh) * n_rows;
+  const unsigned grid_tiles = static_cast<unsigned>((max_tiles + 7) / 8 * 8);
+  const TileTabs tt{w.pb.cnt, w.pb.offs, w.pb.tile_off, w.pb.total, w.pb.pairs, w.pb.tiles};
+  const float stl2 = scale_token * 1.4426950408889634f;
+#define HISA_PC(D_, C_)                                                                          \
+  hipLaunchKernelGGL((hils_pair_chunk_kernel<D_, C_>), dim3(grid_tiles), dim3(256), 0, s, q, qs,  \
+                     k, ks, v, vs, khat, w.kloc, q_pos, H, nq, L, n_rows, m, tt, grid_tiles,      \
+                     scale_chunk, stl2, w.partial, w.logit)
+  if (D == 64) {
+    if (C == 64) HISA_PC(64, 64); else if (C == 128) HISA_PC(64, 128); else HISA_PC(64, 256);
+  } else {
+    if (C == 64) HISA_PC(128, 64); else if (C == 128) HISA_PC(128, 128); else HISA_PC(128, 256);
+  }
+#undef HISA_PC
+  const int64_t nitems = static_cast<int64_t>(bh) * nq;
+  const dim3 cg(static_cast<unsigned>((nitems + 3) / 4));
+  if (D == 64)
+    hipLaunchKernelGGL((hils_prefill_combine_kernel<64>), cg, dim3(256), 0, s, chunk_idx, q_pos,
+                       H, nq, L, C, m, w.partial, w.logit, out, os, nitems);
+  else
+    hipLaunchKernelGGL((hils_prefill_combine_kernel<128>), cg, dim3(256), 0, s, chunk_idx, q_pos,
+                       H, nq, L, C, m, w.partial, w.logit, out, os, nitems);
   return hipGetLastError();
 }
 

@@ -56,6 +56,23 @@ hipError_t launch_mla_attn(const uint16_t* q, Str3 qs, const uint16_t* kv, Str3 
                            int nq, int L, int Hkv, const int32_t* token_idx, int topk, float scale,
                            uint16_t* out, Str3 os, float* lse, hipStream_t s);
 
+// tokens.hip: (query, slot) entries of a [batch][nq][m] block list bucketed by
+// (sequence, block), in tiles of kPairTile entries
+constexpr int kPairTile = 64;
+struct PairBuckets {
+  uint32_t* cnt;        // [nkeys] entries per bucket
+  uint32_t* cursor;     // [nkeys] scatter cursors
+  uint32_t* offs;       // [nkeys] first entry of each bucket in pairs
+  uint32_t* tile_off;   // [nkeys] first tile of each bucket
+  uint32_t* total;      // [4]: entries, tiles
+  uint32_t* part;       // scan partials
+  uint32_t* pairs;      // [npairs] entry indices (b*nq + q)*m + slot, grouped by bucket
+  uint32_t* tiles;      // [max tiles] bucket of each tile
+};
+PairBuckets carve_pair_buckets(void* ws, int batch, int nq, int m, int nblk, size_t* bytes);
+hipError_t launch_pair_buckets(const int32_t* block_idx, int batch, int nq, int m, int nblk,
+                               const PairBuckets& w, hipStream_t s);
+
 // hils.hip; ws (may be null) holds at least hils_workspace() bytes (0 when the
 // shape never splits its chunks over workgroups)
 size_t hils_workspace(int batch, int H, int D, int m);
@@ -69,7 +86,8 @@ hipError_t launch_hils_prefill(const uint16_t* q, Str3 qs, const uint16_t* k, St
                                const int32_t* chunk_idx, const uint16_t* proj,
                                const int32_t* q_pos, int batch, int nq, int L, int H, int D,
                                int C, int n_rows, int m, float scale_chunk, float scale_token,
-                               uint16_t* out, Str3 os, hipStream_t s);
+                               uint16_t* out, Str3 os, void* ws, hipStream_t s);
+size_t hils_prefill_workspace(int batch, int nq, int L, int H, int D, int C, int m);
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 

@@ -23,26 +23,15 @@ constexpr int kTQ = 64;  // pairs per scoring tile
 // keys per thread and per workgroup of the bucket-count scan
 constexpr int kScanPer = 16, kScanChunk = 256 * kScanPer;
 
-struct TokWs {
-  uint32_t* cnt;        // [nkeys]
-  uint32_t* cursor;     // [nkeys]
-  uint32_t* offs;       // [nkeys]
-  uint32_t* tile_off;   // [nkeys]
-  uint32_t* total;      // [4]
-  uint32_t* part;       // [2 * chunks of the bucket scan]
-  uint32_t* pairs;      // [npairs]
-  uint32_t* tiles;      // [max_tiles]
-  float* scores;        // [batch*nq*m*B]
-};
+static_assert(kTQ == kPairTile, "token scoring tiles are pair-bucket tiles");
 
-static TokWs carve(void* ws, int batch, int nq, int L, int B, int m, size_t* bytes) {
-  const size_t nblk = (L + B - 1) / B;
+PairBuckets carve_pair_buckets(void* ws, int batch, int nq, int m, int nblk, size_t* bytes) {
   const size_t nkeys = static_cast<size_t>(batch) * nblk;
   const size_t npairs = static_cast<size_t>(batch) * nq * m;
   const size_t max_tiles = (npairs + kTQ - 1) / kTQ + nkeys;
   char* p = static_cast<char*>(ws);
   size_t off = 0;
-  TokWs w;
+  PairBuckets w;
   auto take = [&](size_t n) { char* r = p ? p + off : nullptr; off += align256(n); return r; };
   w.cnt = reinterpret_cast<uint32_t*>(take(nkeys * 4));
   w.cursor = reinterpret_cast<uint32_t*>(take(nkeys * 4));
@@ -52,7 +41,22 @@ static TokWs carve(void* ws, int batch, int nq, int L, int B, int m, size_t* byt
   w.part = reinterpret_cast<uint32_t*>(take(2 * 4 * ((nkeys + kScanChunk - 1) / kScanChunk)));
   w.pairs = reinterpret_cast<uint32_t*>(take(npairs * 4));
   w.tiles = reinterpret_cast<uint32_t*>(take(max_tiles * 4));
-  w.scores = reinterpret_cast<float*>(take(npairs * B * 4));
+  if (bytes) *bytes = off;
+  return w;
+}
+
+struct TokWs : PairBuckets {
+  float* scores;        // [batch*nq*m*B]
+};
+
+static TokWs carve(void* ws, int batch, int nq, int L, int B, int m, size_t* bytes) {
+  const int nblk = (L + B - 1) / B;
+  const size_t npairs = static_cast<size_t>(batch) * nq * m;
+  size_t off = 0;
+  TokWs w;
+  static_cast<PairBuckets&>(w) = carve_pair_buckets(ws, batch, nq, m, nblk, &off);
+  w.scores = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + off) : nullptr;
+  off += align256(npairs * B * 4);
   if (bytes) *bytes = off;
   return w;
 }
@@ -271,6 +275,46 @@ __global__ void tile_table_kernel(const uint32_t* __restrict__ cnt,
   if (key >= nkeys) return;
   const uint32_t nt = (cnt[key] + kTQ - 1) / kTQ;
   for (uint32_t t = 0; t < nt; ++t) tiles[tile_off[key] + t] = static_cast<uint32_t>(key);
+}
+
+// Buckets of (query, slot) entries by (sequence, block), then the tile table:
+// entry e = (b*nq + q)*m + slot of block_idx goes to bucket b*nblk + block;
+// bucket k holds pairs[offs[k] .. offs[k] + cnt[k]) in no particular order,
+// split into tiles of kPairTile entries numbered from tile_off[k], and
+// tiles[i] names the bucket of tile i (total[0] entries, total[1] tiles).
+hipError_t launch_pair_buckets(const int32_t* block_idx, int batch, int nq, int m, int nblk,
+                               const PairBuckets& w, hipStream_t s) {
+  const int nkeys = batch * nblk;
+  const size_t npairs = static_cast<size_t>(batch) * nq * m;
+  // cnt and cursor are adjacent: clear both with one fill kernel
+  const size_t zero_n = (reinterpret_cast<char*>(w.offs) - reinterpret_cast<char*>(w.cnt)) / 4;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(std::min<size_t>((zero_n + 255) / 256, 4096)),
+                     dim3(256), 0, s, w.cnt, zero_n);
+  const unsigned pg = static_cast<unsigned>((npairs + 255) / 256);
+  const bool lds_hist = nblk <= kHistMax;
+  const int qpw = std::max(1, 4096 / m);
+  const dim3 hg((nq + qpw - 1) / qpw, batch);
+  if (lds_hist)
+    hipLaunchKernelGGL(count_pairs_kernel, hg, dim3(256), nblk * 4, s, block_idx, nq, m, nblk,
+                       qpw, w.cnt);
+  else
+    hipLaunchKernelGGL(count_pairs_direct_kernel, dim3(pg), dim3(256), 0, s, block_idx, nq, m,
+                       nblk, npairs, w.cnt);
+  const int nchunks = (nkeys + kScanChunk - 1) / kScanChunk;
+  if (nchunks > 1)
+    hipLaunchKernelGGL(bucket_partials_kernel, dim3(nchunks), dim3(256), 0, s, w.cnt, nkeys,
+                       w.part);
+  hipLaunchKernelGGL(scan_buckets_kernel, dim3(nchunks), dim3(256), 0, s, w.cnt, nkeys,
+                     nchunks > 1 ? w.part : nullptr, nchunks, w.offs, w.tile_off, w.total);
+  if (lds_hist)
+    hipLaunchKernelGGL(scatter_pairs_kernel, hg, dim3(256), nblk * 8, s, block_idx, nq, m, nblk,
+                       qpw, w.offs, w.cursor, w.pairs);
+  else
+    hipLaunchKernelGGL(scatter_pairs_direct_kernel, dim3(pg), dim3(256), 0, s, block_idx, nq, m,
+                       nblk, npairs, w.offs, w.cursor, w.pairs);
+  hipLaunchKernelGGL(tile_table_kernel, dim3((nkeys + 255) / 256), dim3(256), 0, s, w.cnt,
+                     w.tile_off, nkeys, w.tiles);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------ scoring
@@ -572,34 +616,8 @@ hipError_t launch_token_select(const uint16_t* qidx, Str3 qs, const uint16_t* ki
   const bool direct =
       nq == 1 || npairs * static_cast<size_t>(B) * d * 2 <= (static_cast<size_t>(256) << 20);
   if (!direct) {
-    // cnt and cursor are adjacent: clear both with one fill kernel
-    const size_t zero_n = (reinterpret_cast<char*>(w.offs) - reinterpret_cast<char*>(w.cnt)) / 4;
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(std::min<size_t>((zero_n + 255) / 256, 4096)),
-                       dim3(256), 0, s, w.cnt, zero_n);
-    const unsigned pg = static_cast<unsigned>((npairs + 255) / 256);
-    const bool lds_hist = nblk <= kHistMax;
-    const int qpw = std::max(1, 4096 / m);
-    const dim3 hg((nq + qpw - 1) / qpw, batch);
-    if (lds_hist)
-      hipLaunchKernelGGL(count_pairs_kernel, hg, dim3(256), nblk * 4, s, block_idx, nq, m, nblk,
-                         qpw, w.cnt);
-    else
-      hipLaunchKernelGGL(count_pairs_direct_kernel, dim3(pg), dim3(256), 0, s, block_idx, nq, m,
-                         nblk, npairs, w.cnt);
-    const int nchunks = (nkeys + kScanChunk - 1) / kScanChunk;
-    if (nchunks > 1)
-      hipLaunchKernelGGL(bucket_partials_kernel, dim3(nchunks), dim3(256), 0, s, w.cnt, nkeys,
-                         w.part);
-    hipLaunchKernelGGL(scan_buckets_kernel, dim3(nchunks), dim3(256), 0, s, w.cnt, nkeys,
-                       nchunks > 1 ? w.part : nullptr, nchunks, w.offs, w.tile_off, w.total);
-    if (lds_hist)
-      hipLaunchKernelGGL(scatter_pairs_kernel, hg, dim3(256), nblk * 8, s, block_idx, nq, m,
-                         nblk, qpw, w.offs, w.cursor, w.pairs);
-    else
-      hipLaunchKernelGGL(scatter_pairs_direct_kernel, dim3(pg), dim3(256), 0, s, block_idx, nq, m,
-                         nblk, npairs, w.offs, w.cursor, w.pairs);
-    hipLaunchKernelGGL(tile_table_kernel, dim3((nkeys + 255) / 256), dim3(256), 0, s, w.cnt,
-                       w.tile_off, nkeys, w.tiles);
+    const hipError_t e = launch_pair_buckets(block_idx, batch, nq, m, nblk, w, s);
+    if (e != hipSuccess) return e;
   }
 #define HISA_TS(D_, B_)                                                                       \
   do {                                                                                        \

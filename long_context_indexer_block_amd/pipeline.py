@@ -15,7 +15,7 @@ from __future__ import annotations
 import torch
 
 from . import (flat_indexer_topk, flat_indexer_topk_workspace_bytes, hils_two_level_attn_fwd,
-               hils_two_level_prefill_fwd, hils_workspace,
+               hils_prefill_workspace, hils_two_level_prefill_fwd, hils_workspace,
                hisa_auto_plan, hisa_block_score, hisa_block_summary, hisa_block_summary_update,
                hisa_select_blocks,
                hisa_token_select, hisa_token_select_workspace_bytes, sparse_attn_fwd,
@@ -253,6 +253,8 @@ class HilsPrefill:
         self.scores = torch.empty(b * H, nq, n, dtype=torch.float32, device=dev)
         self.chunk_idx = torch.empty(b * H, nq, m, dtype=torch.int32, device=dev)
         self.out = torch.empty(b, nq, H, D, dtype=torch.bfloat16, device=dev)
+        # bucketed attention (None: one workgroup per query and head)
+        self.ws = hils_prefill_workspace(b, nq, L, H, D, C, m, dev)
 
     def build_keys(self):
         b, L, H, D = self.k.shape
@@ -274,7 +276,7 @@ class HilsPrefill:
     def attend(self):
         hils_two_level_prefill_fwd(self.q, self.k, self.v, self.khat, self.chunk_idx, self.q_pos,
                                    self.C, self.scale_chunk, self.scale_token, proj=self.w_proj,
-                                   out=self.out)
+                                   out=self.out, workspace=self.ws)
 
     def run(self, build=True):
         if build:

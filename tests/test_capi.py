@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_match_header():
     names = _declared()
-    assert len(names) == 16
+    assert len(names) == 17
     lib = ctypes.CDLL(H.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -141,7 +141,7 @@ def test_hils_prefill_validation():
     L = H.lib()
     s = S(0, 1024, 64)
     args = [FAKE, s, FAKE, s, FAKE, s, FAKE, FAKE, FAKE, FAKE, 1, 4096, 4096, 16, 64, 64, 64, 32,
-            0.125, 0.125, FAKE, s, NULL]
+            0.125, 0.125, FAKE, s, NULL, 0, NULL]
     a = list(args)
     a[9] = NULL                                                      # q_pos missing
     assert L.hils_two_level_prefill_fwd(*a) == 1
@@ -164,6 +164,19 @@ def test_hils_prefill_validation():
     a = list(args)
     a[2] = ctypes.c_void_p(0x10002)                                  # k not 16-byte aligned
     assert L.hils_two_level_prefill_fwd(*a) == 2
+    a = list(args)
+    a[1] = S(0, 1024, 4)                                             # q head stride not 8k
+    assert L.hils_two_level_prefill_fwd(*a) == 2
+    # the bucketed path's scratch: per-entry partials dominate
+    need = L.hils_two_level_prefill_fwd_workspace_bytes(1, 4096, 4096, 16, 64, 64, 32)
+    assert need >= 16 * 4096 * 32 * 64 * 4 and need % 256 == 0
+    assert L.hils_two_level_prefill_fwd_workspace_bytes(1, 4096, 4096, 16, 96, 64, 32) == 0
+    a = list(args)
+    a[22], a[23] = FAKE, need - 1                                    # too small
+    assert L.hils_two_level_prefill_fwd(*a) == 5 and "needs" in _err()
+    a = list(args)
+    a[22], a[23] = ctypes.c_void_p(0x10010), need                    # not 256-byte aligned
+    assert L.hils_two_level_prefill_fwd(*a) == 5 and "aligned" in _err()
 
 
 def test_missing_library_raises(monkeypatch):

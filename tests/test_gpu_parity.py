@@ -452,14 +452,18 @@ def test_workload_hils_decode_1m():
 
 
 # ---------------------------------------------------------------- two-level prefill
-def _hils_prefill_check(w, exact, positions=None, heads=None):
+def _hils_prefill_check(w, exact, positions=None, heads=None, bucketed=True):
     """Run the causal two-level prefill of workload w on the GPU and check the
     queries at `positions` (default: all) of `heads` (default: all) against
-    the oracle's decode of the tokens up to each query."""
+    the oracle's decode of the tokens up to each query. bucketed=False runs
+    the per-query kernel (no workspace)."""
     inp = make_inputs(w, DEV, seed=0)
     C, m, nq = w.B, w.m, w.queries
     sc = 1.0 / math.sqrt(w.Dk)
     hp = HilsPrefill(inp["q"], inp["k"], inp["v"], inp["w_proj"], inp["q_pos"], C, m, sc, sc)
+    assert hp.ws is not None
+    if not bucketed:
+        hp.ws = None
     hp.run()
     torch.cuda.synchronize()
     Wp = f64(inp["w_proj"])
@@ -505,23 +509,49 @@ def _hils_prefill_check(w, exact, positions=None, heads=None):
 
 # every position of small causal prefills in the integer twin (exact
 # routing): queries inside the first chunk (only chunk 0), across chunk
-# boundaries, a partial last chunk, head width 128, chunks of 128 tokens,
-# m = 64 (four chunks per wave), two sequences
+# boundaries, a partial last chunk, head width 128, chunks of 128 and 256
+# tokens (several 64-token groups per chunk), m = 64, two sequences
 HILS_PREFILL_SMALL = [
     WORKLOADS["hils_prefill_64k"].with_(name="hilsp_c64", batch=2, L=700, m=8, Hq=3, Hkv=3,
                                         int_mode=True),
     WORKLOADS["hils_prefill_64k"].with_(name="hilsp_d128_c128", batch=1, L=1500, B=128, m=6,
                                         Hq=2, Hkv=2, Dk=128, Dv=128, d_idx=128, nq=700,
                                         int_mode=True),
+    WORKLOADS["hils_prefill_64k"].with_(name="hilsp_c256", batch=2, L=2100, B=256, m=4, Hq=2,
+                                        Hkv=2, nq=900, int_mode=True),
     WORKLOADS["hils_prefill_64k"].with_(name="hilsp_c64_m64", batch=1, L=4480, m=64, Hq=1,
                                         Hkv=1, nq=400, int_mode=True),
 ]
 
 
+@pytest.mark.parametrize("bucketed", [True, False], ids=["bucketed", "per_query"])
 @pytest.mark.parametrize("w", HILS_PREFILL_SMALL, ids=[w.name for w in HILS_PREFILL_SMALL])
-def test_hils_prefill_small(w):
-    log(f"case hils prefill small {w}")
-    assert _hils_prefill_check(w, exact=True) == 0
+def test_hils_prefill_small(w, bucketed):
+    log(f"case hils prefill small {w} bucketed={bucketed}")
+    assert _hils_prefill_check(w, exact=True, bucketed=bucketed) == 0
+
+
+def test_hils_prefill_no_projection():
+    # plain-mean chunk keys (proj None) on both paths
+    w = HILS_PREFILL_SMALL[0]
+    inp = make_inputs(w, DEV, seed=1)
+    sc = 1.0 / math.sqrt(w.Dk)
+    hp = HilsPrefill(inp["q"], inp["k"], inp["v"], None, inp["q_pos"], w.B, w.m, sc, sc)
+    out_b = hp.run().clone()
+    hp.ws = None
+    out_q = hp.run()
+    torch.cuda.synchronize()
+    I = np.eye(w.Dk)
+    for b in range(w.batch):
+        for h in range(w.Hq):
+            K = f64(inp["k"][b, :, h])
+            V = f64(inp["v"][b, :, h])
+            khat = O.block_summary(K, w.B)
+            refs = np.stack([O.hils_prefill_query(f64(inp["q"][b, i, h]), K, V, I, khat, i, w.B,
+                                                  w.m, sc, sc)[0] for i in range(w.L)])
+            for o, nm in ((out_b, "bucketed"), (out_q, "per query")):
+                check_attention(o[b, :, h].float().cpu().numpy(), refs,
+                                f"no-proj {nm} b={b} h={h}")
 
 
 def test_hils_prefill_matches_decode_at_last_position():
