@@ -132,6 +132,16 @@ hisa_status_t hisa_select_blocks(const float* block_scores, const int32_t* q_pos
                                  int nq, int n_rows, int B, int m, int32_t* block_idx,
                                  hisa_stream_t stream);
 
+/* Steps 2 and 3 in one call, for many queries: the same block_idx as
+ * hisa_block_score followed by hisa_select_blocks (bit for bit: the same
+ * exact products and selection), without writing the block scores to memory.
+ * Scores of 16 consecutive queries at a time are held on chip, so n_rows must
+ * be at most 1026 (HISA_ERR_UNSUPPORTED above: use the two calls); arguments
+ * otherwise as for those two. */
+hisa_status_t hisa_route_blocks(const void* qidx, hisa_strides_t qs, const int32_t* q_pos,
+                                int batch, int nq, const void* split, int n_rows, int d, int B,
+                                int m, int32_t* block_idx, hisa_stream_t stream);
+
 /* Step 4: token top-k inside the kept blocks (HISA explainer 1.2.2; HISA news
  * article, fine token selection). Candidates are the tokens j <= t of the
  * blocks in block_idx; each scores qidx . kidx[j]; the best min(k, #cand)
@@ -253,7 +263,8 @@ size_t hils_two_level_attn_fwd_workspace_bytes(int batch, int H, int D, int m);
  *             per-entry partial result merged per query; NULL runs one
  *             workgroup per (query, head) gathering its own chunks (same
  *             result up to fp32 rounding; for few queries). Too small is
- *             HISA_ERR_WORKSPACE. Its size grows as batch*H*nq*m*D*4 bytes.
+ *             HISA_ERR_WORKSPACE. Its size is about batch*H*(nq*m*(2D + 13)
+ *             + L*D*4) bytes (fp16 per-entry partials, the local keys).
  * q, k, v 16-byte aligned with strides in multiples of 8 elements; khat and
  * proj 16-byte aligned. batch*H <= 65535, batch*H*nq*m < 2^32; sizes must be
  * >= 1. */

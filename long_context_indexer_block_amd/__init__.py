@@ -40,6 +40,7 @@ _SIGS = {
     "hisa_block_summary_update": (_I, [_P, Strides, _I, _I, _I, _I, _P, _P, _P, _I, _I, _P]),
     "hisa_block_score": (_I, [_P, Strides, _P, _I, _I, _P, _I, _I, _I, _P, _P]),
     "hisa_select_blocks": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P]),
+    "hisa_route_blocks": (_I, [_P, Strides, _P, _I, _I, _P, _I, _I, _I, _I, _P, _P]),
     "hisa_token_select": (_I, [_P, Strides, _P, Strides, _P, _P, _I, _I, _I, _I, _I, _I, _I,
                                _P, _P, _P, _S, _P]),
     "hisa_token_select_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I]),
@@ -154,6 +155,22 @@ def hisa_select_blocks(block_scores, q_pos, B, m, out=None):
         out = torch.empty(b, nq, m, dtype=torch.int32, device=block_scores.device)
     _check(lib().hisa_select_blocks(_ptr(block_scores), _ptr(q_pos), b, nq, n, B, m, _ptr(out),
                                     _stream()))
+    return out
+
+
+ROUTE_MAX_ROWS = 64 * 16 + 2
+
+
+def hisa_route_blocks(qidx, q_pos, split, B, m, out=None):
+    """Steps 2 and 3 fused: qidx [b, nq, d] bf16, q_pos [b, nq] int32, split
+    [b, n, 3, d] (n <= ROUTE_MAX_ROWS) -> block_idx [b, nq, m] int32."""
+    _need(qidx, torch.bfloat16, "qidx")
+    b, nq, d = qidx.shape
+    n = split.shape[1]
+    if out is None:
+        out = torch.empty(b, nq, m, dtype=torch.int32, device=qidx.device)
+    _check(lib().hisa_route_blocks(_ptr(qidx), _str3(qidx, "bt"), _ptr(q_pos), b, nq, _ptr(split),
+                                   n, d, B, m, _ptr(out), _stream()))
     return out
 
 

@@ -156,6 +156,31 @@ hisa_status_t hisa_select_blocks(const float* block_scores, const int32_t* q_pos
                     "hisa_select_blocks");
 }
 
+hisa_status_t hisa_route_blocks(const void* qidx, hisa_strides_t qs, const int32_t* q_pos,
+                                int batch, int nq, const void* split, int n_rows, int d, int B,
+                                int m, int32_t* block_idx, hisa_stream_t stream) {
+  CHECK(qidx && q_pos && split && block_idx, HISA_ERR_NULL,
+        "qidx, q_pos, split and block_idx are required");
+  CHECK(batch >= 1 && nq >= 1 && n_rows >= 1, HISA_ERR_SHAPE,
+        "batch=%d nq=%d n_rows=%d must be >= 1", batch, nq, n_rows);
+  CHECK(n_rows <= hisa::kRouteMaxRows, HISA_ERR_UNSUPPORTED,
+        "n_rows=%d above %d: use hisa_block_score and hisa_select_blocks", n_rows,
+        hisa::kRouteMaxRows);
+  CHECK(static_cast<long long>(batch) * ((nq + 15) / 16) <= 0x7fffffffLL, HISA_ERR_UNSUPPORTED,
+        "grid too large");
+  CHECK(m >= 2, HISA_ERR_UNSUPPORTED, "m=%d must be >= 2 (first and local block)", m);
+  hisa_status_t st;
+  if ((st = check_d(d)) != HISA_OK) return st;
+  if ((st = check_block(B)) != HISA_OK) return st;
+  if ((st = check_bf16(qidx, qs, "qidx")) != HISA_OK) return st;
+  CHECK(aligned16(split), HISA_ERR_SHAPE, "split must be 16-byte aligned");
+  return hip_status(hisa::launch_route_blocks(static_cast<const uint16_t*>(qidx), s3(qs), q_pos,
+                                              batch, nq, static_cast<const uint16_t*>(split),
+                                              n_rows, d, B, m, block_idx,
+                                              static_cast<hipStream_t>(stream)),
+                    "hisa_route_blocks");
+}
+
 size_t hisa_token_select_workspace_bytes(int batch, int nq, int L, int B, int m, int k) {
   if (batch < 1 || nq < 1 || L < 1 || B < 1 || m < 1) return 0;
   return hisa::token_select_workspace(batch, nq, L, B, m, k);

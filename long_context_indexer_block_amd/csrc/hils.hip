@@ -269,7 +269,7 @@ __global__ __launch_bounds__(64 * W) void hils_prefill_kernel(
 //   1. local keys: kloc[bh][j] = proj @ (mean of tokens j/C*C .. j), every j;
 //   2. per tile, on matrix cores: the chunk's token softmax for the tile's
 //      queries (causal within the local chunk) times V, normalised, into
-//      partial[e][:], and the chunk logit (scale_chunk * q . key) into
+//      partial[e][:] (scaled fp16), and the chunk logit (scale_chunk * q . key) into
 //      logit[e], key = khat of the chunk or kloc of the query's position when
 //      it is the query's local chunk;
 //   3. per query, the softmax over its chosen chunks' logits mixes the
@@ -278,8 +278,9 @@ __global__ __launch_bounds__(64 * W) void hils_prefill_kernel(
 struct PrefillWs {
   PairBuckets pb;
   float* kloc;      // [batch*H][L][D]
-  float* logit;     // [batch*H*nq*m]
-  float* partial;   // [batch*H*nq*m][D]
+  float* logit;        // [batch*H*nq*m]
+  int8_t* pexp;        // [batch*H*nq*m] scale exponent of each partial row
+  uint16_t* partial;   // [batch*H*nq*m][D] fp16, row scaled by 2^-pexp
 };
 
 static PrefillWs carve_prefill(void* ws, int batch, int nq, int L, int H, int D, int C, int m,
@@ -293,7 +294,8 @@ static PrefillWs carve_prefill(void* ws, int batch, int nq, int L, int H, int D,
   auto take = [&](size_t n) { char* r = p ? p + off : nullptr; off += align256(n); return r; };
   w.kloc = reinterpret_cast<float*>(take(static_cast<size_t>(bh) * L * D * 4));
   w.logit = reinterpret_cast<float*>(take(npairs * 4));
-  w.partial = reinterpret_cast<float*>(take(npairs * D * 4));
+  w.pexp = reinterpret_cast<int8_t*>(take(npairs));
+  w.partial = reinterpret_cast<uint16_t*>(take(npairs * D * 2));
   if (bytes) *bytes = off;
   return w;
 }
@@ -376,13 +378,16 @@ __global__ __launch_bounds__(256) void hils_local_keys_kernel(
   }
 }
 
-// Tile kernel: 4 waves, wave w takes entries 16w .. 16w+15 of the tile (one
-// per lane column r = l%16). Per 64-token group of the chunk, V is staged in
-// LDS (rows padded by 16 bytes) and K fragments come straight from global.
-// S^T = K Q^T on 16x16x32 bf16 MFMA leaves in lane l the entry l%16 and the
-// tokens 4(l/16)..+3 of each 16-token tile: the A operand of the 16x16x16
-// P V product, with V^T fragments from ds_read_tr16_b64. Online softmax over
-// the chunk's groups (one group for C = 64).
+// Tile kernel: a workgroup of 4 waves takes TPW consecutive tiles of the
+// tile table (mostly of one bucket, whose chunk K/V it loads once); wave w
+// takes entries 16w .. 16w+15 of each tile, one per lane column r = l%16.
+// The chunk's V rows are staged in LDS (rows padded by 16 bytes); K
+// fragments come straight from global (kept in registers across tiles when
+// the chunk is one 64-token group). S^T = K Q^T on 16x16x32 bf16 MFMA leaves
+// in lane l the entry l%16 and the tokens 4(l/16)..+3 of each 16-token tile:
+// the A operand of the 16x16x16 P V product, with V^T fragments from
+// ds_read_tr16_b64. Online softmax over the chunk's 64-token groups. Each
+// wave's 16 result rows are staged in LDS and written as whole rows.
 struct TileTabs {
   const uint32_t* cnt;
   const uint32_t* offs;
@@ -411,51 +416,91 @@ __device__ __forceinline__ float sum_x4_groups(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <int D, int C>
+template <int D>
+__device__ __forceinline__ void load_kfrags(uint4 (&kf)[4][D / 32], const uint16_t* kb, int64_t kst,
+                                            int j0, int L, int r, int g) {
+#pragma unroll
+  for (int tau = 0; tau < 4; ++tau) {
+    const int j = min(j0 + 16 * tau + r, L - 1);
+#pragma unroll
+    for (int x = 0; x < D / 32; ++x)
+      kf[tau][x] = *reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(j) * kst + 32 * x +
+                                                   8 * g);
+  }
+}
+
+template <int D, int C, int TPW>
 __global__ __launch_bounds__(256) void hils_pair_chunk_kernel(
     const uint16_t* __restrict__ q, Str3 qs, const uint16_t* __restrict__ k, Str3 ks,
     const uint16_t* __restrict__ v, Str3 vs, const float* __restrict__ khat,
     const float* __restrict__ kloc, const int32_t* __restrict__ q_pos, int H, int nq, int L,
-    int n_rows, int m, TileTabs tt, unsigned grid_tiles, float scale_chunk,
-    float scale_token_log2, float* __restrict__ partial, float* __restrict__ logit) {
+    int n_rows, int m, TileTabs tt, unsigned grid_wg, float scale_chunk, float scale_token_log2,
+    uint16_t* __restrict__ partial, int8_t* __restrict__ pexp, float* __restrict__ logit) {
   constexpr int NKS = D / 32;     // k-steps of S^T
   constexpr int NDB = D / 16;     // 16-column blocks of O
+  constexpr int NG = C / 64;      // 64-token groups per chunk
   constexpr int RS = 2 * D + 16;  // LDS bytes per staged V row
-  __shared__ __align__(16) unsigned char vt[64 * RS];
+  constexpr int OS = D + 4;       // LDS floats per staged result row
+  constexpr int LPR = D / 4;      // lanes per result row on the way out
+  constexpr int RPI = 64 / LPR;   // result rows per store instruction
+  __shared__ __align__(16) unsigned char vt[C * RS];
+  __shared__ __align__(16) float ot[4][16 * OS];
   // the chip deals workgroups round-robin to its 8 XCDs: give each XCD a
   // contiguous run of tiles, so that the tiles of one chunk share an L2
-  const unsigned per = grid_tiles / 8;
-  const unsigned tile = (blockIdx.x % 8) * per + blockIdx.x / 8;
-  if (tile >= tt.total[1]) return;
-  const uint32_t key = tt.tiles[tile];
-  const int bh = static_cast<int>(key / n_rows), c = static_cast<int>(key % n_rows);
-  const int b = bh / H, h = bh % H;
-  const uint32_t first = tt.offs[key] + (tile - tt.tile_off[key]) * kPairTile;
-  const uint32_t end = tt.offs[key] + tt.cnt[key];
+  const unsigned per = grid_wg / 8;
+  const unsigned wg = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  const unsigned ntiles = tt.total[1];
+  const unsigned t_first = wg * TPW;
+  if (t_first >= ntiles) return;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 4, r = l & 15;
-  const uint32_t pi = first + 16 * w + r;
-  const bool pv = pi < end;
-  const uint32_t e = pv ? tt.pairs[pi] : 0u;
-  const int qi = pv ? static_cast<int>(e / m - static_cast<uint32_t>(bh) * nq) : 0;
-  const int t = min(max(q_pos[static_cast<int64_t>(b) * nq + qi], 0), L - 1);
-  const int bt = t / C;
-  const uint16_t* qrow = q + b * qs.b + static_cast<int64_t>(qi) * qs.t + h * qs.h;
-  bf16x8 qf[NKS];
+  float* orow = ot[w];
+  // ---- gathers of all TPW tiles first, so that their dependent loads
+  // (tile -> bucket -> entry -> query row, position -> key row) overlap
+  uint32_t key[TPW], e[TPW];
+  int t[TPW];
+  bool pv[TPW];
+  bf16x8 qf[TPW][NKS];
 #pragma unroll
-  for (int x = 0; x < NKS; ++x)
-    qf[x] = as_bf16x8(pv ? *reinterpret_cast<const uint4*>(qrow + 32 * x + 8 * g)
-                         : make_uint4(0u, 0u, 0u, 0u));
-  // chunk logit: q . key over this lane's columns 32x + 8g .. +7
-  {
-    const float* kr = c == bt ? kloc + (static_cast<int64_t>(bh) * L + t) * D
-                              : khat + (static_cast<int64_t>(bh) * n_rows + c) * D;
+  for (int j = 0; j < TPW; ++j)
+    key[j] = t_first + j < ntiles ? tt.tiles[t_first + j] : 0xffffffffu;
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    pv[j] = false;
+    e[j] = 0u;
+    if (key[j] != 0xffffffffu) {
+      const uint32_t first = tt.offs[key[j]] + (t_first + j - tt.tile_off[key[j]]) * kPairTile;
+      const uint32_t pi = first + 16 * w + r;
+      pv[j] = pi < tt.offs[key[j]] + tt.cnt[key[j]];
+      e[j] = pv[j] ? tt.pairs[pi] : 0u;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int bhj = static_cast<int>(key[j] / n_rows);
+    const int bj = bhj / H, hj = bhj % H;
+    const int qi = pv[j] ? static_cast<int>(e[j] / m - static_cast<uint32_t>(bhj) * nq) : 0;
+    const uint16_t* qrow = q + bj * qs.b + static_cast<int64_t>(qi) * qs.t + hj * qs.h;
+#pragma unroll
+    for (int x = 0; x < NKS; ++x)
+      qf[j][x] = as_bf16x8(pv[j] ? *reinterpret_cast<const uint4*>(qrow + 32 * x + 8 * g)
+                                 : make_uint4(0u, 0u, 0u, 0u));
+    t[j] = pv[j] ? min(max(q_pos[static_cast<int64_t>(bj) * nq + qi], 0), L - 1) : 0;
+  }
+  // chunk logits: q . key over this lane's columns 32x + 8g .. +7, key = the
+  // chunk's khat row or, for the query's own chunk, its causal local key
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int bhj = static_cast<int>(key[j] / n_rows), cj = static_cast<int>(key[j] % n_rows);
+    const int btj = t[j] / C;
+    const float* kr = cj == btj ? kloc + (static_cast<int64_t>(bhj) * L + t[j]) * D
+                                : khat + (static_cast<int64_t>(bhj) * n_rows + cj) * D;
     float part = 0.0f;
-    if (pv) {
+    if (pv[j]) {
 #pragma unroll
       for (int x = 0; x < NKS; ++x) {
         const float4 k0 = *reinterpret_cast<const float4*>(kr + 32 * x + 8 * g);
         const float4 k1 = *reinterpret_cast<const float4*>(kr + 32 * x + 8 * g + 4);
-        const uint4 qw = __builtin_bit_cast(uint4, qf[x]);
+        const uint4 qw = __builtin_bit_cast(uint4, qf[j][x]);
         part = fmaf(bf16_lo(qw.x), k0.x, part); part = fmaf(bf16_hi(qw.x), k0.y, part);
         part = fmaf(bf16_lo(qw.y), k0.z, part); part = fmaf(bf16_hi(qw.y), k0.w, part);
         part = fmaf(bf16_lo(qw.z), k1.x, part); part = fmaf(bf16_hi(qw.z), k1.y, part);
@@ -463,105 +508,141 @@ __global__ __launch_bounds__(256) void hils_pair_chunk_kernel(
       }
     }
     part = sum_x4_groups(part);
-    if (pv && g == 0) logit[e] = c <= bt ? part * scale_chunk : -INFINITY;
+    if (pv[j] && g == 0) logit[e[j]] = cj <= btj ? part * scale_chunk : -INFINITY;
   }
-  const uint16_t* kb = k + b * ks.b + h * ks.h;
-  const uint16_t* vb = v + b * vs.b + h * vs.h;
-  float mrun = -INFINITY, lsum = 0.0f;
-  f32x4 o[NDB];
+  // ---- the tiles
+  uint32_t cur = 0xffffffffu;
+  uint4 kf[4][NKS];
 #pragma unroll
-  for (int x = 0; x < NDB; ++x) o[x] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  const int j_end = min(L, (c + 1) * C);
-  for (int j0 = c * C; j0 < j_end; j0 += 64) {
-    if (j0 != c * C) __syncthreads();  // the previous group's V reads are done
-    for (int x = threadIdx.x; x < 64 * D / 8; x += 256) {
-      const int row = x / (D / 8), ch = x % (D / 8);
-      const int j = min(j0 + row, L - 1);
-      *reinterpret_cast<uint4*>(vt + row * RS + 16 * ch) =
-          *reinterpret_cast<const uint4*>(vb + static_cast<int64_t>(j) * vs.t + 8 * ch);
+  for (int j = 0; j < TPW; ++j) {
+    if (key[j] == 0xffffffffu) break;
+    const int bh = static_cast<int>(key[j] / n_rows), c = static_cast<int>(key[j] % n_rows);
+    const int b = bh / H, h = bh % H;
+    const uint16_t* kb = k + b * ks.b + h * ks.h;
+    if (key[j] != cur) {
+      if (cur != 0xffffffffu) __syncthreads();  // the previous chunk's V reads are done
+      cur = key[j];
+      const uint16_t* vb = v + b * vs.b + h * vs.h;
+      for (int x = threadIdx.x; x < C * D / 8; x += 256) {
+        const int row = x / (D / 8), ch = x % (D / 8);
+        const int jj = min(c * C + row, L - 1);
+        *reinterpret_cast<uint4*>(vt + row * RS + 16 * ch) =
+            *reinterpret_cast<const uint4*>(vb + static_cast<int64_t>(jj) * vs.t + 8 * ch);
+      }
+      if constexpr (NG == 1) load_kfrags<D>(kf, kb, ks.t, c * C, L, r, g);
+      __syncthreads();  // V staged
     }
-    uint4 kf[4][NKS];
+    float mrun = -INFINITY, lsum = 0.0f;
+    f32x4 o[NDB];
 #pragma unroll
-    for (int tau = 0; tau < 4; ++tau) {
-      const int j = min(j0 + 16 * tau + r, L - 1);
+    for (int x = 0; x < NDB; ++x) o[x] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int x = 0; x < NKS; ++x)
-        kf[tau][x] = *reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(j) * ks.t +
-                                                     32 * x + 8 * g);
-    }
-    __syncthreads();  // V staged
-    float sv[4][4];
-    float gmax = -INFINITY;
+    for (int gi = 0; gi < NG; ++gi) {
+      const int j0 = c * C + 64 * gi;
+      if (j0 >= L) break;
+      if constexpr (NG > 1) load_kfrags<D>(kf, kb, ks.t, j0, L, r, g);
+      float sv[4][4];
+      float gmax = -INFINITY;
 #pragma unroll
-    for (int tau = 0; tau < 4; ++tau) {
-      f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int tau = 0; tau < 4; ++tau) {
+        f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int x = 0; x < NKS; ++x) sacc = mfma16(as_bf16x8(kf[tau][x]), qf[x], sacc);
+        for (int x = 0; x < NKS; ++x) sacc = mfma16(as_bf16x8(kf[tau][x]), qf[j][x], sacc);
 #pragma unroll
-      for (int ee = 0; ee < 4; ++ee) {
-        const int j = j0 + 16 * tau + 4 * g + ee;
-        sv[tau][ee] = pv && j <= t ? sacc[ee] * scale_token_log2 : -INFINITY;
-        gmax = fmaxf(gmax, sv[tau][ee]);
+        for (int ee = 0; ee < 4; ++ee) {
+          const int jj = j0 + 16 * tau + 4 * g + ee;
+          sv[tau][ee] = pv[j] && jj <= t[j] ? sacc[ee] * scale_token_log2 : -INFINITY;
+          gmax = fmaxf(gmax, sv[tau][ee]);
+        }
+      }
+      gmax = max_x4_groups(gmax);
+      const float mnew = fmaxf(mrun, gmax);
+      if (gi > 0) {
+        const float alpha = mrun == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mrun - mnew);
+        lsum *= alpha;
+#pragma unroll
+        for (int ee = 0; ee < 4; ++ee) {
+          const float ae = __shfl(alpha, 4 * g + ee, 64);
+#pragma unroll
+          for (int x = 0; x < NDB; ++x) o[x][ee] *= ae;
+        }
+      }
+      mrun = mnew;
+      const float moff = mnew == -INFINITY ? 0.0f : -mnew;
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau) {
+        v4s_t pa;
+#pragma unroll
+        for (int ee = 0; ee < 4; ++ee) {
+          const float p = __builtin_amdgcn_exp2f(sv[tau][ee] + moff);
+          lsum += p;
+          pa[ee] = static_cast<short>(f32_to_bf16(p));
+        }
+        const unsigned char* vrow =
+            vt + (64 * gi + 16 * tau + 4 * g + (r >> 2)) * RS + 8 * (r & 3);
+#pragma unroll
+        for (int x = 0; x < NDB; ++x) {
+          const v4s_t vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s_t*)(vrow + 32 * x));
+          o[x] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vf, o[x], 0, 0, 0);
+        }
       }
     }
-    gmax = max_x4_groups(gmax);
-    const float mnew = fmaxf(mrun, gmax);
-    if (j0 != c * C) {
-      const float alpha = mrun == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mrun - mnew);
-      lsum *= alpha;
+    lsum = sum_x4_groups(lsum);
+    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+    // O row 4g + ee (the entry of lane 4g + ee), column 16x + r -> LDS, then
+    // each result row leaves as LPR 16-byte pieces
 #pragma unroll
-      for (int ee = 0; ee < 4; ++ee) {
-        const float ae = __shfl(alpha, 4 * g + ee, 64);
+    for (int ee = 0; ee < 4; ++ee)
 #pragma unroll
-        for (int x = 0; x < NDB; ++x) o[x][ee] *= ae;
+      for (int x = 0; x < NDB; ++x) orow[(4 * g + ee) * OS + 16 * x + r] = o[x][ee];
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+#pragma unroll
+    for (int it = 0; it < 16 / RPI; ++it) {
+      const int rr = RPI * it + l / LPR;
+      const uint32_t er = __shfl(e[j], rr, 64);
+      const float ir = __shfl(inv, rr, 64);
+      const int vr = __shfl(pv[j] ? 1 : 0, rr, 64);
+      const float4 val = *reinterpret_cast<const float4*>(orow + rr * OS + 4 * (l % LPR));
+      const float x0 = val.x * ir, x1 = val.y * ir, x2 = val.z * ir, x3 = val.w * ir;
+      // the row leaves as fp16 scaled by 2^-E, E the exponent of its largest
+      // magnitude (so that it lies in [0.5, 1)): 11 significant bits relative
+      // to the row maximum for any magnitude; E goes to pexp
+      float amax = fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3)));
+#pragma unroll
+      for (int sh = 1; sh < LPR; sh <<= 1) amax = fmaxf(amax, __shfl_xor(amax, sh, 64));
+      const int ex = min(max(static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu) - 126, -125),
+                         126);
+      const float sc = __uint_as_float(static_cast<uint32_t>(127 - ex) << 23);
+      if (vr) {
+        const _Float16 h0 = static_cast<_Float16>(x0 * sc), h1 = static_cast<_Float16>(x1 * sc);
+        const _Float16 h2 = static_cast<_Float16>(x2 * sc), h3 = static_cast<_Float16>(x3 * sc);
+        const uint32_t p01 = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h0)) |
+                             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h1)) << 16);
+        const uint32_t p23 = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h2)) |
+                             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h3)) << 16);
+        *reinterpret_cast<uint2*>(partial + static_cast<int64_t>(er) * D + 4 * (l % LPR)) =
+            make_uint2(p01, p23);
+        if (l % LPR == 0) pexp[er] = static_cast<int8_t>(ex);
       }
     }
-    mrun = mnew;
-    const float moff = mnew == -INFINITY ? 0.0f : -mnew;
-    const int sl = l & 15;
-#pragma unroll
-    for (int tau = 0; tau < 4; ++tau) {
-      v4s_t pa;
-#pragma unroll
-      for (int ee = 0; ee < 4; ++ee) {
-        const float p = __builtin_amdgcn_exp2f(sv[tau][ee] + moff);
-        lsum += p;
-        pa[ee] = static_cast<short>(f32_to_bf16(p));
-      }
-      const unsigned char* vrow = vt + (16 * tau + 4 * g + (sl >> 2)) * RS + 8 * (sl & 3);
-#pragma unroll
-      for (int x = 0; x < NDB; ++x) {
-        const v4s_t vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s_t*)(vrow + 32 * x));
-        o[x] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vf, o[x], 0, 0, 0);
-      }
-    }
-  }
-  lsum = sum_x4_groups(lsum);
-  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-  // O row 4g + ee is the entry of lane 4g + ee; column 16x + r
-#pragma unroll
-  for (int ee = 0; ee < 4; ++ee) {
-    const int src = 4 * g + ee;
-    const uint32_t er = __shfl(e, src, 64);
-    const float ir = __shfl(inv, src, 64);
-    const int vr = __shfl(pv ? 1 : 0, src, 64);
-    if (vr) {
-      float* pr = partial + static_cast<int64_t>(er) * D + r;
-#pragma unroll
-      for (int x = 0; x < NDB; ++x) pr[16 * x] = o[x][ee] * ir;
-    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
   }
 }
 
 // One wave per (bh, query): the softmax over the chosen chunks' logits
-// (lane s holds slot s) mixes the partials; lane l owns columns l + 64x.
+// (lane s holds slot s) mixes the scaled fp16 partials. Lane l reads columns
+// 2(l % (D/2)) .. +1 of slots s = SL*i + l / (D/2), SL = 128 / D slots per
+// load instruction; the SL lane groups are summed at the end.
 template <int D>
 __global__ __launch_bounds__(256) void hils_prefill_combine_kernel(
     const int32_t* __restrict__ chunk_idx, const int32_t* __restrict__ q_pos, int H, int nq,
-    int L, int C, int m, const float* __restrict__ partial, const float* __restrict__ logit,
-    uint16_t* __restrict__ out, Str3 os, int64_t nitems) {
-  constexpr int NX = D / 64;
+    int L, int C, int m, const uint16_t* __restrict__ partial, const int8_t* __restrict__ pexp,
+    const float* __restrict__ logit, uint16_t* __restrict__ out, Str3 os, int64_t nitems) {
+  constexpr int HP = D / 2;        // lanes per slot
+  constexpr int SL = 64 / HP;      // slots per load instruction
   const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (item >= nitems) return;
   const int l = threadIdx.x & 63;
@@ -576,28 +657,44 @@ __global__ __launch_bounds__(256) void hils_prefill_combine_kernel(
   const float mx = wave_max(lg);
   const float wgt = ok && mx != -INFINITY ? __expf(lg - mx) : 0.0f;
   const float z = wave_sum(wgt);
-  float acc[NX];
-#pragma unroll
-  for (int x = 0; x < NX; ++x) acc[x] = 0.0f;
-  for (int s0 = 0; s0 < m; s0 += 8) {
-    float val[8][NX], ws[8];
+  // the mixing weight carries the slot's partial scale 2^E
+  const float wmix = ok ? wgt * __uint_as_float(static_cast<uint32_t>(127 + pexp[e0 + l]) << 23)
+                        : 0.0f;
+  const int sg = l / HP, col = 2 * (l % HP);
+  float a0 = 0.0f, a1 = 0.0f;
+  for (int s0 = 0; s0 < m; s0 += 8 * SL) {
+    uint32_t val[8];
+    float ws[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int s = s0 + u;
-      ws[u] = s < m ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), s)) : 0.0f;
-#pragma unroll
-      for (int x = 0; x < NX; ++x)
-        val[u][x] = ws[u] != 0.0f ? partial[(e0 + s) * D + l + 64 * x] : 0.0f;
+      const int s = s0 + SL * u + sg;
+      ws[u] = __shfl(wmix, s & 63, 64);
+      ws[u] = s < m ? ws[u] : 0.0f;
+      val[u] = ws[u] != 0.0f
+                   ? *reinterpret_cast<const uint32_t*>(partial + (e0 + s) * D + col)
+                   : 0u;
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int x = 0; x < NX; ++x) acc[x] = fmaf(ws[u], val[u][x], acc[x]);
+    for (int u = 0; u < 8; ++u) {
+      const _Float16 h0 = __builtin_bit_cast(_Float16, static_cast<uint16_t>(val[u] & 0xffffu));
+      const _Float16 h1 = __builtin_bit_cast(_Float16, static_cast<uint16_t>(val[u] >> 16));
+      a0 = fmaf(ws[u], static_cast<float>(h0), a0);
+      a1 = fmaf(ws[u], static_cast<float>(h1), a1);
+    }
+  }
+  if constexpr (SL == 2) {
+    const auto s0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a0), __float_as_uint(a0),
+                                                     false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a1), __float_as_uint(a1),
+                                                     false, false);
+    a0 = __uint_as_float(s0[0]) + __uint_as_float(s0[1]);
+    a1 = __uint_as_float(s1[0]) + __uint_as_float(s1[1]);
   }
   const float iz = z > 0.0f ? 1.0f / z : 0.0f;
-  uint16_t* orow = out + b * os.b + static_cast<int64_t>(qi) * os.t + h * os.h;
-#pragma unroll
-  for (int x = 0; x < NX; ++x) orow[l + 64 * x] = f32_to_bf16(acc[x] * iz);
+  if (sg == 0) {
+    uint16_t* orow = out + b * os.b + static_cast<int64_t>(qi) * os.t + h * os.h;
+    *reinterpret_cast<uint32_t*>(orow + col) = pack_bf16x2(a0 * iz, a1 * iz);
+  }
 }
 
 hipError_t launch_hils_prefill(const uint16_t* q, Str3 qs, const uint16_t* k, Str3 ks,
@@ -630,13 +727,15 @@ hipError_t launch_hils_prefill(const uint16_t* q, Str3 qs, const uint16_t* k, St
                        L, C, proj, w.kloc);
   const size_t npairs = static_cast<size_t>(bh) * nq * m;
   const size_t max_tiles = (npairs + kPairTile - 1) / kPairTile + static_cast<size_t>(bh) * n_rows;
-  const unsigned grid_tiles = static_cast<unsigned>((max_tiles + 7) / 8 * 8);
+  const int tpw = 2;  // tiles per workgroup
+  const unsigned grid_wg = static_cast<unsigned>(((max_tiles + tpw - 1) / tpw + 7) / 8 * 8);
   const TileTabs tt{w.pb.cnt, w.pb.offs, w.pb.tile_off, w.pb.total, w.pb.pairs, w.pb.tiles};
   const float stl2 = scale_token * 1.4426950408889634f;
 #define HISA_PC(D_, C_)                                                                          \
-  hipLaunchKernelGGL((hils_pair_chunk_kernel<D_, C_>), dim3(grid_tiles), dim3(256), 0, s, q, qs,  \
-                     k, ks, v, vs, khat, w.kloc, q_pos, H, nq, L, n_rows, m, tt, grid_tiles,      \
-                     scale_chunk, stl2, w.partial, w.logit)
+  hipLaunchKernelGGL((hils_pair_chunk_kernel<D_, C_, 2>), dim3(grid_wg),           \
+                     dim3(256), 0, s, q,                                                          \
+                     qs, k, ks, v, vs, khat, w.kloc, q_pos, H, nq, L, n_rows, m, tt, grid_wg,     \
+                     scale_chunk, stl2, w.partial, w.pexp, w.logit)
   if (D == 64) {
     if (C == 64) HISA_PC(64, 64); else if (C == 128) HISA_PC(64, 128); else HISA_PC(64, 256);
   } else {
@@ -647,10 +746,10 @@ hipError_t launch_hils_prefill(const uint16_t* q, Str3 qs, const uint16_t* k, St
   const dim3 cg(static_cast<unsigned>((nitems + 3) / 4));
   if (D == 64)
     hipLaunchKernelGGL((hils_prefill_combine_kernel<64>), cg, dim3(256), 0, s, chunk_idx, q_pos,
-                       H, nq, L, C, m, w.partial, w.logit, out, os, nitems);
+                       H, nq, L, C, m, w.partial, w.pexp, w.logit, out, os, nitems);
   else
     hipLaunchKernelGGL((hils_prefill_combine_kernel<128>), cg, dim3(256), 0, s, chunk_idx, q_pos,
-                       H, nq, L, C, m, w.partial, w.logit, out, os, nitems);
+                       H, nq, L, C, m, w.partial, w.pexp, w.logit, out, os, nitems);
   return hipGetLastError();
 }
 

@@ -292,6 +292,66 @@ __device__ __forceinline__ void wave_compact(const uint32_t (&key)[IT], uint32_t
   }
 }
 
+// Top K <= 64 of a wave's items with fewer vector instructions: the K-th
+// largest of the 64 lane maxima is a lower bound of the K-th largest item
+// (K lanes hold an item at least that large), so only the items at or above
+// it can be kept. For spread scores they are a few dozen: they are moved to
+// LDS in position order (lkey/lpos, kSelSmall entries) and the exact
+// selection runs on two items per lane. More than kSelSmall of them (mass
+// ties) takes the direct path. emit(rank, position) gets the kept positions
+// in ascending order, rank 0 .. K-1.
+constexpr int kSelSmall = 128;
+
+template <int IT, class Emit>
+__device__ __forceinline__ void wave_topk(const uint32_t (&key)[IT], uint32_t okm, uint32_t K,
+                                          uint32_t* lkey, int* lpos, Emit emit) {
+  const int l = lane_id();
+  if constexpr (IT >= 4) {
+    if (K <= 64) {
+      uint32_t lm = 0;
+#pragma unroll
+      for (int i = 0; i < IT; ++i) lm = (okm >> i) & 1u ? max(lm, key[i]) : lm;
+      const uint32_t lk[1] = {lm};
+      const uint32_t t1 = wave_select(lk, 1u, K).T;
+      uint32_t c = 0;
+#pragma unroll
+      for (int i = 0; i < IT; ++i)
+        c += static_cast<uint32_t>(__popcll(__ballot(((okm >> i) & 1u) && key[i] >= t1)));
+      if (c <= kSelSmall) {
+        uint32_t base = 0;
+#pragma unroll
+        for (int i = 0; i < IT; ++i) {
+          const bool keep = ((okm >> i) & 1u) && key[i] >= t1;
+          const uint64_t km = __ballot(keep);
+          if (keep) {
+            const uint32_t e = base + lanes_below(km);
+            lkey[e] = key[i];
+            lpos[e] = 64 * i + l;
+          }
+          base += static_cast<uint32_t>(__popcll(km));
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        uint32_t k2[kSelSmall / 64];
+        uint32_t ok2 = 0;
+#pragma unroll
+        for (int i = 0; i < kSelSmall / 64; ++i) {
+          const uint32_t e = 64 * i + l;
+          k2[i] = e < c ? lkey[e] : 0u;
+          ok2 |= e < c ? (1u << i) : 0u;
+        }
+        const WaveSel sel = wave_select(k2, ok2, K);
+        wave_compact(k2, ok2, sel, [&](int i, uint32_t pos) { emit(pos, lpos[64 * i + l]); });
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        return;
+      }
+    }
+  }
+  const WaveSel sel = wave_select(key, okm, K);
+  wave_compact(key, okm, sel, [&](int i, uint32_t pos) { emit(pos, 64 * i + l); });
+}
+
 constexpr int kSelUnion = 1024;  // LDS entries for the waves' kept candidates
 
 template <int W, int IT>
@@ -299,7 +359,7 @@ __global__ __launch_bounds__(64 * W) void select_blocks_wave_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ q_pos, int nq, int n_rows,
     int B, int m, int32_t* __restrict__ block_idx) {
   constexpr int S = 64 * IT;  // candidates per wave
-  constexpr int CAP = W > 1 ? kSelUnion : 1;
+  constexpr int CAP = W > 1 ? kSelUnion : kSelSmall;
   __shared__ uint32_t ckey[CAP];
   __shared__ int cpos[CAP];
   __shared__ int ccnt[W];
@@ -325,10 +385,9 @@ __global__ __launch_bounds__(64 * W) void select_blocks_wave_kernel(
     okm |= p < n ? (1u << i) : 0u;
   }
   if constexpr (W == 1) {
-    if (K > 0) {
-      const WaveSel sel = wave_select(key, okm, static_cast<uint32_t>(K));
-      wave_compact(key, okm, sel, [&](int i, uint32_t pos) { out[1 + pos] = 64 * i + l + 1; });
-    }
+    if (K > 0)
+      wave_topk(key, okm, static_cast<uint32_t>(K), ckey, cpos,
+                [&](uint32_t pos, int p) { out[1 + pos] = p + 1; });
   } else {
     const int kw = min(K, max(0, min(S, n - base)));  // kept by this wave
     if (kw > 0) {
@@ -398,6 +457,128 @@ hipError_t launch_select_blocks(const float* scores, const int32_t* q_pos, int b
   else
     hipLaunchKernelGGL((select_blocks_kernel<1024, 16, false>), grid, dim3(1024), 0, s, scores,
                        q_pos, nq, n_rows, B, m, block_idx);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- steps 2 and 3 fused
+// For many queries over at most 64*16 + 2 blocks. A workgroup scores 16
+// consecutive queries of one sequence against every causal candidate block
+// into LDS, with the same exact three-term products (and summation order) as
+// block_score_kernel, then each of its 8 waves selects the top blocks of two
+// of the queries from LDS as select_blocks_wave_kernel does, so the score matrix
+// never reaches HBM and the result equals the two kernels' bit for bit.
+// Workgroups are dealt to the 8 XCDs in contiguous runs of (sequence, query
+// tile), so an XCD's L2 serves few sequences' summary tables.
+constexpr int kRouteQT = 16;
+
+constexpr int kRouteWaves = 8;
+
+template <int D, int IT>
+__global__ __launch_bounds__(64 * kRouteWaves) void route_blocks_kernel(
+    const uint16_t* __restrict__ qidx, int64_t qsb, int64_t qst, const int32_t* __restrict__ q_pos,
+    int nq, const uint16_t* __restrict__ split, int n_rows, int B, float invB, int m,
+    int32_t* __restrict__ block_idx, int batch, int ntq, unsigned grid_wg) {
+  constexpr int KS = D / 32;
+  constexpr int NC = 64 * IT;  // candidate positions (position p is block p + 1)
+  constexpr int LS = NC + 4;   // LDS floats per query row
+  __shared__ __align__(16) float sc[kRouteQT][LS];
+  __shared__ uint32_t lkey[kRouteWaves][kSelSmall];
+  __shared__ int lpos[kRouteWaves][kSelSmall];
+  const unsigned per = grid_wg / 8;
+  const unsigned id = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (id >= static_cast<unsigned>(batch) * ntq) return;
+  const int b = static_cast<int>(id / ntq), q0 = static_cast<int>(id % ntq) * kRouteQT;
+  const int w = threadIdx.x >> 6, l = lane_id(), g = l / 16, r16 = l % 16;
+  const int qq = q0 + r16;
+  const int qc = min(qq, nq - 1);
+  const int bt = qq < nq ? min(max(q_pos[static_cast<int64_t>(b) * nq + qc], 0), n_rows * B - 1) / B
+                         : 0;
+  const int btmax = static_cast<int>(wave_max(static_cast<float>(bt)));
+  const uint16_t* qrow = qidx + b * qsb + static_cast<int64_t>(qc) * qst + 8 * g;
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int x = 0; x < KS; ++x) qf[x] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 32 * x));
+  // row tile tau: blocks 1 + 16 tau .. 16 + 16 tau (positions 16 tau ..);
+  // wave w takes tiles w, w + NW, ..., two per step with all their loads in
+  // flight before the first product
+  constexpr int NW = kRouteWaves;
+  const int ntile = btmax > 1 ? (btmax - 1 + 15) / 16 : 0;
+  for (int tau = w; tau < ntile; tau += 2 * NW) {
+    uint4 sf[2][3 * KS];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int cc = min(1 + 16 * (tau + u * NW) + r16, n_rows - 1);
+      const uint16_t* srow = split + (static_cast<int64_t>(b) * n_rows + cc) * 3 * D + 8 * g;
+#pragma unroll
+      for (int x = 0; x < 3 * KS; ++x)
+        sf[u][x] = *reinterpret_cast<const uint4*>(srow + (x / KS) * D + 32 * (x % KS));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int tu = tau + u * NW;
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int x = 0; x < 3 * KS; ++x) acc = mfma16(as_bf16x8(sf[u][x]), qf[x % KS], acc);
+      // lane: blocks 1 + 16 tu + 4g + (0..3) of query column r16
+      if (tu < ntile)
+        *reinterpret_cast<float4*>(&sc[r16][16 * tu + 4 * g]) =
+            make_float4(acc[0] * invB, acc[1] * invB, acc[2] * invB, acc[3] * invB);
+    }
+  }
+  __syncthreads();
+  for (int j = w; j < kRouteQT; j += NW) {
+    const int q = q0 + j;
+    if (q >= nq) break;
+    const int64_t qi = static_cast<int64_t>(b) * nq + q;
+    int32_t* out = block_idx + qi * m;
+    const int bq = min(max(q_pos[qi], 0), n_rows * B - 1) / B;
+    const int n = max(bq - 1, 0);
+    const int K = m - (bq == 0 ? 1 : 2);  // free slots
+    if (n <= K) {
+      for (int i = l; i < m; i += 64) out[i] = i <= bq ? i : -1;
+      continue;
+    }
+    uint32_t key[IT];
+    uint32_t okm = 0;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int p = 64 * i + l;
+      key[i] = p < n ? order_key(sc[j][p]) : 0u;
+      okm |= p < n ? (1u << i) : 0u;
+    }
+    wave_topk(key, okm, static_cast<uint32_t>(K), lkey[w], lpos[w],
+              [&](uint32_t pos, int p) { out[1 + pos] = p + 1; });
+    if (l == 0) {
+      out[0] = 0;
+      out[1 + K] = bq;
+    }
+  }
+}
+
+hipError_t launch_route_blocks(const uint16_t* qidx, Str3 qs, const int32_t* q_pos, int batch,
+                               int nq, const uint16_t* split, int n_rows, int d, int B, int m,
+                               int32_t* block_idx, hipStream_t s) {
+  const int ntq = (nq + kRouteQT - 1) / kRouteQT;
+  const unsigned grid_wg =
+      static_cast<unsigned>((static_cast<int64_t>(batch) * ntq + 7) / 8 * 8);
+  const float invB = 1.0f / static_cast<float>(B);
+#define HISA_RB(D_, IT_)                                                                        \
+  hipLaunchKernelGGL((route_blocks_kernel<D_, IT_>), dim3(grid_wg), dim3(64 * kRouteWaves), 0, s, \
+                     qidx, qs.b,                                                                \
+                     qs.t, q_pos, nq, split, n_rows, B, invB, m, block_idx, batch, ntq, grid_wg)
+#define HISA_RB_D(IT_)              \
+  do {                              \
+    if (d == 64) HISA_RB(64, IT_);  \
+    else HISA_RB(128, IT_);         \
+  } while (0)
+  if (n_rows <= 64 + 2) HISA_RB_D(1);
+  else if (n_rows <= 128 + 2) HISA_RB_D(2);
+  else if (n_rows <= 256 + 2) HISA_RB_D(4);
+  else if (n_rows <= 512 + 2) HISA_RB_D(8);
+  else HISA_RB_D(16);
+#undef HISA_RB_D
+#undef HISA_RB
   return hipGetLastError();
 }
 

@@ -16,8 +16,8 @@ import torch
 
 from . import (flat_indexer_topk, flat_indexer_topk_workspace_bytes, hils_two_level_attn_fwd,
                hils_prefill_workspace, hils_two_level_prefill_fwd, hils_workspace,
-               hisa_auto_plan, hisa_block_score, hisa_block_summary, hisa_block_summary_update,
-               hisa_select_blocks,
+               ROUTE_MAX_ROWS, hisa_auto_plan, hisa_block_score, hisa_block_summary,
+               hisa_block_summary_update, hisa_route_blocks, hisa_select_blocks,
                hisa_token_select, hisa_token_select_workspace_bytes, sparse_attn_fwd,
                sparse_attn_workspace)
 
@@ -250,7 +250,10 @@ class HilsPrefill:
         self.split = torch.empty(b * H, n, 3, D, dtype=torch.bfloat16, device=dev)
         # routed sequence b*H + h reads the positions of sequence b
         self.q_pos_h = q_pos.repeat_interleave(H, dim=0).contiguous()
-        self.scores = torch.empty(b * H, nq, n, dtype=torch.float32, device=dev)
+        # chunk scores stay on chip when the chunk count allows
+        self.fused_route = n <= ROUTE_MAX_ROWS
+        self.scores = None if self.fused_route else torch.empty(b * H, nq, n, dtype=torch.float32,
+                                                                device=dev)
         self.chunk_idx = torch.empty(b * H, nq, m, dtype=torch.int32, device=dev)
         self.out = torch.empty(b, nq, H, D, dtype=torch.bfloat16, device=dev)
         # bucketed attention (None: one workgroup per query and head)
@@ -268,8 +271,13 @@ class HilsPrefill:
         b, nq, H, D = self.q.shape
         for bi in range(b):
             rows = slice(bi * H, (bi + 1) * H)
-            hisa_block_score(self.q[bi].permute(1, 0, 2), self.q_pos_h[rows], self.split[rows],
-                             self.C, out=self.scores[rows])
+            qv = self.q[bi].permute(1, 0, 2)
+            if self.fused_route:
+                hisa_route_blocks(qv, self.q_pos_h[rows], self.split[rows], self.C, self.m,
+                                  out=self.chunk_idx[rows])
+                continue
+            hisa_block_score(qv, self.q_pos_h[rows], self.split[rows], self.C,
+                             out=self.scores[rows])
             hisa_select_blocks(self.scores[rows], self.q_pos_h[rows], self.C, self.m,
                                out=self.chunk_idx[rows])
 

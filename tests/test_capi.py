@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_match_header():
     names = _declared()
-    assert len(names) == 17
+    assert len(names) == 18
     lib = ctypes.CDLL(H.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -137,6 +137,24 @@ def test_hils_validation():
     assert L.hils_two_level_attn_fwd(*a) == 5 and "needs" in _err()
 
 
+def test_route_validation():
+    L = H.lib()
+    s = S(0, 64, 0)
+    args = [FAKE, s, FAKE, 1, 4096, FAKE, 64, 64, 64, 32, FAKE, NULL]
+    a = list(args)
+    a[6] = 1027                                                      # too many blocks for LDS
+    assert L.hisa_route_blocks(*a) == 3 and "hisa_block_score" in _err()
+    a = list(args)
+    a[9] = 1                                                         # m < 2
+    assert L.hisa_route_blocks(*a) == 3
+    a = list(args)
+    a[8] = 96                                                        # B unsupported
+    assert L.hisa_route_blocks(*a) == 3
+    a = list(args)
+    a[10] = NULL                                                     # no output
+    assert L.hisa_route_blocks(*a) == 1
+
+
 def test_hils_prefill_validation():
     L = H.lib()
     s = S(0, 1024, 64)
@@ -169,7 +187,7 @@ def test_hils_prefill_validation():
     assert L.hils_two_level_prefill_fwd(*a) == 2
     # the bucketed path's scratch: per-entry partials dominate
     need = L.hils_two_level_prefill_fwd_workspace_bytes(1, 4096, 4096, 16, 64, 64, 32)
-    assert need >= 16 * 4096 * 32 * 64 * 4 and need % 256 == 0
+    assert need >= 16 * 4096 * 32 * 64 * 2 and need % 256 == 0
     assert L.hils_two_level_prefill_fwd_workspace_bytes(1, 4096, 4096, 16, 96, 64, 32) == 0
     a = list(args)
     a[22], a[23] = FAKE, need - 1                                    # too small

@@ -583,3 +583,40 @@ def test_workload_hils_prefill_64k_sampled():
     log(f"case hils prefill 64K N(0,1), sampled {w}")
     assert _hils_prefill_check(w, exact=False, positions=sample_positions(w, 24),
                                heads=[0, 5, 10, 15]) <= 4
+
+
+# ---------------------------------------------------------------- fused routing
+# (batch, nq, L, B, d, m, positions, value range): one case per item count of
+# the selection (n_rows up to 66, 130, 258, 514, 1026), queries not a multiple
+# of the 16-query tile, queries in the first block, m above the candidate
+# count, and small integer values so that many scores tie
+ROUTE_CASES = [
+    (2, 100, 3000, 64, 64, 8, "random", 8),
+    (1, 333, 9000, 64, 128, 16, "random", 2),
+    (3, 50, 20000, 64, 64, 32, "random", 1),
+    (1, 200, 32768, 64, 64, 40, "last", 8),
+    (1, 1000, 65536, 64, 64, 32, "prefill", 1),
+    (1, 77, 65600, 64, 64, 64, "random", 8),
+    (2, 40, 4096, 256, 64, 4, "random", 1),
+]
+
+
+@pytest.mark.parametrize("case", ROUTE_CASES, ids=[f"n{c[2] // c[3]}_q{c[1]}" for c in ROUTE_CASES])
+def test_route_blocks_equals_score_then_select(case):
+    b, nq, L, B, d, m, kind, vr = case
+    log(f"case fused route {case}")
+    g = torch.Generator(device=DEV).manual_seed(7)
+    kidx = torch.randint(-vr, vr + 1, (b, L, d), generator=g, device=DEV).to(torch.bfloat16)
+    qidx = torch.randint(-vr, vr + 1, (b, nq, d), generator=g, device=DEV).to(torch.bfloat16)
+    if kind == "random":
+        q_pos = torch.randint(0, L, (b, nq), generator=g, device=DEV, dtype=torch.int32)
+    elif kind == "last":
+        q_pos = torch.full((b, nq), L - 1, dtype=torch.int32, device=DEV)
+    else:
+        q_pos = torch.arange(L - nq, L, dtype=torch.int32, device=DEV).expand(b, nq).contiguous()
+    q_pos[:, :3] = torch.tensor([0, B - 1, B], dtype=torch.int32, device=DEV)
+    _, split = H.hisa_block_summary(kidx, B)
+    ref = H.hisa_select_blocks(H.hisa_block_score(qidx, q_pos, split, B), q_pos, B, m)
+    got = H.hisa_route_blocks(qidx, q_pos, split, B, m)
+    torch.cuda.synchronize()
+    check_index_rows(got.view(-1, m).cpu().numpy(), ref.view(-1, m).cpu().numpy(), "fused route")
