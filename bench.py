@@ -435,6 +435,30 @@ def hils_prefill_flop(w):
     return float(per_head * w.Hq * w.batch)
 
 
+def hils_prefill_bytes(w):
+    """Algorithmic HBM bytes of one bucketed two-level attention call (the
+    entries are the (query, head, chosen chunk) triples, min(t//C + 1, m) per
+    query and head):
+      bucketing   chunk ids read twice, entry ids written: 12 B per id slot;
+      local keys  K read once (2D B per token and head), the fp32 key table
+                  written (4D B);
+      tiles       per entry the query row (2D B) read and the fp16 partial
+                  row (2D B), its exponent and logit (5 B) written; each
+                  chunk's K and V rows (4CD B) read once per head;
+      combine     per entry the partial row, exponent, logit and chunk id
+                  (2D + 9 B) read; per query and head the output row (2D B)
+                  written."""
+    import numpy as np
+    t = np.arange(w.L - w.queries, w.L, dtype=np.int64)
+    entries = float(np.minimum(t // w.B + 1, w.m).sum()) * w.Hq * w.batch
+    slots = float(w.queries * w.m * w.Hq * w.batch)
+    D, C = w.Dk, w.B
+    heads = w.Hq * w.batch
+    n_chunks = -(-w.L // C)
+    return (12 * slots + 6 * D * w.L * heads + entries * (4 * D + 5) + 4 * C * D * n_chunks * heads
+            + entries * (2 * D + 9) + 2 * D * w.queries * heads)
+
+
 def bench_hils_prefill(w, a, inp):
     from long_context_indexer_block_amd.pipeline import HilsPrefill
 
@@ -443,12 +467,13 @@ def bench_hils_prefill(w, a, inp):
     wall, stage = timed([hp.build_keys, hp.route, hp.attend], a.steps, a.warmup)
     res = base_record(w, a, w.batch * w.queries, wall)
     res["stage_ms"] = {"chunk_keys": stage[0], "route": stage[1], "two_level_attention": stage[2]}
-    flop = hils_prefill_flop(w)
-    ach = flop / (stage[2] * 1e-3) / 1e12
-    res["roofline"] = {"kernel": "hils_prefill_kernel", "bound": "alu", "achieved": ach,
-                       "peak": PEAK_FP32_VEC_TFLOPS, "unit": "TFLOP/s",
-                       "frac": ach / PEAK_FP32_VEC_TFLOPS, "traffic": None,
-                       "alg_flop_per_launch": flop}
+    nbytes = hils_prefill_bytes(w)
+    ach = nbytes / (stage[2] * 1e-3) / 1e9
+    res["roofline"] = {"kernel": "two-level attention call (bucketing, local keys, tiles, "
+                                 "combine)", "bound": "hbm", "achieved": ach,
+                       "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+                       "traffic": None, "alg_bytes_per_launch": nbytes,
+                       "vector_flop_per_launch": hils_prefill_flop(w)}
     return res
 
 

@@ -158,12 +158,17 @@ def hisa_select_blocks(block_scores, q_pos, B, m, out=None):
     return out
 
 
-ROUTE_MAX_ROWS = 64 * 16 + 2
+ROUTE_MAX_ROWS = 64 * 16 + 2      # scores kept on chip up to this many blocks
+ROUTE_STREAM_MAX_M = 130          # beyond it, streamed selection for m up to this
+
+
+def route_supported(n_rows, m):
+    return n_rows <= ROUTE_MAX_ROWS or m <= ROUTE_STREAM_MAX_M
 
 
 def hisa_route_blocks(qidx, q_pos, split, B, m, out=None):
     """Steps 2 and 3 fused: qidx [b, nq, d] bf16, q_pos [b, nq] int32, split
-    [b, n, 3, d] (n <= ROUTE_MAX_ROWS) -> block_idx [b, nq, m] int32."""
+    [b, n, 3, d] (route_supported(n, m)) -> block_idx [b, nq, m] int32."""
     _need(qidx, torch.bfloat16, "qidx")
     b, nq, d = qidx.shape
     n = split.shape[1]

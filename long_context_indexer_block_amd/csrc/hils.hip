@@ -266,7 +266,8 @@ __global__ __launch_bounds__(64 * W) void hils_prefill_kernel(
 // query gathering its chosen chunks, the (query, slot) entries of chunk_idx
 // are bucketed by (sequence*head, chunk) and each chunk's K and V rows are
 // read once per tile of 64 entries:
-//   1. local keys: kloc[bh][j] = proj @ (mean of tokens j/C*C .. j), every j;
+//   1. local keys: kloc[bh][j] = proj @ (mean of tokens j/C*C .. j), every j
+//      of the chunks that hold a query of the call;
 //   2. per tile, on matrix cores: the chunk's token softmax for the tile's
 //      queries (causal within the local chunk) times V, normalised, into
 //      partial[e][:] (scaled fp16), and the chunk logit (scale_chunk * q . key) into
@@ -277,6 +278,7 @@ __global__ __launch_bounds__(64 * W) void hils_prefill_kernel(
 // ---------------------------------------------------------------------------
 struct PrefillWs {
   PairBuckets pb;
+  uint32_t* need;   // [batch][n_rows]: a query of the call lies in the chunk
   float* kloc;      // [batch*H][L][D]
   float* logit;        // [batch*H*nq*m]
   int8_t* pexp;        // [batch*H*nq*m] scale exponent of each partial row
@@ -292,6 +294,7 @@ static PrefillWs carve_prefill(void* ws, int batch, int nq, int L, int H, int D,
   w.pb = carve_pair_buckets(ws, bh, nq, m, nblk, &off);
   char* p = static_cast<char*>(ws);
   auto take = [&](size_t n) { char* r = p ? p + off : nullptr; off += align256(n); return r; };
+  w.need = reinterpret_cast<uint32_t*>(take(static_cast<size_t>(batch) * nblk * 4));
   w.kloc = reinterpret_cast<float*>(take(static_cast<size_t>(bh) * L * D * 4));
   w.logit = reinterpret_cast<float*>(take(npairs * 4));
   w.pexp = reinterpret_cast<int8_t*>(take(npairs));
@@ -306,14 +309,30 @@ size_t hils_prefill_workspace(int batch, int nq, int L, int H, int D, int C, int
   return bytes;
 }
 
-// Workgroup (chunk c, pair bh): 64-token groups of the chunk. Thread (rg, d)
+// The chunks that hold a query of the call: only their local keys are read.
+__global__ void hils_need_clear_kernel(uint32_t* __restrict__ need, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) need[i] = 0u;
+}
+__global__ void hils_need_mark_kernel(const int32_t* __restrict__ q_pos, int batch, int nq, int L,
+                                      int C, int n_rows, uint32_t* __restrict__ need) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<int64_t>(batch) * nq) return;
+  const int b = static_cast<int>(i / nq);
+  const int t = min(max(q_pos[i], 0), L - 1);
+  need[static_cast<int64_t>(b) * n_rows + t / C] = 1u;
+}
+
+// Workgroup (chunk c, pair bh): 64-token groups of the chunk; chunks that
+// hold no query of the call (need[b][c] == 0) are skipped. Thread (rg, d)
 // sums column d over its rows of the group (a prefix within them), the row
 // groups are joined with the running carry, then thread (jg, e) projects the
 // prefixes of rows jg, jg + RG, ... onto output column e.
 template <int D>
 __global__ __launch_bounds__(256) void hils_local_keys_kernel(
     const uint16_t* __restrict__ k, Str3 ks, int H, int L, int C,
-    const uint16_t* __restrict__ proj, float* __restrict__ kloc) {
+    const uint16_t* __restrict__ proj, const uint32_t* __restrict__ need,
+    float* __restrict__ kloc) {
   constexpr int RG = 256 / D;      // row groups of the scan
   constexpr int RPG = 64 / RG;     // rows per group
   __shared__ float pre[64][D];
@@ -321,6 +340,7 @@ __global__ __launch_bounds__(256) void hils_local_keys_kernel(
   __shared__ float carry[D];
   const int c = blockIdx.x, bh = blockIdx.y;
   const int b = bh / H, h = bh % H;
+  if (need[static_cast<int64_t>(b) * gridDim.x + c] == 0u) return;
   const int tid = threadIdx.x, d = tid % D, rg = tid / D;
   const uint16_t* kb = k + b * ks.b + h * ks.h;
   float* out = kloc + static_cast<int64_t>(bh) * L * D;
@@ -719,12 +739,18 @@ hipError_t launch_hils_prefill(const uint16_t* q, Str3 qs, const uint16_t* k, St
   PrefillWs w = carve_prefill(ws, batch, nq, L, H, D, C, m, nullptr);
   hipError_t err = launch_pair_buckets(chunk_idx, bh, nq, m, n_rows, w.pb, s);
   if (err != hipSuccess) return err;
+  const int nneed = batch * n_rows;
+  hipLaunchKernelGGL(hils_need_clear_kernel, dim3((nneed + 255) / 256), dim3(256), 0, s, w.need,
+                     nneed);
+  const int64_t nqb = static_cast<int64_t>(batch) * nq;
+  hipLaunchKernelGGL(hils_need_mark_kernel, dim3(static_cast<unsigned>((nqb + 255) / 256)),
+                     dim3(256), 0, s, q_pos, batch, nq, L, C, n_rows, w.need);
   if (D == 64)
     hipLaunchKernelGGL((hils_local_keys_kernel<64>), dim3(n_rows, bh), dim3(256), 0, s, k, ks, H,
-                       L, C, proj, w.kloc);
+                       L, C, proj, w.need, w.kloc);
   else
     hipLaunchKernelGGL((hils_local_keys_kernel<128>), dim3(n_rows, bh), dim3(256), 0, s, k, ks, H,
-                       L, C, proj, w.kloc);
+                       L, C, proj, w.need, w.kloc);
   const size_t npairs = static_cast<size_t>(bh) * nq * m;
   const size_t max_tiles = (npairs + kPairTile - 1) / kPairTile + static_cast<size_t>(bh) * n_rows;
   const int tpw = 2;  // tiles per workgroup

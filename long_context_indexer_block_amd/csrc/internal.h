@@ -56,8 +56,10 @@ hipError_t launch_mla_attn(const uint16_t* q, Str3 qs, const uint16_t* kv, Str3 
                            int nq, int L, int Hkv, const int32_t* token_idx, int topk, float scale,
                            uint16_t* out, Str3 os, float* lse, hipStream_t s);
 
-// indexer.hip: steps 2 and 3 fused (n_rows <= kRouteMaxRows)
+// indexer.hip: steps 2 and 3 fused (scores on chip when n_rows <= kRouteMaxRows,
+// else streamed through per-query candidate buffers, which needs m - 2 <= 128)
 constexpr int kRouteMaxRows = 64 * 16 + 2;
+constexpr int kRouteStreamMaxM = 130;
 hipError_t launch_route_blocks(const uint16_t* qidx, Str3 qs, const int32_t* q_pos, int batch,
                                int nq, const uint16_t* split, int n_rows, int d, int B, int m,
                                int32_t* block_idx, hipStream_t s);

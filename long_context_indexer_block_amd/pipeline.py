@@ -16,7 +16,7 @@ import torch
 
 from . import (flat_indexer_topk, flat_indexer_topk_workspace_bytes, hils_two_level_attn_fwd,
                hils_prefill_workspace, hils_two_level_prefill_fwd, hils_workspace,
-               ROUTE_MAX_ROWS, hisa_auto_plan, hisa_block_score, hisa_block_summary,
+               hisa_auto_plan, route_supported, hisa_block_score, hisa_block_summary,
                hisa_block_summary_update, hisa_route_blocks, hisa_select_blocks,
                hisa_token_select, hisa_token_select_workspace_bytes, sparse_attn_fwd,
                sparse_attn_workspace)
@@ -236,9 +236,11 @@ class HilsPrefill:
     up to it would.
 
     q [b, nq, H, D], k/v [b, L, H, D] bf16, w_proj [D, D] bf16 (or None for
-    plain-mean chunk keys), q_pos [b, nq] int32."""
+    plain-mean chunk keys), q_pos [b, nq] int32. Queries run in slabs of at
+    most `slab` positions, which bounds the attention's scratch memory (its
+    per-entry partial results)."""
 
-    def __init__(self, q, k, v, w_proj, q_pos, C, m, scale_chunk, scale_token):
+    def __init__(self, q, k, v, w_proj, q_pos, C, m, scale_chunk, scale_token, slab=65536):
         self.q, self.k, self.v, self.w_proj, self.q_pos = q, k, v, w_proj, q_pos
         self.C, self.m, self.scale_chunk, self.scale_token = C, m, scale_chunk, scale_token
         b, nq, H, D = q.shape
@@ -248,16 +250,22 @@ class HilsPrefill:
         self.n = n
         self.khat = torch.empty(b * H, n, D, dtype=torch.float32, device=dev)
         self.split = torch.empty(b * H, n, 3, D, dtype=torch.bfloat16, device=dev)
+        self.slabs = [(s0, min(nq, s0 + slab)) for s0 in range(0, nq, slab)]
+        S = self.slabs[0][1] - self.slabs[0][0]
+        self.slab_pos = [q_pos[:, s0:s1].contiguous() for s0, s1 in self.slabs]
         # routed sequence b*H + h reads the positions of sequence b
-        self.q_pos_h = q_pos.repeat_interleave(H, dim=0).contiguous()
-        # chunk scores stay on chip when the chunk count allows
-        self.fused_route = n <= ROUTE_MAX_ROWS
-        self.scores = None if self.fused_route else torch.empty(b * H, nq, n, dtype=torch.float32,
-                                                                device=dev)
-        self.chunk_idx = torch.empty(b * H, nq, m, dtype=torch.int32, device=dev)
+        self.slab_pos_h = [p.repeat_interleave(H, dim=0).contiguous() for p in self.slab_pos]
+        self.slab_idx = [torch.empty(b * H, s1 - s0, m, dtype=torch.int32, device=dev)
+                         for s0, s1 in self.slabs]
+        # routing never writes chunk scores to memory (m <= 64 is always supported)
+        assert route_supported(n, m)
         self.out = torch.empty(b, nq, H, D, dtype=torch.bfloat16, device=dev)
         # bucketed attention (None: one workgroup per query and head)
-        self.ws = hils_prefill_workspace(b, nq, L, H, D, C, m, dev)
+        self.ws = hils_prefill_workspace(b, S, L, H, D, C, m, dev)
+
+    def chunk_ids(self):
+        """The chosen chunks of every query, [b*H, nq, m]."""
+        return self.slab_idx[0] if len(self.slabs) == 1 else torch.cat(self.slab_idx, dim=1)
 
     def build_keys(self):
         b, L, H, D = self.k.shape
@@ -269,22 +277,18 @@ class HilsPrefill:
     def route(self):
         # q[bi] viewed as [H, nq, D] (no copy): head h is routed sequence bi*H + h
         b, nq, H, D = self.q.shape
-        for bi in range(b):
-            rows = slice(bi * H, (bi + 1) * H)
-            qv = self.q[bi].permute(1, 0, 2)
-            if self.fused_route:
-                hisa_route_blocks(qv, self.q_pos_h[rows], self.split[rows], self.C, self.m,
-                                  out=self.chunk_idx[rows])
-                continue
-            hisa_block_score(qv, self.q_pos_h[rows], self.split[rows], self.C,
-                             out=self.scores[rows])
-            hisa_select_blocks(self.scores[rows], self.q_pos_h[rows], self.C, self.m,
-                               out=self.chunk_idx[rows])
+        for (s0, s1), pos_h, idx in zip(self.slabs, self.slab_pos_h, self.slab_idx):
+            for bi in range(b):
+                rows = slice(bi * H, (bi + 1) * H)
+                hisa_route_blocks(self.q[bi, s0:s1].permute(1, 0, 2), pos_h[rows],
+                                  self.split[rows], self.C, self.m, out=idx[rows])
 
     def attend(self):
-        hils_two_level_prefill_fwd(self.q, self.k, self.v, self.khat, self.chunk_idx, self.q_pos,
-                                   self.C, self.scale_chunk, self.scale_token, proj=self.w_proj,
-                                   out=self.out, workspace=self.ws)
+        for (s0, s1), pos, idx in zip(self.slabs, self.slab_pos, self.slab_idx):
+            hils_two_level_prefill_fwd(self.q[:, s0:s1], self.k, self.v, self.khat, idx, pos,
+                                       self.C, self.scale_chunk, self.scale_token,
+                                       proj=self.w_proj, out=self.out[:, s0:s1],
+                                       workspace=self.ws)
 
     def run(self, build=True):
         if build:

@@ -142,7 +142,7 @@ def test_route_validation():
     s = S(0, 64, 0)
     args = [FAKE, s, FAKE, 1, 4096, FAKE, 64, 64, 64, 32, FAKE, NULL]
     a = list(args)
-    a[6] = 1027                                                      # too many blocks for LDS
+    a[6], a[9] = 1027, 131                       # too many blocks for LDS, m too large to stream
     assert L.hisa_route_blocks(*a) == 3 and "hisa_block_score" in _err()
     a = list(args)
     a[9] = 1                                                         # m < 2

@@ -452,15 +452,23 @@ def test_workload_hils_decode_1m():
 
 
 # ---------------------------------------------------------------- two-level prefill
-def _hils_prefill_check(w, exact, positions=None, heads=None, bucketed=True):
+def _hils_prefill_check(w, exact, positions=None, heads=None, bucketed=True, subset=False,
+                        slab=65536):
     """Run the causal two-level prefill of workload w on the GPU and check the
     queries at `positions` (default: all) of `heads` (default: all) against
     the oracle's decode of the tokens up to each query. bucketed=False runs
-    the per-query kernel (no workspace)."""
+    the per-query kernel (no workspace); subset=True runs the GPU on the
+    queries at `positions` only (the full cache, a sample of its queries)."""
     inp = make_inputs(w, DEV, seed=0)
     C, m, nq = w.B, w.m, w.queries
     sc = 1.0 / math.sqrt(w.Dk)
-    hp = HilsPrefill(inp["q"], inp["k"], inp["v"], inp["w_proj"], inp["q_pos"], C, m, sc, sc)
+    first = w.L - nq
+    rows = list(range(nq)) if positions is None else [t - first for t in positions]
+    ridx = torch.tensor(rows, dtype=torch.long, device=DEV)
+    q_in, pos_in = inp["q"], inp["q_pos"]
+    if subset:
+        q_in, pos_in = q_in[:, ridx].contiguous(), pos_in[:, ridx].contiguous()
+    hp = HilsPrefill(q_in, inp["k"], inp["v"], inp["w_proj"], pos_in, C, m, sc, sc, slab=slab)
     assert hp.ws is not None
     if not bucketed:
         hp.ws = None
@@ -468,11 +476,9 @@ def _hils_prefill_check(w, exact, positions=None, heads=None, bucketed=True):
     torch.cuda.synchronize()
     Wp = f64(inp["w_proj"])
     qpos = inp["q_pos"].cpu().numpy()
-    first = w.L - nq
-    rows = list(range(nq)) if positions is None else [t - first for t in positions]
-    ridx = torch.tensor(rows, dtype=torch.long, device=DEV)
-    got_idx = hp.chunk_idx.view(w.batch, w.Hq, nq, m)[:, :, ridx].cpu().numpy()
-    outs = hp.out[:, ridx].float().cpu().numpy()      # [b, rows, H, D]
+    gidx = ridx if not subset else torch.arange(len(rows), device=DEV)
+    got_idx = hp.chunk_ids().view(w.batch, w.Hq, q_in.shape[1], m)[:, :, gidx].cpu().numpy()
+    outs = hp.out[:, gidx].float().cpu().numpy()      # [b, rows, H, D]
     qs = inp["q"][:, ridx].cpu()
     excluded = 0
     for b in range(w.batch):
@@ -531,6 +537,22 @@ def test_hils_prefill_small(w, bucketed):
     assert _hils_prefill_check(w, exact=True, bucketed=bucketed) == 0
 
 
+def test_hils_prefill_slabs():
+    # queries in ragged slabs of 256 (700 = 256 + 256 + 188)
+    w = HILS_PREFILL_SMALL[0]
+    log(f"case hils prefill in slabs {w}")
+    assert _hils_prefill_check(w, exact=True, slab=256) == 0
+
+
+def test_hils_prefill_streamed_routing():
+    # more chunks than the fused routing keeps on chip (1094 > 1026): the
+    # streamed selection; a sample of the queries runs
+    w = WORKLOADS["hils_prefill_64k"].with_(name="hilsp_1094", L=70000, Hq=2, Hkv=2,
+                                            int_mode=True)
+    log(f"case hils prefill, streamed routing {w}")
+    assert _hils_prefill_check(w, exact=True, positions=sample_positions(w, 40), subset=True) == 0
+
+
 def test_hils_prefill_no_projection():
     # plain-mean chunk keys (proj None) on both paths
     w = HILS_PREFILL_SMALL[0]
@@ -566,7 +588,7 @@ def test_hils_prefill_matches_decode_at_last_position():
     hd.ws = None
     hd.run(build=True)
     torch.cuda.synchronize()
-    assert torch.equal(hp.chunk_idx[:, -1], hd.chunk_idx.view(-1, w.m))
+    assert torch.equal(hp.chunk_ids()[:, -1], hd.chunk_idx.view(-1, w.m))
     check_attention(hp.out[:, -1].float().cpu().numpy(), hd.out.float().cpu().numpy(),
                     "prefill last query vs decode")
 
@@ -576,6 +598,14 @@ def test_workload_hils_prefill_64k_int_twin_sampled():
     log(f"case hils prefill 64K int twin, sampled {w}")
     assert _hils_prefill_check(w, exact=True, positions=sample_positions(w, 24),
                                heads=[0, 7, 15]) == 0
+
+
+def test_workload_hils_prefill_512k_sampled():
+    # the 512K cache (8192 chunks) with a sample of its queries
+    w = WORKLOADS["hils_prefill_512k"]
+    log(f"case hils prefill 512K N(0,1), sampled {w}")
+    assert _hils_prefill_check(w, exact=False, positions=sample_positions(w, 24),
+                               heads=[0, 9, 15], subset=True) <= 3
 
 
 def test_workload_hils_prefill_64k_sampled():
@@ -598,6 +628,13 @@ ROUTE_CASES = [
     (1, 1000, 65536, 64, 64, 32, "prefill", 1),
     (1, 77, 65600, 64, 64, 64, "random", 8),
     (2, 40, 4096, 256, 64, 4, "random", 1),
+    # streamed selection (more than 1026 blocks): ragged tiles, first-block
+    # queries, heavy ties through the buffer cuts, K at its limit of 128
+    (1, 300, 70000, 64, 64, 32, "random", 1),
+    (2, 100, 262144, 64, 128, 64, "random", 8),
+    (1, 64, 524288, 64, 64, 130, "random", 1),
+    (1, 50, 300000, 128, 64, 8, "last", 8),
+    (1, 2000, 140000, 64, 64, 16, "prefill", 8),
 ]
 
 

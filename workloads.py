@@ -81,6 +81,8 @@ WORKLOADS = {
                                16, 16, 64, 64),
     "hils_prefill_64k": Workload("hils_prefill_64k", "hils_prefill", 1, 65536, 64, 32, 0, 64,
                                  16, 16, 64, 64),
+    "hils_prefill_512k": Workload("hils_prefill_512k", "hils_prefill", 1, 524288, 64, 32, 0, 64,
+                                  16, 16, 64, 64),
 }
 HEADLINE = "prefill_64k_mla"
 
