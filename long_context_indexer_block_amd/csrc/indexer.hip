@@ -570,43 +570,60 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_blocks_kernel(
 constexpr int kStreamCap = 256;  // buffer entries per query
 constexpr int kStreamK = kStreamCap - 64 - 64;
 
-template <int D>
-__global__ __launch_bounds__(256) void route_blocks_stream_kernel(
+template <int D, int NW, int QS>
+__global__ __launch_bounds__(64 * NW) void route_blocks_stream_kernel(
     const uint16_t* __restrict__ qidx, int64_t qsb, int64_t qst, const int32_t* __restrict__ q_pos,
     int nq, const uint16_t* __restrict__ split, int n_rows, int B, float invB, int m,
     int32_t* __restrict__ block_idx, int batch, int ntq, unsigned grid_wg) {
   constexpr int KS = D / 32;
-  __shared__ __align__(16) float stg[2][kRouteQT][64];
-  __shared__ uint32_t bkey[kRouteQT][kStreamCap];
-  __shared__ int bpos[kRouteQT][kStreamCap];
+  constexpr int NQB = QS / 16;          // 16-query column blocks of the products
+  constexpr int SB = 16 * NW;           // candidate blocks per step
+  constexpr int QW = QS / NW;           // queries filtered per wave
+  __shared__ __align__(16) float stg[2][QS][SB];
+  __shared__ uint32_t bkey[QS][kStreamCap];
+  __shared__ int bpos[QS][kStreamCap];
   const unsigned per = grid_wg / 8;
   const unsigned id = (blockIdx.x % 8) * per + blockIdx.x / 8;
   if (id >= static_cast<unsigned>(batch) * ntq) return;
-  const int b = static_cast<int>(id / ntq), q0 = static_cast<int>(id % ntq) * kRouteQT;
+  const int b = static_cast<int>(id / ntq), q0 = static_cast<int>(id % ntq) * QS;
   const int w = threadIdx.x >> 6, l = lane_id(), g = l / 16, r16 = l % 16;
-  const int qq = q0 + r16;
-  const int qc = min(qq, nq - 1);
-  const int bt = qq < nq ? min(max(q_pos[static_cast<int64_t>(b) * nq + qc], 0), n_rows * B - 1) / B
-                         : 0;
-  const int btmax = static_cast<int>(wave_max(static_cast<float>(bt)));
-  const uint16_t* qrow = qidx + b * qsb + static_cast<int64_t>(qc) * qst + 8 * g;
-  bf16x8 qf[KS];
+  bf16x8 qf[NQB][KS];
+  int bt[NQB];
+  int btm = 0;
 #pragma unroll
-  for (int x = 0; x < KS; ++x) qf[x] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 32 * x));
-  // this wave's four queries: candidates, free slots, threshold, buffer fill
-  int nc[4], kq[4], cnt[4];
-  uint32_t th[4];
+  for (int cb = 0; cb < NQB; ++cb) {
+    const int qq = q0 + 16 * cb + r16;
+    const int qc = min(qq, nq - 1);
+    bt[cb] = qq < nq
+                 ? min(max(q_pos[static_cast<int64_t>(b) * nq + qc], 0), n_rows * B - 1) / B
+                 : 0;
+    btm = max(btm, bt[cb]);
+    const uint16_t* qrow = qidx + b * qsb + static_cast<int64_t>(qc) * qst + 8 * g;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int bq = __shfl(bt, w + 4 * u, 64);
-    nc[u] = q0 + w + 4 * u < nq ? max(bq - 1, 0) : 0;
+    for (int x = 0; x < KS; ++x)
+      qf[cb][x] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 32 * x));
+  }
+  const int btmax = static_cast<int>(wave_max(static_cast<float>(btm)));
+  // this wave's queries: candidates, free slots, threshold, buffer fill
+  int nc[QW], kq[QW], cnt[QW];
+  uint32_t th[QW];
+#pragma unroll
+  for (int u = 0; u < QW; ++u) {
+    const int j = w + NW * u;
+    int bq = 0;
+#pragma unroll
+    for (int cb = 0; cb < NQB; ++cb) {
+      const int v = __shfl(bt[cb], j % 16, 64);
+      bq = j / 16 == cb ? v : bq;
+    }
+    nc[u] = q0 + j < nq ? max(bq - 1, 0) : 0;
     kq[u] = m - (bq == 0 ? 1 : 2);
     th[u] = 0u;
     cnt[u] = 0;
   }
-  const int nsteps = btmax > 1 ? (btmax - 1 + 63) / 64 : 0;
+  const int nsteps = btmax > 1 ? (btmax - 1 + SB - 1) / SB : 0;
   auto load = [&](int step, uint4 (&sf)[3 * KS]) {
-    const int cc = min(1 + 64 * step + 16 * w + r16, n_rows - 1);
+    const int cc = min(1 + SB * step + 16 * w + r16, n_rows - 1);
     const uint16_t* srow = split + (static_cast<int64_t>(b) * n_rows + cc) * 3 * D + 8 * g;
 #pragma unroll
     for (int x = 0; x < 3 * KS; ++x)
@@ -615,59 +632,68 @@ __global__ __launch_bounds__(256) void route_blocks_stream_kernel(
   uint4 sf[3 * KS];
   if (nsteps > 0) load(0, sf);
   for (int step = 0; step < nsteps; ++step) {
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 acc[NQB];
 #pragma unroll
-    for (int x = 0; x < 3 * KS; ++x) acc = mfma16(as_bf16x8(sf[x]), qf[x % KS], acc);
+    for (int cb = 0; cb < NQB; ++cb) {
+      acc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int x = 0; x < 3 * KS; ++x) acc[cb] = mfma16(as_bf16x8(sf[x]), qf[cb][x % KS], acc[cb]);
+    }
     if (step + 1 < nsteps) load(step + 1, sf);
     float* sg = &stg[step & 1][0][0];
-    *reinterpret_cast<float4*>(sg + r16 * 64 + 16 * w + 4 * g) =
-        make_float4(acc[0] * invB, acc[1] * invB, acc[2] * invB, acc[3] * invB);
+#pragma unroll
+    for (int cb = 0; cb < NQB; ++cb)
+      *reinterpret_cast<float4*>(sg + (16 * cb + r16) * SB + 16 * w + 4 * g) =
+          make_float4(acc[cb][0] * invB, acc[cb][1] * invB, acc[cb][2] * invB, acc[cb][3] * invB);
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = w + 4 * u;
-      const int p = 64 * step + l;
-      const uint32_t key = p < nc[u] ? order_key(sg[j * 64 + l]) : 0u;
-      const bool pass = p < nc[u] && key > th[u];
-      const uint64_t pm = __ballot(pass);
-      if (pm == 0ull) continue;
-      if (pass) {
-        const int e = cnt[u] + static_cast<int>(lanes_below(pm));
-        bkey[j][e] = key;
-        bpos[j][e] = p;
-      }
-      cnt[u] += static_cast<int>(__popcll(pm));
-      if (cnt[u] > kStreamCap - 64) {
-        // cut the buffer back to its best kq (in position order)
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-        uint32_t k2[kStreamCap / 64];
-        int p2[kStreamCap / 64];
-        uint32_t ok2 = 0;
+    for (int u = 0; u < QW; ++u) {
+      const int j = w + NW * u;
 #pragma unroll
-        for (int i = 0; i < kStreamCap / 64; ++i) {
-          const int e = 64 * i + l;
-          k2[i] = e < cnt[u] ? bkey[j][e] : 0u;
-          p2[i] = e < cnt[u] ? bpos[j][e] : 0;
-          ok2 |= e < cnt[u] ? (1u << i) : 0u;
+      for (int h = 0; h < SB / 64; ++h) {
+        const int p = SB * step + 64 * h + l;
+        const uint32_t key = p < nc[u] ? order_key(sg[j * SB + 64 * h + l]) : 0u;
+        const bool pass = p < nc[u] && key > th[u];
+        const uint64_t pm = __ballot(pass);
+        if (pm == 0ull) continue;
+        if (pass) {
+          const int e = cnt[u] + static_cast<int>(lanes_below(pm));
+          bkey[j][e] = key;
+          bpos[j][e] = p;
         }
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-        const WaveSel sel = wave_select(k2, ok2, static_cast<uint32_t>(kq[u]));
-        wave_compact(k2, ok2, sel, [&](int i, uint32_t pos) {
-          bkey[j][pos] = k2[i];
-          bpos[j][pos] = p2[i];
-        });
-        th[u] = sel.T;
-        cnt[u] = kq[u];
+        cnt[u] += static_cast<int>(__popcll(pm));
+        if (cnt[u] > kStreamCap - 64) {
+          // cut the buffer back to its best kq (in position order)
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+          uint32_t k2[kStreamCap / 64];
+          int p2[kStreamCap / 64];
+          uint32_t ok2 = 0;
+#pragma unroll
+          for (int i = 0; i < kStreamCap / 64; ++i) {
+            const int e = 64 * i + l;
+            k2[i] = e < cnt[u] ? bkey[j][e] : 0u;
+            p2[i] = e < cnt[u] ? bpos[j][e] : 0;
+            ok2 |= e < cnt[u] ? (1u << i) : 0u;
+          }
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+          const WaveSel sel = wave_select(k2, ok2, static_cast<uint32_t>(kq[u]));
+          wave_compact(k2, ok2, sel, [&](int i, uint32_t pos) {
+            bkey[j][pos] = k2[i];
+            bpos[j][pos] = p2[i];
+          });
+          th[u] = sel.T;
+          cnt[u] = kq[u];
+        }
       }
     }
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int j = w + 4 * u;
+  for (int u = 0; u < QW; ++u) {
+    const int j = w + NW * u;
     const int q = q0 + j;
     if (q >= nq) break;
     const int64_t qi = static_cast<int64_t>(b) * nq + q;
@@ -703,14 +729,18 @@ hipError_t launch_route_blocks(const uint16_t* qidx, Str3 qs, const int32_t* q_p
       static_cast<unsigned>((static_cast<int64_t>(batch) * ntq + 7) / 8 * 8);
   const float invB = 1.0f / static_cast<float>(B);
   if (n_rows > kRouteMaxRows) {
+    constexpr int NW = 4, QS = 16;
+    const int ntq_s = (nq + QS - 1) / QS;
+    const unsigned grid_s =
+        static_cast<unsigned>((static_cast<int64_t>(batch) * ntq_s + 7) / 8 * 8);
     if (d == 64)
-      hipLaunchKernelGGL((route_blocks_stream_kernel<64>), dim3(grid_wg), dim3(256), 0, s, qidx,
-                         qs.b, qs.t, q_pos, nq, split, n_rows, B, invB, m, block_idx, batch, ntq,
-                         grid_wg);
+      hipLaunchKernelGGL((route_blocks_stream_kernel<64, NW, QS>), dim3(grid_s), dim3(64 * NW), 0,
+                         s, qidx, qs.b, qs.t, q_pos, nq, split, n_rows, B, invB, m, block_idx,
+                         batch, ntq_s, grid_s);
     else
-      hipLaunchKernelGGL((route_blocks_stream_kernel<128>), dim3(grid_wg), dim3(256), 0, s, qidx,
-                         qs.b, qs.t, q_pos, nq, split, n_rows, B, invB, m, block_idx, batch, ntq,
-                         grid_wg);
+      hipLaunchKernelGGL((route_blocks_stream_kernel<128, NW, QS>), dim3(grid_s), dim3(64 * NW),
+                         0, s, qidx, qs.b, qs.t, q_pos, nq, split, n_rows, B, invB, m, block_idx,
+                         batch, ntq_s, grid_s);
     return hipGetLastError();
   }
 #define HISA_RB(D_, IT_)                                                                        \
