@@ -527,6 +527,9 @@ HILS_PREFILL_SMALL = [
                                         Hkv=2, nq=900, int_mode=True),
     WORKLOADS["hils_prefill_64k"].with_(name="hilsp_c64_m64", batch=1, L=4480, m=64, Hq=1,
                                         Hkv=1, nq=400, int_mode=True),
+    WORKLOADS["hils_prefill_64k"].with_(name="hilsp_d128_c256", batch=1, L=3000, B=256, m=5,
+                                        Hq=2, Hkv=2, Dk=128, Dv=128, d_idx=128, nq=600,
+                                        int_mode=True),
 ]
 
 
@@ -551,6 +554,14 @@ def test_hils_prefill_streamed_routing():
                                             int_mode=True)
     log(f"case hils prefill, streamed routing {w}")
     assert _hils_prefill_check(w, exact=True, positions=sample_positions(w, 40), subset=True) == 0
+
+
+def test_hils_prefill_streamed_routing_d128():
+    # head width 128 through the streamed routing (1172 chunks of 64)
+    w = WORKLOADS["hils_prefill_64k"].with_(name="hilsp_d128_1172", L=75000, Hq=2, Hkv=2,
+                                            Dk=128, Dv=128, d_idx=128, m=16, int_mode=True)
+    log(f"case hils prefill, streamed routing, width 128 {w}")
+    assert _hils_prefill_check(w, exact=True, positions=sample_positions(w, 32), subset=True) == 0
 
 
 def test_hils_prefill_no_projection():
