@@ -19,6 +19,8 @@
 // write a_c and the chunk logits; a second kernel mixes them per pair. One
 // workgroup per pair would keep the whole step on as many CUs as there are
 // pairs (16 at batch 1), each moving all 32 chunks through its own loads.
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.h"
 
@@ -436,6 +438,20 @@ __device__ __forceinline__ float sum_x4_groups(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// maximum over the 16 lanes of each DPP row (every lane gets it): rotations
+// by 1, 2, 4 and 8 within the row
+__device__ __forceinline__ float row16_max(float v) {
+  auto rot = [](float x, auto ctrl) {
+    return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+        0, static_cast<int>(__float_as_uint(x)), decltype(ctrl)::value, 0xf, 0xf, false)));
+  };
+  v = fmaxf(v, rot(v, std::integral_constant<int, 0x121>{}));  // row_ror:1
+  v = fmaxf(v, rot(v, std::integral_constant<int, 0x122>{}));  // row_ror:2
+  v = fmaxf(v, rot(v, std::integral_constant<int, 0x124>{}));  // row_ror:4
+  v = fmaxf(v, rot(v, std::integral_constant<int, 0x128>{}));  // row_ror:8
+  return v;
+}
+
 template <int D>
 __device__ __forceinline__ void load_kfrags(uint4 (&kf)[4][D / 32], const uint16_t* kb, int64_t kst,
                                             int j0, int L, int r, int g) {
@@ -629,9 +645,8 @@ __global__ __launch_bounds__(256) void hils_pair_chunk_kernel(
       // the row leaves as fp16 scaled by 2^-E, E the exponent of its largest
       // magnitude (so that it lies in [0.5, 1)): 11 significant bits relative
       // to the row maximum for any magnitude; E goes to pexp
-      float amax = fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3)));
-#pragma unroll
-      for (int sh = 1; sh < LPR; sh <<= 1) amax = fmaxf(amax, __shfl_xor(amax, sh, 64));
+      float amax = row16_max(fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3))));
+      if constexpr (LPR == 32) amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
       const int ex = min(max(static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu) - 126, -125),
                          126);
       const float sc = __uint_as_float(static_cast<uint32_t>(127 - ex) << 23);
