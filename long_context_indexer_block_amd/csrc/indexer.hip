@@ -728,7 +728,9 @@ hipError_t launch_route_blocks(const uint16_t* qidx, Str3 qs, const int32_t* q_p
   const unsigned grid_wg =
       static_cast<unsigned>((static_cast<int64_t>(batch) * ntq + 7) / 8 * 8);
   const float invB = 1.0f / static_cast<float>(B);
-  if (n_rows > kRouteMaxRows) {
+  // streamed selection whenever m allows it: faster than holding all scores
+  // on chip even at 1024 blocks (64K two-level prefill routing 2.72 -> 2.39 ms)
+  if (m <= kRouteStreamMaxM) {
     constexpr int NW = 4, QS = 16;
     const int ntq_s = (nq + QS - 1) / QS;
     const unsigned grid_s =

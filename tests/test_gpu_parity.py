@@ -646,6 +646,9 @@ ROUTE_CASES = [
     (1, 64, 524288, 64, 64, 130, "random", 1),
     (1, 50, 300000, 128, 64, 8, "last", 8),
     (1, 2000, 140000, 64, 64, 16, "prefill", 8),
+    # scores held on chip (m above the streamed selection's limit of 130)
+    (1, 300, 65600, 64, 64, 200, "random", 1),
+    (2, 100, 40000, 128, 128, 140, "prefill", 8),
 ]
 
 
