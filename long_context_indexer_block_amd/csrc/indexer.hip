@@ -570,14 +570,14 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_blocks_kernel(
 constexpr int kStreamCap = 256;  // buffer entries per query
 constexpr int kStreamK = kStreamCap - 64 - 64;
 
-template <int D, int NW, int QS>
+template <int D, int NW, int QS, int TW>
 __global__ __launch_bounds__(64 * NW) void route_blocks_stream_kernel(
     const uint16_t* __restrict__ qidx, int64_t qsb, int64_t qst, const int32_t* __restrict__ q_pos,
     int nq, const uint16_t* __restrict__ split, int n_rows, int B, float invB, int m,
     int32_t* __restrict__ block_idx, int batch, int ntq, unsigned grid_wg) {
   constexpr int KS = D / 32;
   constexpr int NQB = QS / 16;          // 16-query column blocks of the products
-  constexpr int SB = 16 * NW;           // candidate blocks per step
+  constexpr int SB = 16 * NW * TW;      // candidate blocks per step (TW tiles per wave)
   constexpr int QW = QS / NW;           // queries filtered per wave
   __shared__ __align__(16) float stg[2][QS][SB];
   __shared__ uint32_t bkey[QS][kStreamCap];
@@ -622,29 +622,39 @@ __global__ __launch_bounds__(64 * NW) void route_blocks_stream_kernel(
     cnt[u] = 0;
   }
   const int nsteps = btmax > 1 ? (btmax - 1 + SB - 1) / SB : 0;
-  auto load = [&](int step, uint4 (&sf)[3 * KS]) {
-    const int cc = min(1 + SB * step + 16 * w + r16, n_rows - 1);
-    const uint16_t* srow = split + (static_cast<int64_t>(b) * n_rows + cc) * 3 * D + 8 * g;
+  // wave w scores tiles w, w + NW, ... (TW of them) of each step
+  auto load = [&](int step, uint4 (&sf)[TW][3 * KS]) {
 #pragma unroll
-    for (int x = 0; x < 3 * KS; ++x)
-      sf[x] = *reinterpret_cast<const uint4*>(srow + (x / KS) * D + 32 * (x % KS));
+    for (int v = 0; v < TW; ++v) {
+      const int cc = min(1 + SB * step + 16 * (w + NW * v) + r16, n_rows - 1);
+      const uint16_t* srow = split + (static_cast<int64_t>(b) * n_rows + cc) * 3 * D + 8 * g;
+#pragma unroll
+      for (int x = 0; x < 3 * KS; ++x)
+        sf[v][x] = *reinterpret_cast<const uint4*>(srow + (x / KS) * D + 32 * (x % KS));
+    }
   };
-  uint4 sf[3 * KS];
+  uint4 sf[TW][3 * KS];
   if (nsteps > 0) load(0, sf);
   for (int step = 0; step < nsteps; ++step) {
-    f32x4 acc[NQB];
+    f32x4 acc[TW][NQB];
 #pragma unroll
-    for (int cb = 0; cb < NQB; ++cb) {
-      acc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int v = 0; v < TW; ++v)
 #pragma unroll
-      for (int x = 0; x < 3 * KS; ++x) acc[cb] = mfma16(as_bf16x8(sf[x]), qf[cb][x % KS], acc[cb]);
-    }
+      for (int cb = 0; cb < NQB; ++cb) {
+        acc[v][cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int x = 0; x < 3 * KS; ++x)
+          acc[v][cb] = mfma16(as_bf16x8(sf[v][x]), qf[cb][x % KS], acc[v][cb]);
+      }
     if (step + 1 < nsteps) load(step + 1, sf);
     float* sg = &stg[step & 1][0][0];
 #pragma unroll
-    for (int cb = 0; cb < NQB; ++cb)
-      *reinterpret_cast<float4*>(sg + (16 * cb + r16) * SB + 16 * w + 4 * g) =
-          make_float4(acc[cb][0] * invB, acc[cb][1] * invB, acc[cb][2] * invB, acc[cb][3] * invB);
+    for (int v = 0; v < TW; ++v)
+#pragma unroll
+      for (int cb = 0; cb < NQB; ++cb)
+        *reinterpret_cast<float4*>(sg + (16 * cb + r16) * SB + 16 * (w + NW * v) + 4 * g) =
+            make_float4(acc[v][cb][0] * invB, acc[v][cb][1] * invB, acc[v][cb][2] * invB,
+                        acc[v][cb][3] * invB);
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < QW; ++u) {
@@ -731,16 +741,16 @@ hipError_t launch_route_blocks(const uint16_t* qidx, Str3 qs, const int32_t* q_p
   // streamed selection whenever m allows it: faster than holding all scores
   // on chip even at 1024 blocks (64K two-level prefill routing 2.72 -> 2.39 ms)
   if (m <= kRouteStreamMaxM) {
-    constexpr int NW = 4, QS = 16;
+    constexpr int NW = 4, QS = 16, TW = 1;
     const int ntq_s = (nq + QS - 1) / QS;
     const unsigned grid_s =
         static_cast<unsigned>((static_cast<int64_t>(batch) * ntq_s + 7) / 8 * 8);
     if (d == 64)
-      hipLaunchKernelGGL((route_blocks_stream_kernel<64, NW, QS>), dim3(grid_s), dim3(64 * NW), 0,
+      hipLaunchKernelGGL((route_blocks_stream_kernel<64, NW, QS, TW>), dim3(grid_s), dim3(64 * NW), 0,
                          s, qidx, qs.b, qs.t, q_pos, nq, split, n_rows, B, invB, m, block_idx,
                          batch, ntq_s, grid_s);
     else
-      hipLaunchKernelGGL((route_blocks_stream_kernel<128, NW, QS>), dim3(grid_s), dim3(64 * NW),
+      hipLaunchKernelGGL((route_blocks_stream_kernel<128, NW, QS, TW>), dim3(grid_s), dim3(64 * NW),
                          0, s, qidx, qs.b, qs.t, q_pos, nq, split, n_rows, B, invB, m, block_idx,
                          batch, ntq_s, grid_s);
     return hipGetLastError();
