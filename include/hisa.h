@@ -261,9 +261,11 @@ size_t hils_two_level_attn_fwd_workspace_bytes(int batch, int H, int D, int m);
  *             bytes, 256-byte aligned, contents on entry ignored. With it, the
  *             (query, slot) entries are bucketed by chunk and each chunk's K
  *             and V rows are read once per 64 entries (matrix cores), with a
- *             per-entry partial result merged per query; NULL runs one
- *             workgroup per (query, head) gathering its own chunks (same
- *             result up to fp32 rounding; for few queries). Too small is
+ *             per-entry partial result (fp16, scaled per row by a power of
+ *             two: 11 significant bits relative to the row's largest value)
+ *             merged per query; NULL runs one workgroup per (query, head)
+ *             gathering its own chunks in fp32 (for few queries; the two
+ *             differ by that rounding). Too small is
  *             HISA_ERR_WORKSPACE. Its size is about batch*H*(nq*m*(2D + 13)
  *             + L*D*4) bytes (fp16 per-entry partials, the local keys).
  * q, k, v 16-byte aligned with strides in multiples of 8 elements; khat and
