@@ -268,8 +268,8 @@ size_t hils_two_level_attn_fwd_workspace_bytes(int batch, int H, int D, int m);
  *             differ by that rounding). Too small is
  *             HISA_ERR_WORKSPACE. Its size is about batch*H*(nq*m*(2D + 13)
  *             + L*D*4) bytes (fp16 per-entry partials, the local keys).
- * q, k, v 16-byte aligned with strides in multiples of 8 elements; khat and
- * proj 16-byte aligned. batch*H <= 65535, batch*H*nq*m < 2^32; sizes must be
+ * q, k, v and out 16-byte aligned with strides in multiples of 8 elements;
+ * khat and proj 16-byte aligned. batch*H <= 65535, batch*H*nq*m < 2^32; sizes must be
  * >= 1. */
 hisa_status_t hils_two_level_prefill_fwd(const void* q, hisa_strides_t qs, const void* k,
                                          hisa_strides_t ks, const void* v, hisa_strides_t vs,

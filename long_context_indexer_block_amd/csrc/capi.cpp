@@ -376,7 +376,7 @@ hisa_status_t hils_two_level_prefill_fwd(const void* q, hisa_strides_t qs, const
   if ((st = check_bf16(v, vs, "v")) != HISA_OK) return st;
   CHECK(aligned16(khat), HISA_ERR_SHAPE, "khat must be 16-byte aligned");
   CHECK(proj == nullptr || aligned16(proj), HISA_ERR_SHAPE, "proj must be 16-byte aligned");
-  CHECK(nonneg(os), HISA_ERR_SHAPE, "out strides must be non-negative");
+  if ((st = check_bf16(out, os, "out")) != HISA_OK) return st;
   if (workspace != nullptr) {
     CHECK((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, HISA_ERR_WORKSPACE,
           "workspace must be 256-byte aligned");

@@ -668,16 +668,17 @@ __global__ __launch_bounds__(256) void hils_pair_chunk_kernel(
 }
 
 // One wave per (bh, query): the softmax over the chosen chunks' logits
-// (lane s holds slot s) mixes the scaled fp16 partials. Lane l reads columns
-// 2(l % (D/2)) .. +1 of slots s = SL*i + l / (D/2), SL = 128 / D slots per
-// load instruction; the SL lane groups are summed at the end.
+// (lane s holds slot s) mixes the scaled fp16 partials. Lane l reads eight
+// columns 8(l % LPS) .. +7 (16 bytes) of slots s = SL*i + l / LPS, LPS = D/8
+// lanes per partial row, SL = 64/LPS slots per load instruction, four loads
+// in flight; the SL lane groups are summed at the end with lane swaps.
 template <int D>
 __global__ __launch_bounds__(256) void hils_prefill_combine_kernel(
     const int32_t* __restrict__ chunk_idx, const int32_t* __restrict__ q_pos, int H, int nq,
     int L, int C, int m, const uint16_t* __restrict__ partial, const int8_t* __restrict__ pexp,
     const float* __restrict__ logit, uint16_t* __restrict__ out, Str3 os, int64_t nitems) {
-  constexpr int HP = D / 2;        // lanes per slot
-  constexpr int SL = 64 / HP;      // slots per load instruction
+  constexpr int LPS = D / 8;       // lanes per partial row
+  constexpr int SL = 64 / LPS;     // slots per load instruction
   const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (item >= nitems) return;
   const int l = threadIdx.x & 63;
@@ -695,40 +696,49 @@ __global__ __launch_bounds__(256) void hils_prefill_combine_kernel(
   // the mixing weight carries the slot's partial scale 2^E
   const float wmix = ok ? wgt * __uint_as_float(static_cast<uint32_t>(127 + pexp[e0 + l]) << 23)
                         : 0.0f;
-  const int sg = l / HP, col = 2 * (l % HP);
-  float a0 = 0.0f, a1 = 0.0f;
-  for (int s0 = 0; s0 < m; s0 += 8 * SL) {
-    uint32_t val[8];
-    float ws[8];
+  const int sg = l / LPS, col = 8 * (l % LPS);
+  float a[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+  for (int x = 0; x < 8; ++x) a[x] = 0.0f;
+  for (int s0 = 0; s0 < m; s0 += 4 * SL) {
+    uint4 val[4];
+    float ws[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
       const int s = s0 + SL * u + sg;
       ws[u] = __shfl(wmix, s & 63, 64);
       ws[u] = s < m ? ws[u] : 0.0f;
-      val[u] = ws[u] != 0.0f
-                   ? *reinterpret_cast<const uint32_t*>(partial + (e0 + s) * D + col)
-                   : 0u;
+      val[u] = ws[u] != 0.0f ? *reinterpret_cast<const uint4*>(partial + (e0 + s) * D + col)
+                             : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const _Float16 h0 = __builtin_bit_cast(_Float16, static_cast<uint16_t>(val[u] & 0xffffu));
-      const _Float16 h1 = __builtin_bit_cast(_Float16, static_cast<uint16_t>(val[u] >> 16));
-      a0 = fmaf(ws[u], static_cast<float>(h0), a0);
-      a1 = fmaf(ws[u], static_cast<float>(h1), a1);
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t wv[4] = {val[u].x, val[u].y, val[u].z, val[u].w};
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const _Float16 h0 = __builtin_bit_cast(_Float16, static_cast<uint16_t>(wv[x] & 0xffffu));
+        const _Float16 h1 = __builtin_bit_cast(_Float16, static_cast<uint16_t>(wv[x] >> 16));
+        a[2 * x] = fmaf(ws[u], static_cast<float>(h0), a[2 * x]);
+        a[2 * x + 1] = fmaf(ws[u], static_cast<float>(h1), a[2 * x + 1]);
+      }
     }
   }
-  if constexpr (SL == 2) {
-    const auto s0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a0), __float_as_uint(a0),
-                                                     false, false);
-    const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a1), __float_as_uint(a1),
-                                                     false, false);
-    a0 = __uint_as_float(s0[0]) + __uint_as_float(s0[1]);
-    a1 = __uint_as_float(s1[0]) + __uint_as_float(s1[1]);
+  // sum the SL slot groups: lanes 8 apart within a row (width 64), then the
+  // four rows of 16 lanes
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    float v = a[x];
+    if constexpr (LPS == 8)
+      v += __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+          0, static_cast<int>(__float_as_uint(v)), 0x128, 0xf, 0xf, false)));  // row_ror:8
+    a[x] = sum_x4_groups(v);
   }
   const float iz = z > 0.0f ? 1.0f / z : 0.0f;
   if (sg == 0) {
     uint16_t* orow = out + b * os.b + static_cast<int64_t>(qi) * os.t + h * os.h;
-    *reinterpret_cast<uint32_t*>(orow + col) = pack_bf16x2(a0 * iz, a1 * iz);
+    *reinterpret_cast<uint4*>(orow + col) =
+        make_uint4(pack_bf16x2(a[0] * iz, a[1] * iz), pack_bf16x2(a[2] * iz, a[3] * iz),
+                   pack_bf16x2(a[4] * iz, a[5] * iz), pack_bf16x2(a[6] * iz, a[7] * iz));
   }
 }
 

@@ -185,6 +185,9 @@ def test_hils_prefill_validation():
     a = list(args)
     a[1] = S(0, 1024, 4)                                             # q head stride not 8k
     assert L.hils_two_level_prefill_fwd(*a) == 2
+    a = list(args)
+    a[21] = S(0, 1020, 64)                                           # out token stride not 8k
+    assert L.hils_two_level_prefill_fwd(*a) == 2 and "out" in _err()
     # the bucketed path's scratch: per-entry partials dominate
     need = L.hils_two_level_prefill_fwd_workspace_bytes(1, 4096, 4096, 16, 64, 64, 32)
     assert need >= 16 * 4096 * 32 * 64 * 2 and need % 256 == 0
