@@ -3,9 +3,12 @@ scores, top-m blocks, token top-k, sparse attention) over the 64K-token MLA
 prefill (65536 queries, B=128, m=64, k=2048, 64 query heads over one
 576/512 latent kv head), inputs resident in HBM.
 
-Prints one JSON line: queries/s, per-stage milliseconds (HIP events on the
-launch stream), the dominant kernel's roofline, the flat-indexer comparison
-and the CPU oracle timed on a bounded sample of the same workload.
+Prints one JSON line: queries/s of the step with the token selection of
+each query slab overlapping the attention of the slab before it (two
+streams), per-stage milliseconds from a run of the stages one after another
+(HIP events on the launch stream), the dominant kernel's roofline, the
+flat-indexer comparison and the CPU oracle timed on a bounded sample of the
+same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-flat] [--no-cpu]
        python bench.py --sweep [--workload NAME]   (block size / kept-block sweep)
@@ -40,6 +43,10 @@ def parse():
     ap.add_argument("--workload", default="prefill_64k_mla")
     ap.add_argument("--no-flat", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--overlap-slabs", type=int, default=-1,
+                    help="prefill: query slabs whose token selection overlaps the attention of "
+                         "the slab before (0: stages one after another; default: 16 from 32768 "
+                         "queries on)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
@@ -268,8 +275,10 @@ def bench_prefill(w, a, inp):
     from long_context_indexer_block_amd.pipeline import FlatPipeline, HierPipeline
 
     nq = w.batch * w.queries
+    # query slabs whose token selection overlaps the attention of the slab before
+    slabs = a.overlap_slabs if a.overlap_slabs >= 0 else (16 if nq >= 32768 else 0)
     p = HierPipeline(inp["kidx"], inp["qidx"], inp["q_pos"], inp["q"], inp["k"], inp["v"], w.B,
-                     w.m, w.k, w.scale)
+                     w.m, w.k, w.scale, overlap_slabs=slabs)
     stages = ["summary", "block_score", "select_blocks", "token_select", "attention"]
     calls = [
         p.summarize,
@@ -279,9 +288,11 @@ def bench_prefill(w, a, inp):
                                     token_idx=p.token_idx, want_scores=False, workspace=p.ws),
         p.attend,
     ]
-    log(f"timing {a.steps} steps (warmup {a.warmup})")
-    wall, stage = timed(calls, a.steps, a.warmup)
+    log(f"timing {a.steps} steps (warmup {a.warmup}), stages one after another")
+    wall_seq, stage = timed(calls, a.steps, a.warmup)
     stage_ms = dict(zip(stages, stage))
+    log(f"timing {a.steps} steps (warmup {a.warmup}), slabs overlapped")
+    wall, _ = timed([p.run_overlapped], a.steps, a.warmup)
     # algorithmic work of the attention launch: 2*(Dk+Dv) flop per (query, head, kept token)
     n_sel = int((p.token_idx >= 0).sum().item())
     attn_flop = 2.0 * n_sel * w.Hq * (w.Dk + w.Dv)
@@ -291,6 +302,9 @@ def bench_prefill(w, a, inp):
     res["config"]["kv"] = ("MLA latent, V = first 512 columns of K" if w.mla else
                            f"{w.Hkv} kv head(s)")
     res["stage_ms"] = stage_ms
+    res["sequential"] = {"ms_per_step": wall_seq * 1e3 / a.steps,
+                         "note": "stages one after another; stage_ms are from this run",
+                         "overlap_slabs": len(p.slabs)}
     # the same step replayed as one HIP graph (no per-launch host cost)
     g_ms = graph_ms([calls], a.steps)
     res["graph"] = {"ms_per_step": g_ms, "queries_per_s": nq / (g_ms * 1e-3)}

@@ -23,8 +23,12 @@ from . import (flat_indexer_topk, flat_indexer_topk_workspace_bytes, hils_two_le
 
 
 class HierPipeline:
+    """The hierarchical step a1-a5. overlap_slabs > 1 (one sequence only) sets
+    up run_overlapped(): the token selection of query slab i+1 on one stream
+    while slab i attends on another."""
+
     def __init__(self, kidx, qidx, q_pos, q, k, v, B, m, k_top, scale, want_scores=False,
-                 want_lse=False):
+                 want_lse=False, overlap_slabs=0):
         self.kidx, self.qidx, self.q_pos, self.q, self.k, self.v = kidx, qidx, q_pos, q, k, v
         self.B, self.m, self.k_top, self.scale = B, m, k_top, scale
         b, L, d = kidx.shape
@@ -44,6 +48,16 @@ class HierPipeline:
         self.out = torch.empty(b, nq, Hq, Dv, dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty(b, nq, Hq, dtype=torch.float32, device=dev) if want_lse else None
         self.attn_ws = sparse_attn_workspace(q, k, v, self.token_idx)
+        self.slabs = []
+        if overlap_slabs > 1 and b == 1 and nq >= overlap_slabs:
+            sl = -(-nq // overlap_slabs)
+            self.slabs = [(s0, min(nq, s0 + sl)) for s0 in range(0, nq, sl)]
+            self.slab_pos = [q_pos[:, s0:s1].contiguous() for s0, s1 in self.slabs]
+            self.slab_done = [torch.cuda.Event() for _ in self.slabs]
+            nbytes = hisa_token_select_workspace_bytes(1, sl, L, B, m, k_top)
+            self.slab_ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+            self.slab_attn_ws = sparse_attn_workspace(q[:, :sl], k, v, self.token_idx[:, :sl])
+            self.streams = (torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev))
 
     def summarize(self):
         hisa_block_summary(self.kidx, self.B, summary=self.summary, split=self.split)
@@ -64,6 +78,38 @@ class HierPipeline:
     def run(self, summarize=True):
         self.index(summarize)
         self.attend()
+        return self.out
+
+    def run_overlapped(self, summarize=True):
+        """The same step, the query slabs' token selection (stream A) ahead of
+        their attention (stream B); same results as run()."""
+        if not self.slabs:
+            return self.run(summarize)
+        sa, sb = self.streams
+        cur = torch.cuda.current_stream()
+        sa.wait_stream(cur)
+        sb.wait_stream(cur)
+        ts, lse = self.token_scores, self.lse
+        with torch.cuda.stream(sa):
+            if summarize:
+                self.summarize()
+            hisa_block_score(self.qidx, self.q_pos, self.split, self.B, out=self.block_scores)
+            hisa_select_blocks(self.block_scores, self.q_pos, self.B, self.m, out=self.block_idx)
+            for (s0, s1), pos, done in zip(self.slabs, self.slab_pos, self.slab_done):
+                hisa_token_select(self.qidx[:, s0:s1], self.kidx, pos, self.block_idx[:, s0:s1],
+                                  self.B, self.k_top, token_idx=self.token_idx[:, s0:s1],
+                                  token_scores=None if ts is None else ts[:, s0:s1],
+                                  want_scores=ts is not None, workspace=self.slab_ws)
+                done.record(sa)
+        with torch.cuda.stream(sb):
+            for (s0, s1), done in zip(self.slabs, self.slab_done):
+                sb.wait_event(done)
+                sparse_attn_fwd(self.q[:, s0:s1], self.k, self.v, self.token_idx[:, s0:s1],
+                                self.scale, out=self.out[:, s0:s1],
+                                lse=None if lse is None else lse[:, s0:s1],
+                                want_lse=lse is not None, workspace=self.slab_attn_ws)
+        cur.wait_stream(sa)
+        cur.wait_stream(sb)
         return self.out
 
 

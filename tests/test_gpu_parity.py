@@ -671,3 +671,25 @@ def test_route_blocks_equals_score_then_select(case):
     got = H.hisa_route_blocks(qidx, q_pos, split, B, m)
     torch.cuda.synchronize()
     check_index_rows(got.view(-1, m).cpu().numpy(), ref.view(-1, m).cpu().numpy(), "fused route")
+
+
+def test_overlapped_step_equals_sequential():
+    # query slabs (ragged: 2048 = 683 + 683 + 682) with the token selection
+    # of the next slab on another stream: the same ids, scores, outputs, LSE
+    w = WORKLOADS["prefill_2k_tiny"]
+    inp = make_inputs(w, DEV, seed=3)
+    kw = dict(want_scores=True, want_lse=True)
+    a = HierPipeline(inp["kidx"], inp["qidx"], inp["q_pos"], inp["q"], inp["k"], inp["v"], w.B,
+                     w.m, w.k, w.scale, **kw)
+    b = HierPipeline(inp["kidx"], inp["qidx"], inp["q_pos"], inp["q"], inp["k"], inp["v"], w.B,
+                     w.m, w.k, w.scale, overlap_slabs=3, **kw)
+    assert len(b.slabs) == 3
+    a.run()
+    for _ in range(2):
+        b.run_overlapped()
+    torch.cuda.synchronize()
+    assert torch.equal(a.token_idx, b.token_idx)
+    # bit patterns: the padding is NaN
+    assert torch.equal(a.token_scores.view(torch.int32), b.token_scores.view(torch.int32))
+    assert torch.equal(a.out, b.out)
+    assert torch.equal(a.lse, b.lse)
