@@ -308,6 +308,8 @@ class HilsPrefill:
         self.out = torch.empty(b, nq, H, D, dtype=torch.bfloat16, device=dev)
         # bucketed attention (None: one workgroup per query and head)
         self.ws = hils_prefill_workspace(b, S, L, H, D, C, m, dev)
+        self.slab_done = [torch.cuda.Event() for _ in self.slabs]
+        self.streams = (torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev))
 
     def chunk_ids(self):
         """The chosen chunks of every query, [b*H, nq, m]."""
@@ -320,21 +322,50 @@ class HilsPrefill:
             hisa_block_summary(kv, self.C, proj=self.w_proj, summary=self.khat[bi * H:(bi + 1) * H],
                                split=self.split[bi * H:(bi + 1) * H])
 
-    def route(self):
+    def route_slab(self, i):
         # q[bi] viewed as [H, nq, D] (no copy): head h is routed sequence bi*H + h
         b, nq, H, D = self.q.shape
-        for (s0, s1), pos_h, idx in zip(self.slabs, self.slab_pos_h, self.slab_idx):
-            for bi in range(b):
-                rows = slice(bi * H, (bi + 1) * H)
-                hisa_route_blocks(self.q[bi, s0:s1].permute(1, 0, 2), pos_h[rows],
-                                  self.split[rows], self.C, self.m, out=idx[rows])
+        s0, s1 = self.slabs[i]
+        for bi in range(b):
+            rows = slice(bi * H, (bi + 1) * H)
+            hisa_route_blocks(self.q[bi, s0:s1].permute(1, 0, 2), self.slab_pos_h[i][rows],
+                              self.split[rows], self.C, self.m, out=self.slab_idx[i][rows])
+
+    def attend_slab(self, i):
+        s0, s1 = self.slabs[i]
+        hils_two_level_prefill_fwd(self.q[:, s0:s1], self.k, self.v, self.khat,
+                                   self.slab_idx[i], self.slab_pos[i], self.C, self.scale_chunk,
+                                   self.scale_token, proj=self.w_proj, out=self.out[:, s0:s1],
+                                   workspace=self.ws)
+
+    def route(self):
+        for i in range(len(self.slabs)):
+            self.route_slab(i)
 
     def attend(self):
-        for (s0, s1), pos, idx in zip(self.slabs, self.slab_pos, self.slab_idx):
-            hils_two_level_prefill_fwd(self.q[:, s0:s1], self.k, self.v, self.khat, idx, pos,
-                                       self.C, self.scale_chunk, self.scale_token,
-                                       proj=self.w_proj, out=self.out[:, s0:s1],
-                                       workspace=self.ws)
+        for i in range(len(self.slabs)):
+            self.attend_slab(i)
+
+    def run_overlapped(self, build=True):
+        """The same prefill with the routing of slab i+1 (stream A) running
+        while slab i attends (stream B)."""
+        sa, sb = self.streams
+        cur = torch.cuda.current_stream()
+        sa.wait_stream(cur)
+        sb.wait_stream(cur)
+        with torch.cuda.stream(sa):
+            if build:
+                self.build_keys()
+            for i, done in enumerate(self.slab_done):
+                self.route_slab(i)
+                done.record(sa)
+        with torch.cuda.stream(sb):
+            for i, done in enumerate(self.slab_done):
+                sb.wait_event(done)
+                self.attend_slab(i)
+        cur.wait_stream(sa)
+        cur.wait_stream(sb)
+        return self.out
 
     def run(self, build=True):
         if build:

@@ -564,6 +564,22 @@ def test_hils_prefill_streamed_routing_d128():
     assert _hils_prefill_check(w, exact=True, positions=sample_positions(w, 32), subset=True) == 0
 
 
+def test_hils_prefill_overlapped_equals_sequential():
+    # routing of the next slab on another stream: the same chunk ids and outputs
+    w = HILS_PREFILL_SMALL[0]
+    inp = make_inputs(w, DEV, seed=2)
+    sc = 1.0 / math.sqrt(w.Dk)
+    a = HilsPrefill(inp["q"], inp["k"], inp["v"], inp["w_proj"], inp["q_pos"], w.B, w.m, sc, sc,
+                    slab=256)
+    a.run()
+    ref_idx, ref_out = a.chunk_ids().clone(), a.out.clone()
+    for _ in range(2):
+        a.run_overlapped()
+    torch.cuda.synchronize()
+    assert torch.equal(a.chunk_ids(), ref_idx)
+    assert torch.equal(a.out, ref_out)
+
+
 def test_hils_prefill_no_projection():
     # plain-mean chunk keys (proj None) on both paths
     w = HILS_PREFILL_SMALL[0]
