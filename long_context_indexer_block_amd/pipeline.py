@@ -114,8 +114,12 @@ class HierPipeline:
 
 
 class FlatPipeline:
+    """The flat step (score every causal token, top k, attention);
+    overlap_slabs > 1 (one sequence only) sets up run_overlapped() as for
+    HierPipeline."""
+
     def __init__(self, kidx, qidx, q_pos, q, k, v, k_top, scale, want_scores=False,
-                 want_lse=False):
+                 want_lse=False, overlap_slabs=0):
         self.kidx, self.qidx, self.q_pos, self.q, self.k, self.v = kidx, qidx, q_pos, q, k, v
         self.k_top, self.scale = k_top, scale
         b, L, d = kidx.shape
@@ -130,6 +134,16 @@ class FlatPipeline:
         self.out = torch.empty(b, nq, Hq, Dv, dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty(b, nq, Hq, dtype=torch.float32, device=dev) if want_lse else None
         self.attn_ws = sparse_attn_workspace(q, k, v, self.token_idx)
+        self.slabs = []
+        if overlap_slabs > 1 and b == 1 and nq >= overlap_slabs:
+            sl = -(-nq // overlap_slabs)
+            self.slabs = [(s0, min(nq, s0 + sl)) for s0 in range(0, nq, sl)]
+            self.slab_pos = [q_pos[:, s0:s1].contiguous() for s0, s1 in self.slabs]
+            self.slab_done = [torch.cuda.Event() for _ in self.slabs]
+            nbytes = flat_indexer_topk_workspace_bytes(1, sl, L, k_top)
+            self.slab_ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+            self.slab_attn_ws = sparse_attn_workspace(q[:, :sl], k, v, self.token_idx[:, :sl])
+            self.streams = (torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev))
 
     def index(self):
         flat_indexer_topk(self.qidx, self.kidx, self.q_pos, self.k_top, token_idx=self.token_idx,
@@ -143,6 +157,34 @@ class FlatPipeline:
     def run(self):
         self.index()
         self.attend()
+        return self.out
+
+    def run_overlapped(self):
+        """The flat selection of query slab i+1 (stream A) while slab i
+        attends (stream B); same results as run()."""
+        if not self.slabs:
+            return self.run()
+        sa, sb = self.streams
+        cur = torch.cuda.current_stream()
+        sa.wait_stream(cur)
+        sb.wait_stream(cur)
+        ts, lse = self.token_scores, self.lse
+        with torch.cuda.stream(sa):
+            for (s0, s1), pos, done in zip(self.slabs, self.slab_pos, self.slab_done):
+                flat_indexer_topk(self.qidx[:, s0:s1], self.kidx, pos, self.k_top,
+                                  token_idx=self.token_idx[:, s0:s1],
+                                  token_scores=None if ts is None else ts[:, s0:s1],
+                                  want_scores=ts is not None, workspace=self.slab_ws)
+                done.record(sa)
+        with torch.cuda.stream(sb):
+            for (s0, s1), done in zip(self.slabs, self.slab_done):
+                sb.wait_event(done)
+                sparse_attn_fwd(self.q[:, s0:s1], self.k, self.v, self.token_idx[:, s0:s1],
+                                self.scale, out=self.out[:, s0:s1],
+                                lse=None if lse is None else lse[:, s0:s1],
+                                want_lse=lse is not None, workspace=self.slab_attn_ws)
+        cur.wait_stream(sa)
+        cur.wait_stream(sb)
         return self.out
 
 

@@ -689,6 +689,24 @@ def test_route_blocks_equals_score_then_select(case):
     check_index_rows(got.view(-1, m).cpu().numpy(), ref.view(-1, m).cpu().numpy(), "fused route")
 
 
+def test_flat_overlapped_equals_sequential():
+    # slabs of 683 queries: enough (query, head) items that the attention
+    # never splits its lists, so the results match bit for bit
+    w = WORKLOADS["prefill_2k_tiny"]
+    inp = make_inputs(w, DEV, seed=4)
+    a = FlatPipeline(inp["kidx"], inp["qidx"], inp["q_pos"], inp["q"], inp["k"], inp["v"], w.k,
+                     w.scale, want_lse=True)
+    b = FlatPipeline(inp["kidx"], inp["qidx"], inp["q_pos"], inp["q"], inp["k"], inp["v"], w.k,
+                     w.scale, want_lse=True, overlap_slabs=3)
+    a.run()
+    for _ in range(2):
+        b.run_overlapped()
+    torch.cuda.synchronize()
+    assert torch.equal(a.token_idx, b.token_idx)
+    assert torch.equal(a.out, b.out)
+    assert torch.equal(a.lse, b.lse)
+
+
 def test_overlapped_step_equals_sequential():
     # query slabs (ragged: 2048 = 683 + 683 + 682) with the token selection
     # of the next slab on another stream: the same ids, scores, outputs, LSE
