@@ -135,10 +135,11 @@ hisa_status_t hisa_select_blocks(const float* block_scores, const int32_t* q_pos
 /* Steps 2 and 3 in one call, for many queries: the same block_idx as
  * hisa_block_score followed by hisa_select_blocks (bit for bit: the same
  * exact products and selection), without writing the block scores to memory.
- * For m <= 130 the scores of 16 consecutive queries are streamed through
- * per-query candidate buffers on chip (any n_rows); for larger m all of their
- * scores are held on chip, which needs n_rows <= 1026 (HISA_ERR_UNSUPPORTED
- * otherwise: use the two calls). Arguments as for those two. */
+ * For m <= 130 and n_rows <= 65537 the scores of 16 or 32 consecutive
+ * queries are streamed through per-query candidate buffers on chip; otherwise
+ * all of their scores are held on chip, which needs n_rows <= 1026
+ * (HISA_ERR_UNSUPPORTED beyond both: use the two calls). Arguments as for
+ * those two. */
 hisa_status_t hisa_route_blocks(const void* qidx, hisa_strides_t qs, const int32_t* q_pos,
                                 int batch, int nq, const void* split, int n_rows, int d, int B,
                                 int m, int32_t* block_idx, hisa_stream_t stream);

@@ -159,11 +159,12 @@ def hisa_select_blocks(block_scores, q_pos, B, m, out=None):
 
 
 ROUTE_MAX_ROWS = 64 * 16 + 2      # scores kept on chip up to this many blocks
-ROUTE_STREAM_MAX_M = 130          # beyond it, streamed selection for m up to this
+ROUTE_STREAM_MAX_M = 130          # streamed selection for m up to this
+ROUTE_STREAM_MAX_ROWS = 65537     # and up to this many blocks
 
 
 def route_supported(n_rows, m):
-    return n_rows <= ROUTE_MAX_ROWS or m <= ROUTE_STREAM_MAX_M
+    return n_rows <= ROUTE_MAX_ROWS or (m <= ROUTE_STREAM_MAX_M and n_rows <= ROUTE_STREAM_MAX_ROWS)
 
 
 def hisa_route_blocks(qidx, q_pos, split, B, m, out=None):

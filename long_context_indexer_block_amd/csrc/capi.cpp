@@ -163,9 +163,12 @@ hisa_status_t hisa_route_blocks(const void* qidx, hisa_strides_t qs, const int32
         "qidx, q_pos, split and block_idx are required");
   CHECK(batch >= 1 && nq >= 1 && n_rows >= 1, HISA_ERR_SHAPE,
         "batch=%d nq=%d n_rows=%d must be >= 1", batch, nq, n_rows);
-  CHECK(n_rows <= hisa::kRouteMaxRows || m <= hisa::kRouteStreamMaxM, HISA_ERR_UNSUPPORTED,
-        "n_rows=%d above %d with m=%d above %d: use hisa_block_score and hisa_select_blocks",
-        n_rows, hisa::kRouteMaxRows, m, hisa::kRouteStreamMaxM);
+  CHECK(n_rows <= hisa::kRouteMaxRows ||
+            (m <= hisa::kRouteStreamMaxM && n_rows <= hisa::kRouteStreamMaxRows),
+        HISA_ERR_UNSUPPORTED,
+        "n_rows=%d with m=%d: on chip up to %d rows, streamed up to m=%d and %d rows; use "
+        "hisa_block_score and hisa_select_blocks",
+        n_rows, m, hisa::kRouteMaxRows, hisa::kRouteStreamMaxM, hisa::kRouteStreamMaxRows);
   CHECK(static_cast<long long>(batch) * ((nq + 15) / 16) <= 0x7fffffffLL, HISA_ERR_UNSUPPORTED,
         "grid too large");
   CHECK(m >= 2, HISA_ERR_UNSUPPORTED, "m=%d must be >= 2 (first and local block)", m);

@@ -7,6 +7,8 @@
 // block features (same sources); the block choice keeps the first block and
 // the query's own block and fills the rest with the best-scoring complete
 // blocks before it (HISA explainer 1.2.1 item 3, HISA news article).
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.h"
 #include "select.hpp"
@@ -567,10 +569,9 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_blocks_kernel(
 // order), whose K-th key becomes the threshold: a later block equal to it
 // has a higher position and could not displace it. A last select over the
 // buffer gives the kept blocks. K = m - 2 <= kStreamK.
-constexpr int kStreamCap = 256;  // buffer entries per query
-constexpr int kStreamK = kStreamCap - 64 - 64;
-
-template <int D, int NW, int QS, int TW>
+// buffer entries per query: CAP >= K + 128 (a cut leaves K, at most 64 come
+// per filtering round, a cut follows when more than CAP - 64 are held)
+template <int D, int NW, int QS, int TW, int CAP>
 __global__ __launch_bounds__(64 * NW) void route_blocks_stream_kernel(
     const uint16_t* __restrict__ qidx, int64_t qsb, int64_t qst, const int32_t* __restrict__ q_pos,
     int nq, const uint16_t* __restrict__ split, int n_rows, int B, float invB, int m,
@@ -580,8 +581,8 @@ __global__ __launch_bounds__(64 * NW) void route_blocks_stream_kernel(
   constexpr int SB = 16 * NW * TW;      // candidate blocks per step (TW tiles per wave)
   constexpr int QW = QS / NW;           // queries filtered per wave
   __shared__ __align__(16) float stg[2][QS][SB];
-  __shared__ uint32_t bkey[QS][kStreamCap];
-  __shared__ int bpos[QS][kStreamCap];
+  __shared__ uint32_t bkey[QS][CAP];
+  __shared__ uint16_t bpos[QS][CAP];  // positions < 65536 (n_rows <= 65537)
   const unsigned per = grid_wg / 8;
   const unsigned id = (blockIdx.x % 8) * per + blockIdx.x / 8;
   if (id >= static_cast<unsigned>(batch) * ntq) return;
@@ -672,15 +673,15 @@ __global__ __launch_bounds__(64 * NW) void route_blocks_stream_kernel(
           bpos[j][e] = p;
         }
         cnt[u] += static_cast<int>(__popcll(pm));
-        if (cnt[u] > kStreamCap - 64) {
+        if (cnt[u] > CAP - 64) {
           // cut the buffer back to its best kq (in position order)
           __builtin_amdgcn_wave_barrier();
           __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-          uint32_t k2[kStreamCap / 64];
-          int p2[kStreamCap / 64];
+          uint32_t k2[CAP / 64];
+          int p2[CAP / 64];
           uint32_t ok2 = 0;
 #pragma unroll
-          for (int i = 0; i < kStreamCap / 64; ++i) {
+          for (int i = 0; i < CAP / 64; ++i) {
             const int e = 64 * i + l;
             k2[i] = e < cnt[u] ? bkey[j][e] : 0u;
             p2[i] = e < cnt[u] ? bpos[j][e] : 0;
@@ -714,10 +715,10 @@ __global__ __launch_bounds__(64 * NW) void route_blocks_stream_kernel(
       for (int i = l; i < m; i += 64) out[i] = i <= bqq ? i : -1;
       continue;
     }
-    uint32_t k2[kStreamCap / 64];
+    uint32_t k2[CAP / 64];
     uint32_t ok2 = 0;
 #pragma unroll
-    for (int i = 0; i < kStreamCap / 64; ++i) {
+    for (int i = 0; i < CAP / 64; ++i) {
       const int e = 64 * i + l;
       k2[i] = e < cnt[u] ? bkey[j][e] : 0u;
       ok2 |= e < cnt[u] ? (1u << i) : 0u;
@@ -739,20 +740,34 @@ hipError_t launch_route_blocks(const uint16_t* qidx, Str3 qs, const int32_t* q_p
       static_cast<unsigned>((static_cast<int64_t>(batch) * ntq + 7) / 8 * 8);
   const float invB = 1.0f / static_cast<float>(B);
   // streamed selection whenever m allows it: faster than holding all scores
-  // on chip even at 1024 blocks (64K two-level prefill routing 2.72 -> 2.39 ms)
-  if (m <= kRouteStreamMaxM) {
-    constexpr int NW = 4, QS = 16, TW = 1;
-    const int ntq_s = (nq + QS - 1) / QS;
-    const unsigned grid_s =
-        static_cast<unsigned>((static_cast<int64_t>(batch) * ntq_s + 7) / 8 * 8);
-    if (d == 64)
-      hipLaunchKernelGGL((route_blocks_stream_kernel<64, NW, QS, TW>), dim3(grid_s), dim3(64 * NW), 0,
-                         s, qidx, qs.b, qs.t, q_pos, nq, split, n_rows, B, invB, m, block_idx,
-                         batch, ntq_s, grid_s);
+  // on chip even at 1024 blocks (64K two-level prefill routing 2.72 -> 2.39
+  // ms). With many blocks (more than 3072) and up to 64 free slots, 32
+  // queries per workgroup with 128-entry buffers: each summary row load feeds
+  // twice the products at the same 40 KB of LDS (512K routing 89 -> 66 ms,
+  // 256K 24.3 -> 22.1; at 2048 blocks 7.0 -> 7.6, so fewer blocks keep 16
+  // queries and 256 entries, as does m above 66).
+  if (m <= kRouteStreamMaxM && n_rows <= kRouteStreamMaxRows) {
+    auto go = [&](auto nw, auto qsz, auto cap) {
+      constexpr int NW = decltype(nw)::value, QS = decltype(qsz)::value;
+      constexpr int CAP = decltype(cap)::value;
+      const int ntq_s = (nq + QS - 1) / QS;
+      const unsigned grid_s =
+          static_cast<unsigned>((static_cast<int64_t>(batch) * ntq_s + 7) / 8 * 8);
+      if (d == 64)
+        hipLaunchKernelGGL((route_blocks_stream_kernel<64, NW, QS, 1, CAP>), dim3(grid_s),
+                           dim3(64 * NW), 0, s, qidx, qs.b, qs.t, q_pos, nq, split, n_rows, B,
+                           invB, m, block_idx, batch, ntq_s, grid_s);
+      else
+        hipLaunchKernelGGL((route_blocks_stream_kernel<128, NW, QS, 1, CAP>), dim3(grid_s),
+                           dim3(64 * NW), 0, s, qidx, qs.b, qs.t, q_pos, nq, split, n_rows, B,
+                           invB, m, block_idx, batch, ntq_s, grid_s);
+    };
+    if (m - 2 <= 64 && n_rows > 3072)
+      go(std::integral_constant<int, 4>{}, std::integral_constant<int, 32>{},
+         std::integral_constant<int, 128>{});
     else
-      hipLaunchKernelGGL((route_blocks_stream_kernel<128, NW, QS, TW>), dim3(grid_s), dim3(64 * NW),
-                         0, s, qidx, qs.b, qs.t, q_pos, nq, split, n_rows, B, invB, m, block_idx,
-                         batch, ntq_s, grid_s);
+      go(std::integral_constant<int, 4>{}, std::integral_constant<int, 16>{},
+         std::integral_constant<int, 256>{});
     return hipGetLastError();
   }
 #define HISA_RB(D_, IT_)                                                                        \

@@ -60,6 +60,7 @@ hipError_t launch_mla_attn(const uint16_t* q, Str3 qs, const uint16_t* kv, Str3 
 // else streamed through per-query candidate buffers, which needs m - 2 <= 128)
 constexpr int kRouteMaxRows = 64 * 16 + 2;
 constexpr int kRouteStreamMaxM = 130;
+constexpr int kRouteStreamMaxRows = 65537;  // candidate positions fit 16 bits
 hipError_t launch_route_blocks(const uint16_t* qidx, Str3 qs, const int32_t* q_pos, int batch,
                                int nq, const uint16_t* split, int n_rows, int d, int B, int m,
                                int32_t* block_idx, hipStream_t s);

@@ -145,6 +145,9 @@ def test_route_validation():
     a[6], a[9] = 1027, 131                       # too many blocks for LDS, m too large to stream
     assert L.hisa_route_blocks(*a) == 3 and "hisa_block_score" in _err()
     a = list(args)
+    a[6] = 65538                                                     # too many to stream
+    assert L.hisa_route_blocks(*a) == 3
+    a = list(args)
     a[9] = 1                                                         # m < 2
     assert L.hisa_route_blocks(*a) == 3
     a = list(args)

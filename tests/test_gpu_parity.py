@@ -662,6 +662,12 @@ ROUTE_CASES = [
     (1, 64, 524288, 64, 64, 130, "random", 1),
     (1, 50, 300000, 128, 64, 8, "last", 8),
     (1, 2000, 140000, 64, 64, 16, "prefill", 8),
+    # the two buffer sizes of the streamed selection at their boundary (more
+    # than 3072 blocks: K = 64 takes 32 queries and 128 entries, K = 65 16
+    # queries and 256)
+    (1, 200, 200000, 64, 64, 66, "random", 1),
+    (1, 200, 200000, 64, 64, 67, "random", 1),
+    (1, 100, 196700, 64, 64, 32, "random", 8),
     # scores held on chip (m above the streamed selection's limit of 130)
     (1, 300, 65600, 64, 64, 200, "random", 1),
     (2, 100, 40000, 128, 128, 140, "prefill", 8),
