@@ -403,9 +403,11 @@ __global__ __launch_bounds__(256) void hils_local_keys_kernel(
 // Tile kernel: a workgroup of 4 waves takes TPW consecutive tiles of the
 // tile table (mostly of one bucket, whose chunk K/V it loads once); wave w
 // takes entries 16w .. 16w+15 of each tile, one per lane column r = l%16.
-// The chunk's V rows are staged in LDS (rows padded by 16 bytes); K
-// fragments come straight from global (kept in registers across tiles when
-// the chunk is one 64-token group). S^T = K Q^T on 16x16x32 bf16 MFMA leaves
+// The chunk's V rows are staged in LDS (rows padded by 16 bytes); so are its
+// K rows when the chunk is one 64-token group (the four waves' fragments then
+// come from LDS and stay in registers across tiles: K read from global once
+// per workgroup instead of once per wave, 64K 6.07 -> 5.78 ms); longer
+// chunks read K fragments from global per group. S^T = K Q^T on 16x16x32 bf16 MFMA leaves
 // in lane l the entry l%16 and the tokens 4(l/16)..+3 of each 16-token tile:
 // the A operand of the 16x16x16 P V product, with V^T fragments from
 // ds_read_tr16_b64. Online softmax over the chunk's 64-token groups. Each
@@ -480,6 +482,7 @@ __global__ __launch_bounds__(256) void hils_pair_chunk_kernel(
   constexpr int LPR = D / 4;      // lanes per result row on the way out
   constexpr int RPI = 64 / LPR;   // result rows per store instruction
   __shared__ __align__(16) unsigned char vt[C * RS];
+  __shared__ __align__(16) unsigned char kt[NG == 1 ? 64 * RS : 16];
   __shared__ __align__(16) float ot[4][16 * OS];
   // the chip deals workgroups round-robin to its 8 XCDs: give each XCD a
   // contiguous run of tiles, so that the tiles of one chunk share an L2
@@ -564,9 +567,18 @@ __global__ __launch_bounds__(256) void hils_pair_chunk_kernel(
         const int jj = min(c * C + row, L - 1);
         *reinterpret_cast<uint4*>(vt + row * RS + 16 * ch) =
             *reinterpret_cast<const uint4*>(vb + static_cast<int64_t>(jj) * vs.t + 8 * ch);
+        if constexpr (NG == 1)
+          *reinterpret_cast<uint4*>(kt + row * RS + 16 * ch) =
+              *reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(jj) * ks.t + 8 * ch);
       }
-      if constexpr (NG == 1) load_kfrags<D>(kf, kb, ks.t, c * C, L, r, g);
-      __syncthreads();  // V staged
+      __syncthreads();  // V (and K) staged
+      if constexpr (NG == 1) {
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+          for (int x = 0; x < NKS; ++x)
+            kf[tau][x] = *reinterpret_cast<const uint4*>(kt + (16 * tau + r) * RS + 64 * x + 16 * g);
+      }
     }
     float mrun = -INFINITY, lsum = 0.0f;
     f32x4 o[NDB];
