@@ -320,7 +320,10 @@ hipError_t launch_pair_buckets(const int32_t* block_idx, int batch, int nq, int 
 // ------------------------------------------------------------ scoring
 // S^T[token, pair] = K_blk[token, :] . Q[pair, :]. Wave w owns tokens
 // [w*BS/4, (w+1)*BS/4) of the key block (A operand, straight from global),
-// all 64 pairs of the tile are the B operand (gathered query rows). The
+// all 64 pairs of the tile are the B operand: their query rows are gathered
+// once per workgroup into LDS (rows padded by 16 bytes), which every wave
+// reads (each wave gathering them itself read them four times: 64K token
+// select 2.25 -> 2.07 ms). The
 // accumulator lane layout (column = pair, 4 consecutive tokens) is stored
 // as one 16-byte write per pair.
 // DIRECT (one query per sequence, so no key block has two pairs): workgroup
@@ -355,6 +358,19 @@ __global__ __launch_bounds__(256) void token_score_kernel(
   }
   const int wave = threadIdx.x / kWave, lane = lane_id();
   const int g = lane / 16, r16 = lane % 16;
+  // the tile's query rows, gathered once into LDS (every wave needs all of them)
+  constexpr int QRS = 2 * D + 16;  // padded row stride (bytes)
+  __shared__ __align__(16) unsigned char qs_lds[DIRECT ? 16 : kTQ * QRS];
+  if constexpr (!DIRECT) {
+    for (int x = threadIdx.x; x < kTQ * (D / 8); x += 256) {
+      const int pr = x / (D / 8), ch = x % (D / 8);
+      const uint32_t pl = min(static_cast<uint32_t>(pr), np - 1);
+      const uint32_t qrow = pairs[p0 + pl] / m;
+      const int qq = qrow % nq;
+      *reinterpret_cast<uint4*>(qs_lds + pr * QRS + 16 * ch) = *reinterpret_cast<const uint4*>(
+          qidx + b * qsb + static_cast<int64_t>(qq) * qst + 8 * ch);
+    }
+  }
 
   bf16x8 a[MT][KS];
   const int tok0 = c * BS + wave * (BS / 4);
@@ -370,12 +386,20 @@ __global__ __launch_bounds__(256) void token_score_kernel(
     if (nt * 16 >= static_cast<int>(np)) break;
     const uint32_t pl = min(static_cast<uint32_t>(nt * 16 + r16), np - 1);
     const uint32_t pid = DIRECT ? p0 : pairs[p0 + pl];
-    const uint32_t qrow = pid / m;  // b*nq + q
-    const int qq = qrow % nq;
-    const uint16_t* qr = qidx + b * qsb + static_cast<int64_t>(qq) * qst + 8 * g;
     bf16x8 bq[KS];
+    if constexpr (DIRECT) {
+      const uint32_t qrow = pid / m;  // b*nq + q
+      const int qq = qrow % nq;
+      const uint16_t* qr = qidx + b * qsb + static_cast<int64_t>(qq) * qst + 8 * g;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) bq[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + 32 * s));
+      for (int s = 0; s < KS; ++s) bq[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + 32 * s));
+    } else {
+      if (nt == 0) __syncthreads();  // query rows staged
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        bq[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qs_lds + (nt * 16 + r16) * QRS +
+                                                           64 * s + 16 * g));
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
