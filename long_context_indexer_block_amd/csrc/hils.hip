@@ -790,12 +790,14 @@ hipError_t launch_hils_prefill(const uint16_t* q, Str3 qs, const uint16_t* k, St
                        L, C, proj, w.need, w.kloc);
   const size_t npairs = static_cast<size_t>(bh) * nq * m;
   const size_t max_tiles = (npairs + kPairTile - 1) / kPairTile + static_cast<size_t>(bh) * n_rows;
-  const int tpw = 2;  // tiles per workgroup
+  // tiles per workgroup (64K at width 64: 1, 2, 4, 6, 8 tiles took 6.22,
+  // 5.78, 5.59, 5.79, 5.75 ms; width 128 keeps 2 for its registers)
+  const int tpw = D == 64 ? 4 : 2;
   const unsigned grid_wg = static_cast<unsigned>(((max_tiles + tpw - 1) / tpw + 7) / 8 * 8);
   const TileTabs tt{w.pb.cnt, w.pb.offs, w.pb.tile_off, w.pb.total, w.pb.pairs, w.pb.tiles};
   const float stl2 = scale_token * 1.4426950408889634f;
 #define HISA_PC(D_, C_)                                                                          \
-  hipLaunchKernelGGL((hils_pair_chunk_kernel<D_, C_, 2>), dim3(grid_wg),           \
+  hipLaunchKernelGGL((hils_pair_chunk_kernel<D_, C_, D_ == 64 ? 4 : 2>), dim3(grid_wg),           \
                      dim3(256), 0, s, q,                                                          \
                      qs, k, ks, v, vs, khat, w.kloc, q_pos, H, nq, L, n_rows, m, tt, grid_wg,     \
                      scale_chunk, stl2, w.partial, w.pexp, w.logit)
