@@ -36,7 +36,6 @@ hisa_status_t hip_status(hipError_t e, const char* where) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 hisa::Str3 s3(hisa_strides_t s) { return hisa::Str3{s.batch, s.token, s.head}; }
 bool strides8(hisa_strides_t s) { return s.batch % 8 == 0 && s.token % 8 == 0 && s.head % 8 == 0; }
 bool nonneg(hisa_strides_t s) { return s.batch >= 0 && s.token >= 0 && s.head >= 0; }
