@@ -142,7 +142,7 @@ TRAFFIC_PASSES = {
 
 
 def counter_rows(folder, counter):
-    """(kernel name, value) of every dispatch in a rocprofv3 counter csv."""
+    """(kernel name, value, grid size) of every dispatch in a rocprofv3 counter csv."""
     import csv
     import glob
     files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
@@ -152,7 +152,8 @@ def counter_rows(folder, counter):
     for f in files:
         for r in csv.DictReader(open(f)):
             if r["Counter_Name"] == counter:
-                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"]),
+                             int(r.get("Grid_Size") or 0)))
     return rows
 
 
@@ -160,13 +161,16 @@ def write_traffic(folder, copy_bytes=1 << 30):
     """Traffic record of the MLA attention kernel from four counter passes:
     FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of one bench step, and the
     same counters over a plain copy of `copy_bytes`, whose known size gives
-    the factor from counter units to bytes."""
+    the factor from counter units to bytes. The step launches the attention
+    over all queries (the launch the roofline times) and per query slab: only
+    the all-query launches (the largest grid) are taken."""
     def one(sub, pick):
-        rows = [v for name, v in counter_rows(os.path.join(folder, sub), TRAFFIC_PASSES[sub])
-                if pick(name)]
+        rows = [(v, gsz) for name, v, gsz in
+                counter_rows(os.path.join(folder, sub), TRAFFIC_PASSES[sub]) if pick(name)]
         if not rows:
             raise SystemExit(f"no matching dispatch in {sub}")
-        return rows
+        top = max(gsz for _, gsz in rows)
+        return [v for v, gsz in rows if gsz == top]
     attn = lambda n: "mla_attn_kernel" in n
     copy = lambda n: "copyBuffer" in n or ("copy" in n.lower() and "Fill" not in n)
     f_kib = one("fetch", attn)
