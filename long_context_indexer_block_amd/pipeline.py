@@ -24,8 +24,8 @@ from . import (flat_indexer_topk, flat_indexer_topk_workspace_bytes, hils_two_le
 
 class HierPipeline:
     """The hierarchical step a1-a5. overlap_slabs > 1 (one sequence only) sets
-    up run_overlapped(): the token selection of query slab i+1 on one stream
-    while slab i attends on another."""
+    up run_overlapped(): the block scores, block and token selection of query
+    slab i+1 on one stream while slab i attends on another."""
 
     def __init__(self, kidx, qidx, q_pos, q, k, v, B, m, k_top, scale, want_scores=False,
                  want_lse=False, overlap_slabs=0):
@@ -81,8 +81,9 @@ class HierPipeline:
         return self.out
 
     def run_overlapped(self, summarize=True):
-        """The same step, the query slabs' token selection (stream A) ahead of
-        their attention (stream B); same results as run()."""
+        """The same step, the query slabs' block scores, block and token
+        selection (stream A) ahead of their attention (stream B); same results
+        as run()."""
         if not self.slabs:
             return self.run(summarize)
         sa, sb = self.streams
@@ -93,9 +94,11 @@ class HierPipeline:
         with torch.cuda.stream(sa):
             if summarize:
                 self.summarize()
-            hisa_block_score(self.qidx, self.q_pos, self.split, self.B, out=self.block_scores)
-            hisa_select_blocks(self.block_scores, self.q_pos, self.B, self.m, out=self.block_idx)
             for (s0, s1), pos, done in zip(self.slabs, self.slab_pos, self.slab_done):
+                hisa_block_score(self.qidx[:, s0:s1], pos, self.split, self.B,
+                                 out=self.block_scores[:, s0:s1])
+                hisa_select_blocks(self.block_scores[:, s0:s1], pos, self.B, self.m,
+                                   out=self.block_idx[:, s0:s1])
                 hisa_token_select(self.qidx[:, s0:s1], self.kidx, pos, self.block_idx[:, s0:s1],
                                   self.B, self.k_top, token_idx=self.token_idx[:, s0:s1],
                                   token_scores=None if ts is None else ts[:, s0:s1],

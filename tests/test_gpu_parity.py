@@ -714,8 +714,9 @@ def test_flat_overlapped_equals_sequential():
 
 
 def test_overlapped_step_equals_sequential():
-    # query slabs (ragged: 2048 = 683 + 683 + 682) with the token selection
-    # of the next slab on another stream: the same ids, scores, outputs, LSE
+    # query slabs (ragged: 2048 = 683 + 683 + 682) with the block scores,
+    # block and token selection of the next slab on another stream: the same
+    # block ids, ids, scores, outputs, LSE
     w = WORKLOADS["prefill_2k_tiny"]
     inp = make_inputs(w, DEV, seed=3)
     kw = dict(want_scores=True, want_lse=True)
@@ -728,6 +729,8 @@ def test_overlapped_step_equals_sequential():
     for _ in range(2):
         b.run_overlapped()
     torch.cuda.synchronize()
+    assert torch.equal(a.block_scores.view(torch.int32), b.block_scores.view(torch.int32))
+    assert torch.equal(a.block_idx, b.block_idx)
     assert torch.equal(a.token_idx, b.token_idx)
     # bit patterns: the padding is NaN
     assert torch.equal(a.token_scores.view(torch.int32), b.token_scores.view(torch.int32))
