@@ -356,7 +356,10 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&key)[IT], uint32_t ok
 
 constexpr int kSelUnion = 1024;  // LDS entries for the waves' kept candidates
 
-template <int W, int IT>
+// TOPK (W > 1): each wave, and wave 0 over the union, uses wave_topk, the
+// faster choice for a few queries keeping at most 32 blocks; many queries
+// fill the chip better with the plain wave_select.
+template <int W, int IT, bool TOPK = false>
 __global__ __launch_bounds__(64 * W) void select_blocks_wave_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ q_pos, int nq, int n_rows,
     int B, int m, int32_t* __restrict__ block_idx) {
@@ -365,6 +368,9 @@ __global__ __launch_bounds__(64 * W) void select_blocks_wave_kernel(
   __shared__ uint32_t ckey[CAP];
   __shared__ int cpos[CAP];
   __shared__ int ccnt[W];
+  // with TOPK: wave_topk's survivors, one slice per wave
+  __shared__ uint32_t skey[TOPK ? W : 1][kSelSmall];
+  __shared__ int spos[TOPK ? W : 1][kSelSmall];
   const int64_t qi = static_cast<int64_t>(blockIdx.y) * nq + blockIdx.x;
   const float* row = scores + qi * n_rows;
   int32_t* out = block_idx + qi * m;
@@ -393,11 +399,19 @@ __global__ __launch_bounds__(64 * W) void select_blocks_wave_kernel(
   } else {
     const int kw = min(K, max(0, min(S, n - base)));  // kept by this wave
     if (kw > 0) {
-      const WaveSel sel = wave_select(key, okm, static_cast<uint32_t>(kw));
-      wave_compact(key, okm, sel, [&](int i, uint32_t pos) {
-        ckey[w * K + pos] = key[i];
-        cpos[w * K + pos] = base + 64 * i + l;
-      });
+      if constexpr (TOPK) {
+        // the kept key is read back from the row (it is in cache)
+        wave_topk(key, okm, static_cast<uint32_t>(kw), skey[w], spos[w], [&](uint32_t pos, int p) {
+          ckey[w * K + pos] = order_key(row[1 + base + p]);
+          cpos[w * K + pos] = base + p;
+        });
+      } else {
+        const WaveSel sel = wave_select(key, okm, static_cast<uint32_t>(kw));
+        wave_compact(key, okm, sel, [&](int i, uint32_t pos) {
+          ckey[w * K + pos] = key[i];
+          cpos[w * K + pos] = base + 64 * i + l;
+        });
+      }
     }
     if (l == 0) ccnt[w] = kw;
     __syncthreads();
@@ -414,8 +428,14 @@ __global__ __launch_bounds__(64 * W) void select_blocks_wave_kernel(
         k2[i] = ok ? ckey[e] : 0u;
         ok2 |= ok ? (1u << i) : 0u;
       }
-      const WaveSel sel = wave_select(k2, ok2, static_cast<uint32_t>(K));
-      wave_compact(k2, ok2, sel, [&](int i, uint32_t pos) { out[1 + pos] = cpos[64 * i + l] + 1; });
+      if constexpr (TOPK) {
+        wave_topk(k2, ok2, static_cast<uint32_t>(K), skey[0], spos[0],
+                  [&](uint32_t pos, int e) { out[1 + pos] = cpos[e] + 1; });
+      } else {
+        const WaveSel sel = wave_select(k2, ok2, static_cast<uint32_t>(K));
+        wave_compact(k2, ok2, sel,
+                     [&](int i, uint32_t pos) { out[1 + pos] = cpos[64 * i + l] + 1; });
+      }
     }
   }
   if (threadIdx.x == 0) {
@@ -439,6 +459,12 @@ hipError_t launch_select_blocks(const float* scores, const int32_t* q_pos, int b
     if (n_rows <= 64 * 16)
       hipLaunchKernelGGL((select_blocks_kernel<64, 16, true>), grid, dim3(64), 0, s, scores,
                          q_pos, nq, n_rows, B, m, block_idx);
+    // measured: from 6,144 blocks on, with m = 32, 16 waves with wave_topk
+    // beat the histogram select (16,384 blocks: 22 vs 32 us); with m = 64
+    // and at 4,096 blocks the histogram select stays faster
+    else if (n_rows > 4 * 1024 + 2 && n_rows <= 16 * 1024 && m - 2 <= 32)
+      hipLaunchKernelGGL((select_blocks_wave_kernel<16, 16, true>), grid, dim3(64 * 16), 0, s,
+                         scores, q_pos, nq, n_rows, B, m, block_idx);
     else if (n_rows <= 1024 * 16)
       hipLaunchKernelGGL((select_blocks_kernel<1024, 16, true>), grid, dim3(1024), 0, s, scores,
                          q_pos, nq, n_rows, B, m, block_idx);

@@ -125,10 +125,12 @@ def test_block_summary_exact(L, B, d, proj):
                                       (3000, 70)])
 def test_select_blocks_ties(n_rows, m, nq):
     # integer scores from a narrow range (many ties at the threshold, +0.0 and
-    # -0.0 among them). Few queries take the workgroup histogram select; from
-    # 1024 queries on, one wave per query up to 1024 candidates, 16 waves and
-    # a union of their kept candidates beyond (the histogram select when the
-    # union would not fit). Exact sets against the oracle.
+    # -0.0 among them). Few queries take the workgroup histogram select (16
+    # waves with the lane-maximum bound beyond 4098 blocks when at most 32 are
+    # free: the (16384, 32) case); from 1024 queries on, one wave per query up
+    # to 1024 candidates, 16 waves and a union of their kept candidates beyond
+    # (the histogram select when the union would not fit). Exact sets against
+    # the oracle.
     B = 64
     log(f"case select_blocks n_rows={n_rows} m={m} nq={nq}")
     g = torch.Generator(device="cpu").manual_seed(n_rows * 131 + m)
@@ -146,6 +148,29 @@ def test_select_blocks_ties(n_rows, m, nq):
         ref = np.stack([O.select_blocks_for_query(sc[b, i].double().numpy(), int(pos[b, i]), B, m)
                         for i in rows])
         check_index_rows(out[b, rows], ref, f"select_blocks b={b}")
+
+
+@pytest.mark.parametrize("n_rows,m", [(4099, 20), (6000, 34), (16384, 32), (16384, 35)])
+def test_select_blocks_few_spread(n_rows, m):
+    # few queries, spread scores: beyond 4098 blocks with at most 32 free
+    # slots each of 16 waves keeps its best through the lane-maximum bound
+    # (survivors compacted in LDS), wave 0 the best of their union; m = 35
+    # is the first to take the histogram select again. Exact sets.
+    B = 64
+    log(f"case select_blocks_few_spread n_rows={n_rows} m={m}")
+    g = torch.Generator(device="cpu").manual_seed(n_rows * 7 + m)
+    nq = 6
+    sc = torch.randn(3, nq, n_rows, generator=g)
+    pos = torch.randint(0, n_rows * B, (3, nq), generator=g, dtype=torch.int32)
+    pos[:, 0] = n_rows * B - 1
+    pos[:, 1] = B * (m - 1)
+    pos[:, 2] = B * m
+    pos[:, 3] = B * (n_rows // 2) + 5
+    out = H.hisa_select_blocks(sc.to(DEV), pos.to(DEV), B, m).cpu().numpy()
+    for b in range(3):
+        ref = np.stack([O.select_blocks_for_query(sc[b, i].double().numpy(), int(pos[b, i]), B, m)
+                        for i in range(nq)])
+        check_index_rows(out[b], ref, f"select_blocks_few_spread b={b}")
 
 
 @pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
