@@ -851,6 +851,9 @@ __global__ __launch_bounds__(256) void hils_chunks_kernel(
 }
 
 // Split form, second kernel: one workgroup per pair, one thread per column.
+// The same arithmetic as hils_mix, in the same order, without its chain of
+// dependent loads: lane ci holds chunk ci's logit (m <= 64), read by every
+// wave at once, and the partials are loaded eight chunks at a time.
 template <int D>
 __global__ __launch_bounds__(D) void hils_merge_kernel(const float* __restrict__ ws_a,
                                                        const float* __restrict__ ws_r, int H,
@@ -859,8 +862,30 @@ __global__ __launch_bounds__(D) void hils_merge_kernel(const float* __restrict__
   const int bh = blockIdx.x;
   const int b = bh / H, h = bh % H;
   const int64_t base = static_cast<int64_t>(bh) * m;
-  out[b * os.b + h * os.h + threadIdx.x] =
-      f32_to_bf16(hils_mix<D>(ws_r + base, ws_a + base * D, m, threadIdx.x));
+  const int e = threadIdx.x, lane = lane_id();
+  const float lg = lane < m ? ws_r[base + lane] : -INFINITY;
+  const float mx = wave_max(lg);
+  const float* ac = ws_a + base * D + e;
+  float z = 0.0f, acc = 0.0f;
+  for (int c0 = 0; c0 < m; c0 += 8) {
+    float a[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = c0 + j < m ? ac[(c0 + j) * D] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int ci = c0 + j;
+      if (ci < m) {
+        const float l = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lg), ci));
+        if (l != -INFINITY) {
+          const float w = __expf(l - mx);
+          z += w;
+          acc = fmaf(w, a[j], acc);
+        }
+      }
+    }
+  }
+  out[b * os.b + h * os.h + e] = f32_to_bf16(z > 0.0f ? acc / z : 0.0f);
 }
 
 // the split form pays while the pairs leave most CUs idle
