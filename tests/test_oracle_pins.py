@@ -47,8 +47,11 @@ def test_golden_attention():
     np.testing.assert_allclose(lse, np.array(g["lse"]), rtol=0, atol=1e-12)
 
 
-def test_golden_hils():
-    g = json.load(open(GOLD))["hils"]
+@pytest.mark.parametrize("case", ["hils", "hils_scaled"])
+def test_golden_hils(case):
+    # "hils_scaled" has unequal chunk and token scales (0.5 and 2), so the
+    # chunk logit scale and the token logit scale are each pinned
+    g = json.load(open(GOLD))[case]
     K = np.array(g["K"])
     khat = O.block_summary(K, g["C"], proj=np.array(g["W"]))
     out, chosen = O.hils_decode_head(np.array(g["q"]), K, np.array(g["V"]), khat, g["t"],
