@@ -54,6 +54,20 @@ def parse():
                     help="only time the indexer (steps 1-4) for block sizes 64/128/256 and "
                          "several m on this workload, one JSON line each, with the share of "
                          "the flat indexer's tokens each keeps")
+    ap.add_argument("--attn-only", action="store_true",
+                    help="prefill: select the tokens once, then time only the sparse attention "
+                         "launch over all queries (for counter passes and kernel A/B runs)")
+    ap.add_argument("--gather-probe", action="store_true",
+                    help="prefill: time the gather-rate probe (the attention's row gathers "
+                         "alone) on the selected ids, on the same lists shifted to one hot "
+                         "set of rows, and on contiguous rows; one JSON line")
+    ap.add_argument("--write-counters", default="",
+                    help="only summarise rocprofv3 --pmc csv folders found under this folder "
+                         "(one per pass) into a markdown table (--counters-out)")
+    ap.add_argument("--counters-out", default="")
+    ap.add_argument("--counters-kernel", default="attn")
+    ap.add_argument("--counters-title", default="")
+    ap.add_argument("--counters-command", default="")
     ap.add_argument("--write-traffic", default="",
                     help="only summarise rocprofv3 byte counters found under this folder "
                          "(fetch/, write/, cfetch/, cwrite/) into the traffic record")
@@ -343,6 +357,191 @@ def bench_prefill(w, a, inp):
     return res
 
 
+def attn_table(w, inp):
+    """The K table the attention gathers from as [L, row] (batch 1), and its
+    row width in bytes: the 576-wide latent row, or one kv head's K row."""
+    k = inp["k"][0, :, 0, :]
+    return k, k.shape[-1] * k.element_size()
+
+
+def time_launch(fn, steps, warmup=1):
+    """Mean milliseconds of fn() over `steps` calls, HIP events on the current
+    stream (the one every binding call enqueues on)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(steps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def gather_ceiling(w, inp, ids, steps, configs=((4, 2), (8, 2), (4, 3), (8, 3))):
+    """Best time of the gather-rate probe over `configs` (waves, depth) on the
+    id lists the attention reads: the ceiling that gathering those rows alone
+    allows. Returns (ms, waves, depth)."""
+    import long_context_indexer_block_amd as H
+    table, row_bytes = attn_table(w, inp)
+    best = None
+    for wv, dp in configs:
+        ms = time_launch(lambda: H.hisa_gather_probe(table, ids, row_bytes, wv, dp), steps)
+        if best is None or ms < best[0]:
+            best = (ms, wv, dp)
+    return best
+
+
+def bench_attn_only(w, a, inp):
+    """Select the tokens once, then time the attention launch over all queries
+    alone (HIP events on its stream)."""
+    from long_context_indexer_block_amd.pipeline import HierPipeline
+    p = HierPipeline(inp["kidx"], inp["qidx"], inp["q_pos"], inp["q"], inp["k"], inp["v"], w.B,
+                     w.m, w.k, w.scale)
+    p.index()
+    ms = time_launch(p.attend, a.steps, a.warmup)
+    n_sel = int((p.token_idx >= 0).sum().item())
+    flop = 2.0 * n_sel * w.Hq * (w.Dk + w.Dv)
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"attn_only": w.name, "ms": ms, "tflops": tf, "frac_mfma": tf / PEAK_BF16_TFLOPS,
+            "kept_tokens": n_sel, "steps": a.steps, "warmup": a.warmup}
+
+
+def bench_gather_probe(w, a, inp):
+    """The gather-rate probe on three id sets of the workload's shape: the
+    ids the hierarchical selection keeps, the same count of rows that every
+    query shares (served from L2), and contiguous rows per query; the
+    attention launch on the kept ids timed beside them."""
+    import torch
+
+    import long_context_indexer_block_amd as H
+    from long_context_indexer_block_amd.pipeline import HierPipeline
+    p = HierPipeline(inp["kidx"], inp["qidx"], inp["q_pos"], inp["q"], inp["k"], inp["v"], w.B,
+                     w.m, w.k, w.scale)
+    p.index()
+    ids = p.token_idx[0].contiguous()
+    nq, topk = ids.shape
+    dev = ids.device
+    table, row_bytes = attn_table(w, inp)
+    hot = torch.arange(topk, dtype=torch.int32, device=dev).expand(nq, topk).contiguous()
+    seq = ((torch.arange(nq, dtype=torch.int64, device=dev)[:, None] * 97 +
+            torch.arange(topk, dtype=torch.int64, device=dev)[None]) % w.L).to(torch.int32)
+    rows_read = nq * (-(-topk // 32) * 32)
+    out = {"gather_probe": w.name, "row_bytes": row_bytes, "rows_per_launch": rows_read,
+           "bytes_per_launch": rows_read * row_bytes, "results": []}
+    for name, idset in (("selected", ids), ("hot_rows", hot), ("contiguous", seq)):
+        for wv, dp in ((4, 1), (4, 2), (4, 3), (4, 4), (8, 1), (8, 2), (8, 3)):
+            ms = time_launch(lambda: H.hisa_gather_probe(table, idset, row_bytes, wv, dp), a.steps)
+            out["results"].append({"ids": name, "waves": wv, "depth": dp, "ms": ms,
+                                   "GBps": rows_read * row_bytes / (ms * 1e-3) / 1e9})
+    ams = time_launch(p.attend, a.steps)
+    out["attention_ms"] = ams
+    # the attention kernels gather each kept token's K row and, unless V is
+    # the latent row itself, its V row as well
+    per_token = row_bytes if w.mla else row_bytes * 2
+    out["attention_gather_GBps"] = rows_read * per_token / (ams * 1e-3) / 1e9
+    return out
+
+
+N_XCD, N_CU, N_SIMD, CLOCK_GHZ = 8, 256, 1024, 2.4   # MI355X
+
+
+def write_counters(folder, out_path, kernel_sub, title="", command=""):
+    """Summarise rocprofv3 --pmc csv folders (one per pass, any names) for the
+    dispatches of kernels whose name holds `kernel_sub`, largest grid only:
+    the mean of every counter per dispatch and the figures derived from them.
+    GRBM_GUI_ACTIVE comes summed over the eight XCDs, so the kernel's cycles
+    are that / 8; MFMA busy is SQ_VALU_MFMA_BUSY_CYCLES per SIMD over those
+    cycles, and over the cycles of the datasheet clock (2.4 GHz) in the
+    dispatch's measured duration; LDS bank-conflict cycles are set against
+    the cycles the LDS was busy with indexed operations; L2 hit rate is
+    TCC_HIT / (TCC_HIT + TCC_MISS)."""
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(folder, "**", "*counter_collection.csv"),
+                             recursive=True))
+    if not files:
+        raise SystemExit(f"no counter csv under {folder}")
+    per = {}
+    dur = {}
+    for f in files:
+        rows = [r for r in csv.DictReader(open(f)) if kernel_sub in r["Kernel_Name"]]
+        if not rows:
+            continue
+        top = max(int(r.get("Grid_Size") or 0) for r in rows)
+        for r in rows:
+            if int(r.get("Grid_Size") or 0) != top:
+                continue
+            key = (r["Kernel_Name"].split("(")[0], top)
+            d = per.setdefault(key, {})
+            d.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            dur.setdefault(key, {})[(f, r["Dispatch_Id"])] = (
+                int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    lines = [f"# {title}", ""] if title else []
+    if command:
+        lines += ["Commands (repository root, each pass a run of its own):", "", "```",
+                  command.strip(), "```", ""]
+    for (name, grid), d in per.items():
+        avg = {c: sum(v) / len(v) for c, v in d.items()}
+        ds = list(dur[(name, grid)].values())
+        ns = sum(ds) / len(ds)
+        lines.append(f"## `{name}` (grid {grid:,} threads)\n")
+        lines.append(f"Mean dispatch duration under the counter runs: {ns / 1e6:.3f} ms "
+                     f"({len(ds)} dispatches).\n")
+        lines.append("| counter | mean per dispatch | dispatches |")
+        lines.append("|---|---|---|")
+        for c in sorted(avg):
+            lines.append(f"| {c} | {avg[c]:,.0f} | {len(d[c])} |")
+        der = []
+        gui = avg.get("GRBM_GUI_ACTIVE")
+        cyc = gui / N_XCD if gui else None
+        if cyc:
+            der.append(("kernel cycles (GRBM_GUI_ACTIVE / 8 XCDs)", f"{cyc:,.0f}"))
+            der.append(("clock implied (cycles / duration)", f"{cyc / ns:.3f} GHz"))
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+            busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / N_SIMD
+            der.append(("MFMA busy cycles per SIMD", f"{busy:,.0f}"))
+            if cyc:
+                der.append(("MFMA busy / kernel cycles", f"{busy / cyc:.3f}"))
+            der.append(("MFMA busy / (duration x 2.4 GHz): fraction of the datasheet peak",
+                        f"{busy / (ns * CLOCK_GHZ):.3f}"))
+        if "SQ_LDS_BANK_CONFLICT" in avg and avg.get("SQ_LDS_IDX_ACTIVE"):
+            der.append(("LDS bank-conflict cycles / LDS indexed-active cycles",
+                        f"{avg['SQ_LDS_BANK_CONFLICT'] / avg['SQ_LDS_IDX_ACTIVE']:.3f}"))
+        if "SQ_LDS_BANK_CONFLICT" in avg and avg.get("SQ_ACTIVE_INST_LDS"):
+            der.append(("LDS bank-conflict cycles / SQ_ACTIVE_INST_LDS",
+                        f"{avg['SQ_LDS_BANK_CONFLICT'] / avg['SQ_ACTIVE_INST_LDS']:.3f}"))
+        if cyc and "SQ_LDS_IDX_ACTIVE" in avg:
+            der.append(("LDS indexed-active cycles per CU / kernel cycles",
+                        f"{avg['SQ_LDS_IDX_ACTIVE'] / N_CU / cyc:.3f}"))
+        if "TCC_HIT_sum" in avg and "TCC_MISS_sum" in avg:
+            tot = avg["TCC_HIT_sum"] + avg["TCC_MISS_sum"]
+            if tot:
+                der.append(("L2 hit rate (TCC_HIT / (TCC_HIT + TCC_MISS))",
+                            f"{avg['TCC_HIT_sum'] / tot:.3f}"))
+        waves = grid / 64.0
+        for c in ("SQ_INSTS_LDS", "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_SALU"):
+            if c in avg:
+                der.append((f"{c} per wave", f"{avg[c] / waves:,.1f}"))
+        if "SQ_WAIT_INST_LDS" in avg and "SQ_WAVE_CYCLES" in avg and avg["SQ_WAVE_CYCLES"]:
+            der.append(("SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES (share of wave time waiting to "
+                        "issue LDS)", f"{avg['SQ_WAIT_INST_LDS'] / avg['SQ_WAVE_CYCLES']:.3f}"))
+        if der:
+            lines.append("")
+            lines.append("| derived | value |")
+            lines.append("|---|---|")
+            for k, v in der:
+                lines.append(f"| {k} | {v} |")
+        lines.append("")
+    text = "\n".join(lines)
+    if out_path:
+        with open(out_path, "w") as fh:
+            fh.write(text + "\n")
+    print(text)
+
+
 def bench_decode(w, a, inp):
     import torch
 
@@ -611,6 +810,10 @@ def main():
     if a.write_traffic:
         write_traffic(a.write_traffic)
         return
+    if a.write_counters:
+        write_counters(a.write_counters, a.counters_out, a.counters_kernel,
+                       a.counters_title, a.counters_command)
+        return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the path has no "
               "multi-GPU form", file=sys.stderr)
@@ -630,6 +833,12 @@ def main():
     torch.cuda.synchronize()
     if a.sweep:
         bench_sweep(w, a, inp)
+        return
+    if a.attn_only:
+        print(json.dumps(bench_attn_only(w, a, inp)), flush=True)
+        return
+    if a.gather_probe:
+        print(json.dumps(bench_gather_probe(w, a, inp)), flush=True)
         return
     if w.kind == "prefill":
         res = bench_prefill(w, a, inp)

@@ -189,9 +189,12 @@ size_t flat_indexer_topk_workspace_bytes(int batch, int nq, int L, int k);
  *   k    bf16 [batch][L][Hkv][Dk]   strides ks.
  *   v    bf16 [batch][L][Hkv][Dv]   strides vs; may alias k (the first Dv
  *        columns of a latent row, as in multi-head latent attention).
- *   token_idx int32 [batch][nq][topk]; entries < 0 are skipped; every entry
- *        must be < L.
- *   out  bf16 [batch][nq][Hq][Dv]   strides os.
+ *   token_idx int32 [batch][nq][topk]; entries outside [0, L) (the -1
+ *        padding, or any other out-of-range id) are skipped: they take no
+ *        part in the softmax and read no memory beyond the cache.
+ *   out  bf16 [batch][nq][Hq][Dv]   strides os; like q, k and v it must be
+ *        16-byte aligned with strides in multiples of 8 elements (the kernels
+ *        store whole 16-byte pieces), else HISA_ERR_SHAPE.
  *   lse  optional fp32 [batch][nq][Hq]: natural-log sum of exp(scale*q.k)
  *        over the kept tokens (-inf for an empty set, whose output is 0).
  *   workspace  optional device scratch of sparse_attn_fwd_workspace_bytes()
@@ -282,6 +285,27 @@ hisa_status_t hils_two_level_prefill_fwd(const void* q, hisa_strides_t qs, const
                                          size_t workspace_bytes, hisa_stream_t stream);
 size_t hils_two_level_prefill_fwd_workspace_bytes(int batch, int nq, int L, int H, int D, int C,
                                                   int m);
+
+/* Gather-rate probe: the memory side of sparse attention alone. For each of
+ * nq queries it streams the rows named by ids[q][0 .. topk) of a resident
+ * table into on-chip memory the way the attention kernels do (16-byte direct
+ * loads, 8 lanes per 128-byte line, one workgroup per query, queries dealt
+ * to the XCDs in contiguous ranges, `depth` tiles of 32 rows in flight per
+ * wave) and discards them. Its rate is the ceiling that gathering alone
+ * allows for those id lists; the attention over the selected tokens (HISA
+ * explainer 1.1) and the memory-bound token selection (explainer 1.3) are
+ * measured against it. Writes no memory.
+ *   table      device rows of row_stride_bytes (a multiple of 16, >= row_bytes),
+ *              n_rows of them, 16-byte aligned.
+ *   row_bytes  256 or 1152 (a 128-wide bf16 K row, or a 576-wide latent row).
+ *   ids        int32 [nq][topk], 1 <= topk <= 4096; ids outside [0, n_rows)
+ *              read row 0.
+ *   waves      4 or 8 waves per workgroup; depth 1 .. 4.
+ * HISA_ERR_NULL / _SHAPE / _UNSUPPORTED on bad arguments, HISA_ERR_HIP on a
+ * launch error. */
+hisa_status_t hisa_gather_probe(const void* table, int64_t row_stride_bytes, int row_bytes,
+                                int n_rows, const int32_t* ids, int nq, int topk, int waves,
+                                int depth, hisa_stream_t stream);
 
 #ifdef __cplusplus
 }

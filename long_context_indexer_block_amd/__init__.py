@@ -15,7 +15,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libhisa.so")
+# HISA_LIBRARY may name another build of the same library (the host-sanitized
+# test copy); by default the in-tree libhisa.so is loaded
+LIB_PATH = os.environ.get("HISA_LIBRARY") or os.path.join(_PKG, "libhisa.so")
 _lib = None
 
 
@@ -58,6 +60,7 @@ _SIGS = {
                                         _I, _I, _I, _I, _I, _I, _I, _I, _F, _F, _P, Strides, _P,
                                         _S, _P]),
     "hils_two_level_prefill_fwd_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I, _I]),
+    "hisa_gather_probe": (_I, [_P, ctypes.c_int64, _I, _I, _P, _I, _I, _I, _I, _P]),
 }
 EXPORTS = [n for n in _SIGS]
 
@@ -340,6 +343,23 @@ def hils_two_level_prefill_fwd(q, k, v, khat, chunk_idx, q_pos, C, scale_chunk, 
                                             _ptr(out), _str3(out, "bth"), _ptr(workspace), wsb,
                                             _stream()))
     return out
+
+
+# ----------------------------------------------------------------- measurement
+def hisa_gather_probe(table, ids, row_bytes, waves=4, depth=2):
+    """Stream the rows ids [nq, topk] name from table [n_rows, row_stride] (any
+    dtype, rows contiguous) into on-chip memory the way the attention kernels
+    gather them, and discard them (a gather-rate ceiling). Enqueued on the
+    current stream; returns nothing."""
+    if not table.is_cuda or not ids.is_cuda:
+        raise TypeError("table and ids must be device tensors")
+    if ids.dtype != torch.int32 or not ids.is_contiguous() or ids.dim() != 2:
+        raise ValueError("ids must be a contiguous int32 [nq, topk] tensor")
+    n_rows = table.shape[0]
+    stride = table.stride(0) * table.element_size()
+    nq, topk = ids.shape
+    _check(lib().hisa_gather_probe(_ptr(table), stride, int(row_bytes), n_rows, _ptr(ids), nq,
+                                   topk, int(waves), int(depth), _stream()))
 
 
 # ----------------------------------------------------------------- pipelines

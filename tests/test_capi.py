@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_match_header():
     names = _declared()
-    assert len(names) == 18
+    assert len(names) == 19
     lib = ctypes.CDLL(H.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -94,6 +94,73 @@ def test_attention_validation():
     b5 = list(base)
     b5[0] = NULL
     assert L.sparse_attn_fwd(*b5) == 1
+
+
+def test_attention_out_checks():
+    # the kernels store whole 16-byte pieces of out: a misaligned base or a
+    # stride that is not a multiple of 8 elements is rejected before launch
+    L = H.lib()
+    s = S(0, 128 * 16, 128)
+    args = [FAKE, s, FAKE, S(0, 128, 128), FAKE, S(0, 128, 128), 1, 4, 64, 16, 1, 128, 128,
+            FAKE, 8, 0.1]
+    assert L.sparse_attn_fwd(*args, ctypes.c_void_p(0x10008), s, NULL, NULL, 0, NULL) == 2
+    assert "out" in _err() and "aligned" in _err()
+    assert L.sparse_attn_fwd(*args, FAKE, S(0, 128 * 16, 132), NULL, NULL, 0, NULL) == 2
+    assert "out" in _err() and "strides" in _err()
+    assert L.sparse_attn_fwd(*args, FAKE, S(0, -2048, 128), NULL, NULL, 0, NULL) == 2
+    assert "out" in _err()
+    mla = [FAKE, S(0, 576 * 64, 576), FAKE, S(0, 576, 576), FAKE, S(0, 576, 576), 1, 4, 64, 64,
+           1, 576, 512, FAKE, 8, 0.1]
+    assert L.sparse_attn_fwd(*mla, ctypes.c_void_p(0x10004), S(0, 512 * 64, 512), NULL, NULL,
+                             0, NULL) == 2 and "out" in _err()
+
+
+def test_gather_probe_validation():
+    L = H.lib()
+    args = [FAKE, 1152, 1152, 1024, FAKE, 16, 2048, 4, 2, NULL]
+    a = list(args)
+    a[0] = NULL
+    assert L.hisa_gather_probe(*a) == 1
+    a = list(args)
+    a[2] = 512                                                       # row width
+    assert L.hisa_gather_probe(*a) == 3 and "row_bytes" in _err()
+    a = list(args)
+    a[7] = 6                                                         # waves
+    assert L.hisa_gather_probe(*a) == 3
+    a = list(args)
+    a[8] = 5                                                         # depth
+    assert L.hisa_gather_probe(*a) == 3
+    a = list(args)
+    a[6] = 4097                                                      # topk
+    assert L.hisa_gather_probe(*a) == 3
+    a = list(args)
+    a[1] = 1144                                                      # stride below the row
+    assert L.hisa_gather_probe(*a) == 2 and "row_stride" in _err()
+    a = list(args)
+    a[0] = ctypes.c_void_p(0x10004)
+    assert L.hisa_gather_probe(*a) == 2 and "aligned" in _err()
+
+
+NO_DEVICE = not os.path.exists("/dev/kfd")
+
+
+@pytest.mark.skipif(not NO_DEVICE, reason="launches with placeholder pointers: only on a host "
+                                          "without a GPU, where the launch itself must fail")
+def test_launch_error_is_hip_status():
+    # every check passes, so the call reaches the HIP launch, which fails for
+    # want of a device: HISA_ERR_HIP with HIP's own text, prefixed by the entry
+    L = H.lib()
+    st = L.hisa_gather_probe(FAKE, 1152, 1152, 1024, FAKE, 16, 2048, 4, 2, NULL)
+    assert st == 4
+    msg = _err()
+    assert msg.startswith("hisa_gather_probe: ") and len(msg) > len("hisa_gather_probe: ")
+    s = S(0, 128, 128)
+    st = L.sparse_attn_fwd(FAKE, s, FAKE, s, FAKE, s, 1, 4, 64, 1, 1, 128, 128, FAKE, 8, 0.1,
+                           FAKE, s, NULL, NULL, 0, NULL)
+    assert st == 4 and _err().startswith("sparse_attn_fwd: ")
+    # a later failing check replaces the text
+    assert L.hisa_gather_probe(NULL, 1152, 1152, 1024, FAKE, 16, 2048, 4, 2, NULL) == 1
+    assert "required" in _err()
 
 
 def test_attention_workspace():
