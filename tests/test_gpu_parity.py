@@ -287,6 +287,16 @@ def test_decode_session_grows_like_a_rebuild():
         assert torch.equal(s.split[:, :n], r.split), L
         assert torch.equal(s.block_idx, r.block_idx) and torch.equal(s.token_idx, r.token_idx), L
         assert torch.equal(s.out, r.out), L
+        # and against the oracle on the cache cut to L tokens
+        for b in range(w.batch):
+            kb = f64(kidx[b, :L])
+            bidx, _, tidx, _ = O.hier_query(f64(qidx[b, 0]), kb, O.block_summary(kb, w.B), L - 1,
+                                            w.B, w.m, w.k)
+            check_index_rows(s.block_idx[b].cpu().numpy(), bidx[None], f"session block_idx L={L}")
+            check_index_rows(s.token_idx[b].cpu().numpy(), tidx[None], f"session token_idx L={L}")
+            ro, _ = O.sparse_attention_for_query(f64(q[b, 0]), f64(k[b, :L]), f64(v[b, :L]), tidx,
+                                                 w.scale)
+            check_attention(s.out[b, 0].float().cpu().numpy(), ro, f"session attention L={L} b={b}")
     # the incrementally built rows against the oracle (integer keys: exact)
     for b in range(w.batch):
         ref = O.block_summary(f64(kidx[b]), w.B)
@@ -352,25 +362,142 @@ def test_workload_prefill_16k_mqa():
     _check_hier(w, inp, p, rows, what=w.name)
 
 
-def test_workload_prefill_64k_mla():
+def _rows_64k(w, slabs, n_total=4096, seed=0):
+    """Rows of the 64K check: every slab boundary (last row of a slab, first
+    of the next), the edge positions, the first and last two rows, and
+    seeded random rows up to n_total."""
+    nq = w.queries
+    sl = -(-nq // slabs)
+    rows = set()
+    for s0 in range(sl, nq, sl):
+        rows.update((s0 - 1, s0))
+    rows.update(p for p in sample_positions(w, 0) if p < nq)
+    rows.update((0, 1, nq - 2, nq - 1))
+    g = np.random.default_rng(seed)
+    while len(rows) < n_total:
+        rows.add(int(g.integers(0, nq)))
+    return sorted(rows)
+
+
+def _attn_rows_64k(w, slabs):
+    """Attention rows: slab boundaries, edges and seeded rows, 64 or more."""
+    nq = w.queries
+    sl = -(-nq // slabs)
+    rows = {0, 1, 127, 128, 2047, 2048, 8191, 8192, nq - 1}
+    rows.update(s0 for s0 in range(sl, nq, sl))
+    rows.update(s0 - 1 for s0 in range(sl, nq, sl))
+    g = np.random.default_rng(1)
+    while len(rows) < 72:
+        rows.add(int(g.integers(0, nq)))
+    return sorted(rows)
+
+
+@pytest.fixture(scope="module")
+def inputs_64k():
     w = WORKLOADS["prefill_64k_mla"]
-    log(f"case {w.name}")
     inp = make_inputs(w, DEV, seed=0)
-    p = _run_hier(w, inp)
-    rows = _rows(w, 24)
-    _check_hier(w, inp, p, rows, what=w.name)
+    torch.cuda.synchronize()
+    yield w, inp
+    del inp
+    torch.cuda.empty_cache()
+
+
+def test_workload_prefill_64k_mla_timed_step(inputs_64k):
+    # the step exactly as the benchmark times it: 16 query slabs, the block
+    # scores, block and token selection of slab i+1 on one stream while slab
+    # i attends on another (HierPipeline.run_overlapped, no scores, no LSE);
+    # block scores, block ids and token ids against the oracle bit for bit on
+    # 4096 rows (every slab boundary, the edges), attention on 72 rows
+    import oracle_pool as OP
+    w, inp = inputs_64k
+    slabs = 16
+    log(f"case {w.name} timed step, {slabs} overlapped slabs")
+    p = HierPipeline(inp["kidx"], inp["qidx"], inp["q_pos"], inp["q"], inp["k"], inp["v"], w.B,
+                     w.m, w.k, w.scale, overlap_slabs=slabs)
+    assert len(p.slabs) == slabs
+    p.run_overlapped()
+    p.run_overlapped()
+    torch.cuda.synchronize()
+    rows = _rows_64k(w, slabs)
+    arows = _attn_rows_64k(w, slabs)
+    ridx = torch.tensor(rows, device=DEV)
+    bs = p.block_scores[0, ridx].cpu().numpy()
+    bi = p.block_idx[0, ridx].cpu().numpy()
+    ti_all = p.token_idx.clone()
+    out_all = p.out.clone()
+    ti = ti_all[0, ridx].cpu().numpy()
+    aidx = torch.tensor(arows, device=DEV)
+    go = out_all[0, aidx].float().cpu().numpy()
+    # the one-stream step on the same buffers gives the same ids and outputs
+    p.run()
+    torch.cuda.synchronize()
+    assert torch.equal(p.token_idx, ti_all) and torch.equal(p.out, out_all)
+    kidx = inp["kidx"][0].float().cpu().numpy()
+    qidx = inp["qidx"][0].float().cpu().numpy()
+    pos = inp["q_pos"][0].cpu().numpy()
+    log(f"  oracle on {len(rows)} rows, {OP.workers()} workers")
+    ref = OP.hier_rows(kidx, qidx, pos, w.B, w.m, w.k, rows)
+    check_score_rows(bs, np.stack([ref[r][1] for r in rows]), "64k timed block scores")
+    check_index_rows(bi, np.stack([ref[r][0] for r in rows]), "64k timed block_idx")
+    check_index_rows(ti, np.stack([ref[r][2] for r in rows]), "64k timed token_idx")
+    # attention rows on the oracle's own token lists
+    K = inp["k"][0].float().cpu().numpy()
+    V = inp["v"][0].float().cpu().numpy()
+    qa = inp["q"][0, aidx].float().cpu().numpy()
+    jobs = [(r, qa[i], ref[r][2] if r in ref else None) for i, r in enumerate(arows)]
+    missing = [r for r in arows if r not in ref]
+    if missing:
+        extra = OP.hier_rows(kidx, qidx, pos, w.B, w.m, w.k, missing)
+        jobs = [(r, q, t if t is not None else extra[r][2]) for r, q, t in jobs]
+    log(f"  oracle attention on {len(arows)} rows")
+    att = OP.attend_rows(K, V, w.scale, jobs)
+    mx, mean, rel = check_attention(go, np.stack([att[r][0] for r in arows]), "64k timed attention")
+    log(f"  64k timed step: attention max-abs {mx:.2e} mean-abs {mean:.2e} rel {rel:.2e}")
+
+
+def test_workload_prefill_64k_mla_scores(inputs_64k):
+    # the same overlapped step asked for its token scores: scores bit for bit
+    # on the same 4096 rows
+    import oracle_pool as OP
+    w, inp = inputs_64k
+    log(f"case {w.name} overlapped step with token scores")
+    p = HierPipeline(inp["kidx"], inp["qidx"], inp["q_pos"], inp["q"], inp["k"], inp["v"], w.B,
+                     w.m, w.k, w.scale, want_scores=True, overlap_slabs=16)
+    p.run_overlapped()
+    torch.cuda.synchronize()
+    rows = _rows_64k(w, 16)
+    ridx = torch.tensor(rows, device=DEV)
+    ti = p.token_idx[0, ridx].cpu().numpy()
+    ts = p.token_scores[0, ridx].cpu().numpy()
     del p
     torch.cuda.empty_cache()
+    ref = OP.hier_rows(inp["kidx"][0].float().cpu().numpy(), inp["qidx"][0].float().cpu().numpy(),
+                       inp["q_pos"][0].cpu().numpy(), w.B, w.m, w.k, rows)
+    check_index_rows(ti, np.stack([ref[r][2] for r in rows]), "64k token_idx (scores run)")
+    check_score_rows(ts, np.stack([ref[r][3] for r in rows]), "64k token scores")
+
+
+def test_workload_prefill_64k_flat(inputs_64k):
+    # the flat comparison path as the benchmark runs it (16 overlapped
+    # slabs), ids and scores on the same 4096 rows
+    import oracle_pool as OP
+    w, inp = inputs_64k
+    log(f"case {w.name} flat path, overlapped slabs")
     f = FlatPipeline(inp["kidx"], inp["qidx"], inp["q_pos"], inp["q"], inp["k"], inp["v"], w.k,
-                     w.scale, want_scores=True)
-    f.run()
+                     w.scale, want_scores=True, overlap_slabs=16)
+    f.run_overlapped()
     torch.cuda.synchronize()
-    so = SeqOracle(inp, 0, w.B, with_attention=False)
-    frows = rows[:12] + rows[-4:]
-    ref = [so.flat(r, w.k) for r in frows]
-    check_index_rows(f.token_idx[0, frows].cpu().numpy(), np.stack([x[0] for x in ref]), "flat 64k")
-    check_score_rows(f.token_scores[0, frows].cpu().numpy(), np.stack([x[1] for x in ref]),
-                     "flat 64k scores")
+    rows = _rows_64k(w, 16)
+    ridx = torch.tensor(rows, device=DEV)
+    ti = f.token_idx[0, ridx].cpu().numpy()
+    ts = f.token_scores[0, ridx].cpu().numpy()
+    del f
+    torch.cuda.empty_cache()
+    log(f"  flat oracle on {len(rows)} rows, {OP.workers()} workers")
+    ref = OP.flat_rows(inp["kidx"][0].float().cpu().numpy(), inp["qidx"][0].float().cpu().numpy(),
+                       inp["q_pos"][0].cpu().numpy(), w.k, rows)
+    check_index_rows(ti, np.stack([ref[r][0] for r in rows]), "flat 64k token_idx")
+    check_score_rows(ts, np.stack([ref[r][1] for r in rows]), "flat 64k scores")
 
 
 def test_workload_decode_128k_b64():
@@ -381,21 +508,21 @@ def test_workload_decode_128k_b64():
     bi, ti, ts = (p.block_idx.cpu().numpy(), p.token_idx.cpu().numpy(),
                   p.token_scores.cpu().numpy())
     for b in range(w.batch):
-        so = SeqOracle(inp, b, w.B, with_attention=(b % 8 == 0))
+        so = SeqOracle(inp, b, w.B)
         bidx, _, tidx, tval = so.hier(0, w.m, w.k)
         check_index_rows(bi[b, :1], bidx[None], f"decode block_idx b={b}")
         check_index_rows(ti[b, :1], tidx[None], f"decode token_idx b={b}")
         check_score_rows(ts[b, :1], tval[None], f"decode token scores b={b}")
-        if b % 8 == 0:
-            ro, _ = so.attend(0, tidx, w.scale)
-            check_attention(p.out[b, 0].float().cpu().numpy(), ro, f"decode attention b={b}")
+        ro, _ = so.attend(0, tidx, w.scale)
+        check_attention(p.out[b, 0].float().cpu().numpy(), ro, f"decode attention b={b}")
 
 
-def _hils_check(w, exact, split=True):
+def _hils_check(w, exact, split=True, scales=None):
     inp = make_inputs(w, DEV, seed=0)
     C, m = w.B, w.m
     sc = 1.0 / math.sqrt(w.Dk)
-    hd = HilsDecode(inp["q"], inp["k"], inp["v"], inp["w_proj"], C, m, sc, sc)
+    s_chunk, s_token = (sc, sc) if scales is None else scales
+    hd = HilsDecode(inp["q"], inp["k"], inp["v"], inp["w_proj"], C, m, s_chunk, s_token)
     # few (sequence, head) pairs: the chunks are spread over workgroups and
     # merged, unless the workspace is withheld
     assert hd.ws is not None
@@ -414,7 +541,7 @@ def _hils_check(w, exact, split=True):
             V = f64(inp["v"][b, :, h])
             q = f64(inp["q"][b, h])
             khat = O.block_summary(K, C, proj=Wp)
-            ref_out, ref_idx = O.hils_decode_head(q, K, V, khat, t, C, m, sc, sc)
+            ref_out, ref_idx = O.hils_decode_head(q, K, V, khat, t, C, m, s_chunk, s_token)
             if exact:
                 check_index_rows(got_idx[b, h:h + 1], ref_idx[None],
                                  f"hils int chunk_idx b={b} h={h}")
@@ -438,7 +565,11 @@ def _hils_check(w, exact, split=True):
                 bound = 4 * 2.0 ** -24 * w.Dk * 2 * np.abs(khat[order[m - 3:m - 1]] * q).sum()
                 assert gap <= bound, f"hils b={b} h={h}: chunk sets differ with gap {gap} > {bound}"
                 excluded += 1
-                continue
+                # the output is still checked: the oracle's two-level combine
+                # over the chunk set the GPU chose
+                gi = got_idx[b, h]
+                logits = [s_chunk * float(khat[c] @ q) if c >= 0 else 0.0 for c in gi]
+                ref_out = O.hils_combine(q, K, V, gi, logits, t, C, s_token)
             check_attention(outs[b, h:h + 1], ref_out[None], f"hils out b={b} h={h}")
     log(f"  hils exact={exact}: heads excluded as near-ties: {excluded}")
     return excluded
@@ -464,6 +595,15 @@ def test_hils_small(w, split):
     assert _hils_check(w, exact=True, split=split) == 0
 
 
+@pytest.mark.parametrize("split", [True, False], ids=["split", "one_workgroup_per_pair"])
+def test_hils_unequal_scales(split):
+    # chunk-logit and token-logit scales that differ (0.5 and 0.125): a kernel
+    # that dropped or swapped either would leave the tolerance
+    w = HILS_SMALL[0]
+    log(f"case hils unequal scales {w} split={split}")
+    assert _hils_check(w, exact=True, split=split, scales=(0.5, 0.125)) == 0
+
+
 def test_workload_hils_decode_int_twin():
     w = WORKLOADS["hils_decode_1m"].with_(int_mode=True)
     log(f"case hils int twin {w}")
@@ -478,7 +618,7 @@ def test_workload_hils_decode_1m():
 
 # ---------------------------------------------------------------- two-level prefill
 def _hils_prefill_check(w, exact, positions=None, heads=None, bucketed=True, subset=False,
-                        slab=65536):
+                        slab=65536, scales=None):
     """Run the causal two-level prefill of workload w on the GPU and check the
     queries at `positions` (default: all) of `heads` (default: all) against
     the oracle's decode of the tokens up to each query. bucketed=False runs
@@ -487,13 +627,15 @@ def _hils_prefill_check(w, exact, positions=None, heads=None, bucketed=True, sub
     inp = make_inputs(w, DEV, seed=0)
     C, m, nq = w.B, w.m, w.queries
     sc = 1.0 / math.sqrt(w.Dk)
+    s_chunk, s_token = (sc, sc) if scales is None else scales
     first = w.L - nq
     rows = list(range(nq)) if positions is None else [t - first for t in positions]
     ridx = torch.tensor(rows, dtype=torch.long, device=DEV)
     q_in, pos_in = inp["q"], inp["q_pos"]
     if subset:
         q_in, pos_in = q_in[:, ridx].contiguous(), pos_in[:, ridx].contiguous()
-    hp = HilsPrefill(q_in, inp["k"], inp["v"], inp["w_proj"], pos_in, C, m, sc, sc, slab=slab)
+    hp = HilsPrefill(q_in, inp["k"], inp["v"], inp["w_proj"], pos_in, C, m, s_chunk, s_token,
+                     slab=slab)
     assert hp.ws is not None
     if not bucketed:
         hp.ws = None
@@ -515,7 +657,8 @@ def _hils_prefill_check(w, exact, positions=None, heads=None, bucketed=True, sub
             for r, i in enumerate(rows):
                 t = int(qpos[b, i])
                 q = f64(qs[b, r, h])
-                ref_out, ref_idx = O.hils_prefill_query(q, K, V, Wp, khat, t, C, m, sc, sc)
+                ref_out, ref_idx = O.hils_prefill_query(q, K, V, Wp, khat, t, C, m, s_chunk,
+                                                        s_token)
                 if not np.array_equal(got_idx[b, h, r], ref_idx):
                     assert not exact, (f"hils prefill chunk_idx b={b} h={h} t={t}: gpu "
                                        f"{got_idx[b, h, r].tolist()} ref {ref_idx.tolist()}")
@@ -563,6 +706,14 @@ HILS_PREFILL_SMALL = [
 def test_hils_prefill_small(w, bucketed):
     log(f"case hils prefill small {w} bucketed={bucketed}")
     assert _hils_prefill_check(w, exact=True, bucketed=bucketed) == 0
+
+
+@pytest.mark.parametrize("bucketed", [True, False], ids=["bucketed", "per_query"])
+def test_hils_prefill_unequal_scales(bucketed):
+    # chunk-logit scale 0.5, token-logit scale 0.125 on every position
+    w = HILS_PREFILL_SMALL[0]
+    log(f"case hils prefill unequal scales {w} bucketed={bucketed}")
+    assert _hils_prefill_check(w, exact=True, bucketed=bucketed, scales=(0.5, 0.125)) == 0
 
 
 def test_hils_prefill_slabs():
