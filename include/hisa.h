@@ -160,6 +160,27 @@ hisa_status_t hisa_token_select(const void* qidx, hisa_strides_t qs, const void*
                                 size_t workspace_bytes, hisa_stream_t stream);
 size_t hisa_token_select_workspace_bytes(int batch, int nq, int L, int B, int m, int k);
 
+/* hisa_token_select without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation. Same arguments (less the workspace), checks and
+ * results as hisa_token_select. Its scratch is one fixed array of
+ * HISA_NOALLOC_SCRATCH_BYTES in device memory that the library holds on every
+ * GPU it runs on until the process ends; the array of the current device is
+ * used (the stream must belong to that device). Shapes whose
+ * hisa_token_select_workspace_bytes() exceed HISA_NOALLOC_SCRATCH_BYTES (the
+ * decode and small-prefill shapes fit; a 16K-query prefill does not) return
+ * HISA_ERR_UNSUPPORTED. Every call on a GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (different streams, or threads without ordering)
+ * race and their results are undefined; calls in stream order are safe (each
+ * clears what it needs). Calls no allocating routine; the first call on a
+ * device looks up the array's device address (HISA_ERR_HIP if that fails). */
+#define HISA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+hisa_status_t hisa_token_select_noalloc(const void* qidx, hisa_strides_t qs, const void* kidx,
+                                        hisa_strides_t ks, const int32_t* q_pos,
+                                        const int32_t* block_idx, int batch, int nq, int L, int d,
+                                        int B, int m, int k, int32_t* token_idx,
+                                        float* token_scores, hisa_stream_t stream);
+
 /* Runtime policy (HISA explainer 1.3 item 3, the adaptive mechanism, and
  * 3.2 item 2, the dynamic number of kept blocks; HISA news article: short
  * texts fall back to the original indexer). For a sequence of L keys and

@@ -46,6 +46,8 @@ _SIGS = {
     "hisa_token_select": (_I, [_P, Strides, _P, Strides, _P, _P, _I, _I, _I, _I, _I, _I, _I,
                                _P, _P, _P, _S, _P]),
     "hisa_token_select_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I]),
+    "hisa_token_select_noalloc": (_I, [_P, Strides, _P, Strides, _P, _P, _I, _I, _I, _I, _I, _I,
+                                       _I, _P, _P, _P]),
     "flat_indexer_topk": (_I, [_P, Strides, _P, Strides, _P, _I, _I, _I, _I, _I, _P, _P, _P, _S,
                                _P]),
     "flat_indexer_topk_workspace_bytes": (_S, [_I, _I, _I, _I]),
@@ -215,6 +217,25 @@ def hisa_token_select(qidx, kidx, q_pos, block_idx, B, k, token_idx=None, token_
                                    _ptr(q_pos), _ptr(block_idx), b, nq, L, d, B, m, k,
                                    _ptr(token_idx), _ptr(token_scores), _ptr(ws), ws.numel(),
                                    _stream()))
+    return token_idx, token_scores
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def hisa_token_select_noalloc(qidx, kidx, q_pos, block_idx, B, k, token_idx, token_scores=None):
+    """hisa_token_select with the library's fixed scratch instead of a
+    workspace: nothing is allocated (token_idx, and token_scores if wanted,
+    are caller-provided)."""
+    _need(qidx, torch.bfloat16, "qidx")
+    _need(kidx, torch.bfloat16, "kidx")
+    b, nq, d = qidx.shape
+    L = kidx.shape[1]
+    m = block_idx.shape[-1]
+    _check(lib().hisa_token_select_noalloc(_ptr(qidx), _str3(qidx, "bt"), _ptr(kidx),
+                                           _str3(kidx, "bt"), _ptr(q_pos), _ptr(block_idx), b, nq,
+                                           L, d, B, m, k, _ptr(token_idx), _ptr(token_scores),
+                                           _stream()))
     return token_idx, token_scores
 
 

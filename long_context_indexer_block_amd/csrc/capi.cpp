@@ -222,6 +222,42 @@ hisa_status_t hisa_token_select(const void* qidx, hisa_strides_t qs, const void*
                     "hisa_token_select");
 }
 
+hisa_status_t hisa_token_select_noalloc(const void* qidx, hisa_strides_t qs, const void* kidx,
+                                        hisa_strides_t ks, const int32_t* q_pos,
+                                        const int32_t* block_idx, int batch, int nq, int L, int d,
+                                        int B, int m, int k, int32_t* token_idx,
+                                        float* token_scores, hisa_stream_t stream) {
+  static_assert(hisa::kNoallocScratchBytes == HISA_NOALLOC_SCRATCH_BYTES, "header limit");
+  CHECK(qidx && kidx && q_pos && block_idx && token_idx, HISA_ERR_NULL,
+        "qidx, kidx, q_pos, block_idx and token_idx are required");
+  CHECK(batch >= 1 && nq >= 1 && L >= 1, HISA_ERR_SHAPE, "batch=%d nq=%d L=%d must be >= 1",
+        batch, nq, L);
+  hisa_status_t st;
+  if ((st = check_d(d)) != HISA_OK) return st;
+  if ((st = check_block(B)) != HISA_OK) return st;
+  CHECK(m >= 2 && static_cast<long>(m) * B <= 16384, HISA_ERR_UNSUPPORTED,
+        "m=%d must be >= 2 with m*B <= 16384", m);
+  CHECK(k >= 1 && k <= 16384, HISA_ERR_UNSUPPORTED, "k=%d must be in [1, 16384]", k);
+  CHECK(static_cast<long long>(batch) * nq * m < 2147483647LL, HISA_ERR_UNSUPPORTED,
+        "batch*nq*m too large");
+  if ((st = check_bf16(qidx, qs, "qidx")) != HISA_OK) return st;
+  if ((st = check_bf16(kidx, ks, "kidx")) != HISA_OK) return st;
+  CHECK(aligned16(token_idx), HISA_ERR_SHAPE, "token_idx must be 16-byte aligned");
+  const size_t need = hisa::token_select_workspace(batch, nq, L, B, m, k);
+  CHECK(need <= hisa::kNoallocScratchBytes, HISA_ERR_UNSUPPORTED,
+        "this shape needs %zu bytes of scratch, above the fixed %zu of "
+        "hisa_token_select_noalloc (use hisa_token_select with a workspace)",
+        need, hisa::kNoallocScratchBytes);
+  void* ws = nullptr;
+  hisa_status_t hs = hip_status(hisa::noalloc_scratch(&ws), "hisa_token_select_noalloc scratch");
+  if (hs != HISA_OK) return hs;
+  return hip_status(hisa::launch_token_select(static_cast<const uint16_t*>(qidx), s3(qs),
+                                              static_cast<const uint16_t*>(kidx), s3(ks), q_pos,
+                                              block_idx, batch, nq, L, d, B, m, k, token_idx,
+                                              token_scores, ws, static_cast<hipStream_t>(stream)),
+                    "hisa_token_select_noalloc");
+}
+
 hisa_status_t hisa_auto_plan(int L, int B, int* hierarchical, int* m) {
   CHECK(hierarchical && m, HISA_ERR_NULL, "hierarchical and m are required");
   CHECK(L >= 1, HISA_ERR_SHAPE, "L=%d must be >= 1", L);

@@ -29,6 +29,10 @@ hipError_t launch_token_select(const uint16_t* qidx, Str3 qs, const uint16_t* ki
                               const int32_t* q_pos, const int32_t* block_idx, int batch, int nq,
                               int L, int d, int B, int m, int k, int32_t* token_idx,
                               float* token_scores, void* ws, hipStream_t s);
+// the allocation-free token selection: the device address of the fixed
+// scratch array on the current device (looked up on the first call there)
+constexpr size_t kNoallocScratchBytes = static_cast<size_t>(64) << 20;
+hipError_t noalloc_scratch(void** ptr);
 size_t flat_workspace(int batch, int nq, int L, int k);
 hipError_t launch_flat_topk(const uint16_t* qidx, Str3 qs, const uint16_t* kidx, Str3 ks,
                             const int32_t* q_pos, int batch, int nq, int L, int d, int k,

@@ -12,6 +12,7 @@
 // [query][slot][B] whose position order is ascending token id, and one
 // workgroup per query then selects the top k from it.
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 #include "internal.h"
@@ -65,6 +66,33 @@ size_t token_select_workspace(int batch, int nq, int L, int B, int m, int /*k*/)
   size_t bytes = 0;
   carve(nullptr, batch, nq, L, B, m, &bytes);
   return bytes;
+}
+
+// ------------------------------------------------------------ fixed scratch
+// The scratch of the allocation-free token selection: one array in device
+// memory per GPU, held from the library's load on that GPU until the process
+// ends. In host code `scratch` only names the symbol; its device address on
+// each GPU comes from hipGetSymbolAddress and is the only form passed on.
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    // once per device, with that device current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 // ------------------------------------------------------------ pair buckets

@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_match_header():
     names = _declared()
-    assert len(names) == 19
+    assert len(names) == 20
     lib = ctypes.CDLL(H.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -161,6 +161,25 @@ def test_launch_error_is_hip_status():
     # a later failing check replaces the text
     assert L.hisa_gather_probe(NULL, 1152, 1152, 1024, FAKE, 16, 2048, 4, 2, NULL) == 1
     assert "required" in _err()
+
+
+def test_token_select_noalloc_limits():
+    # the allocation-free form: same checks as the workspace form, and shapes
+    # whose scratch exceeds the fixed array are rejected before any HIP call
+    L = H.lib()
+    args = [FAKE, S(0, 128, 0), FAKE, S(0, 128, 0), FAKE, FAKE, 1, 16384, 16384, 128, 128, 32,
+            2048, FAKE, NULL, NULL]
+    assert L.hisa_token_select_workspace_bytes(1, 16384, 16384, 128, 32, 2048) > 64 << 20
+    assert L.hisa_token_select_noalloc(*args) == 3 and "scratch" in _err()
+    a = list(args)
+    a[13] = NULL
+    assert L.hisa_token_select_noalloc(*a) == 1
+    a = list(args)
+    a[11] = 1                                                        # m < 2
+    assert L.hisa_token_select_noalloc(*a) == 3
+    a = list(args)
+    a[13] = ctypes.c_void_p(0x10004)                                 # token_idx alignment
+    assert L.hisa_token_select_noalloc(*a) == 2
 
 
 def test_attention_workspace():
