@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--attn-only", action="store_true",
                     help="prefill: select the tokens once, then time only the sparse attention "
                          "launch over all queries (for counter passes and kernel A/B runs)")
+    ap.add_argument("--attn-ids", default="selected", choices=["selected", "hot"],
+                    help="--attn-only: the selected ids, or every query reading the same "
+                         "rows 0..k-1 (all served from L2: the kernel's own ceiling)")
     ap.add_argument("--gather-probe", action="store_true",
                     help="prefill: time the gather-rate probe (the attention's row gathers "
                          "alone) on the selected ids, on the same lists shifted to one hot "
@@ -388,7 +391,7 @@ def gather_ceiling(w, inp, ids, steps, configs=((4, 2), (8, 2), (4, 3), (8, 3)))
     table, row_bytes = attn_table(w, inp)
     best = None
     for wv, dp in configs:
-        ms = time_launch(lambda: H.hisa_gather_probe(table, ids, row_bytes, wv, dp), steps)
+        ms = time_launch(lambda: H.hisa_gather_probe(table, ids, row_bytes, wv, dp, 0), steps)
         if best is None or ms < best[0]:
             best = (ms, wv, dp)
     return best
@@ -401,19 +404,28 @@ def bench_attn_only(w, a, inp):
     p = HierPipeline(inp["kidx"], inp["qidx"], inp["q_pos"], inp["q"], inp["k"], inp["v"], w.B,
                      w.m, w.k, w.scale)
     p.index()
+    if a.attn_ids == "hot":
+        import torch
+        nq, k = p.token_idx.shape[1], p.token_idx.shape[2]
+        p.token_idx.copy_(torch.arange(k, dtype=torch.int32, device=p.token_idx.device)
+                          .expand_as(p.token_idx))
     ms = time_launch(p.attend, a.steps, a.warmup)
     n_sel = int((p.token_idx >= 0).sum().item())
     flop = 2.0 * n_sel * w.Hq * (w.Dk + w.Dv)
     tf = flop / (ms * 1e-3) / 1e12
-    return {"attn_only": w.name, "ms": ms, "tflops": tf, "frac_mfma": tf / PEAK_BF16_TFLOPS,
+    return {"attn_only": w.name, "ids": a.attn_ids, "ms": ms, "tflops": tf,
+            "frac_mfma": tf / PEAK_BF16_TFLOPS,
             "kept_tokens": n_sel, "steps": a.steps, "warmup": a.warmup}
 
 
 def bench_gather_probe(w, a, inp):
-    """The gather-rate probe on three id sets of the workload's shape: the
-    ids the hierarchical selection keeps, the same count of rows that every
-    query shares (served from L2), and contiguous rows per query; the
-    attention launch on the kept ids timed beside them."""
+    """The gather-rate probe on id sets of the workload's shape: the ids the
+    hierarchical selection keeps (also read in a clock-rotated order, see
+    hisa_gather_probe), the same count of rows shared by every query (served
+    from L2), contiguous rows per query, uniformly random rows of the table
+    (no sharing between neighbouring queries), and uniformly random rows of a
+    4 GB table (beyond the last-level cache); the attention launch on the kept
+    ids timed beside them."""
     import torch
 
     import long_context_indexer_block_amd as H
@@ -425,17 +437,29 @@ def bench_gather_probe(w, a, inp):
     nq, topk = ids.shape
     dev = ids.device
     table, row_bytes = attn_table(w, inp)
+    g = torch.Generator(device=dev).manual_seed(5)
     hot = torch.arange(topk, dtype=torch.int32, device=dev).expand(nq, topk).contiguous()
     seq = ((torch.arange(nq, dtype=torch.int64, device=dev)[:, None] * 97 +
             torch.arange(topk, dtype=torch.int64, device=dev)[None]) % w.L).to(torch.int32)
+    uni = torch.randint(0, w.L, (nq, topk), generator=g, device=dev, dtype=torch.int32)
+    big_rows = (4 << 30) // row_bytes
+    big = torch.empty(big_rows, row_bytes // 2, dtype=torch.bfloat16, device=dev)
+    uni_big = torch.randint(0, big_rows, (nq, topk), generator=g, device=dev, dtype=torch.int32)
     rows_read = nq * (-(-topk // 32) * 32)
     out = {"gather_probe": w.name, "row_bytes": row_bytes, "rows_per_launch": rows_read,
            "bytes_per_launch": rows_read * row_bytes, "results": []}
-    for name, idset in (("selected", ids), ("hot_rows", hot), ("contiguous", seq)):
-        for wv, dp in ((4, 1), (4, 2), (4, 3), (4, 4), (8, 1), (8, 2), (8, 3)):
-            ms = time_launch(lambda: H.hisa_gather_probe(table, idset, row_bytes, wv, dp), a.steps)
-            out["results"].append({"ids": name, "waves": wv, "depth": dp, "ms": ms,
-                                   "GBps": rows_read * row_bytes / (ms * 1e-3) / 1e9})
+    grid = ((4, 1), (4, 2), (4, 3), (8, 1), (8, 2), (8, 3))
+    runs = [("selected", ids, table, wv, dp, 0) for wv, dp in grid]
+    runs += [("selected_rotated", ids, table, wv, dp, r) for wv, dp in ((4, 2), (8, 1))
+             for r in (32, 64, 128, 256)]
+    runs += [("hot_rows", hot, table, wv, dp, 0) for wv, dp in ((4, 2), (8, 1))]
+    runs += [("contiguous", seq, table, wv, dp, 0) for wv, dp in ((4, 2), (8, 1))]
+    runs += [("uniform", uni, table, wv, dp, 0) for wv, dp in ((4, 2), (8, 1), (8, 2))]
+    runs += [("uniform_4GB_table", uni_big, big, wv, dp, 0) for wv, dp in ((4, 2), (8, 1), (8, 2))]
+    for name, idset, tab, wv, dp, rot in runs:
+        ms = time_launch(lambda: H.hisa_gather_probe(tab, idset, row_bytes, wv, dp, rot), a.steps)
+        out["results"].append({"ids": name, "waves": wv, "depth": dp, "rot_ticks": rot, "ms": ms,
+                               "GBps": rows_read * row_bytes / (ms * 1e-3) / 1e9})
     ams = time_launch(p.attend, a.steps)
     out["attention_ms"] = ams
     # the attention kernels gather each kept token's K row and, unless V is

@@ -322,11 +322,15 @@ size_t hils_two_level_prefill_fwd_workspace_bytes(int batch, int nq, int L, int 
  *   ids        int32 [nq][topk], 1 <= topk <= 4096; ids outside [0, n_rows)
  *              read row 0.
  *   waves      4 or 8 waves per workgroup; depth 1 .. 4.
+ *   rot_ticks  0: every query reads its rows in list order. > 0: each query
+ *              starts at tile (t / rot_ticks) mod tiles, t the GPU's
+ *              constant-rate real-time counter when its workgroup starts, and
+ *              wraps around (the order of the rows read changes, not the set).
  * HISA_ERR_NULL / _SHAPE / _UNSUPPORTED on bad arguments, HISA_ERR_HIP on a
  * launch error. */
 hisa_status_t hisa_gather_probe(const void* table, int64_t row_stride_bytes, int row_bytes,
                                 int n_rows, const int32_t* ids, int nq, int topk, int waves,
-                                int depth, hisa_stream_t stream);
+                                int depth, int rot_ticks, hisa_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -62,7 +62,7 @@ _SIGS = {
                                         _I, _I, _I, _I, _I, _I, _I, _I, _F, _F, _P, Strides, _P,
                                         _S, _P]),
     "hils_two_level_prefill_fwd_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I, _I]),
-    "hisa_gather_probe": (_I, [_P, ctypes.c_int64, _I, _I, _P, _I, _I, _I, _I, _P]),
+    "hisa_gather_probe": (_I, [_P, ctypes.c_int64, _I, _I, _P, _I, _I, _I, _I, _I, _P]),
 }
 EXPORTS = [n for n in _SIGS]
 
@@ -367,7 +367,7 @@ def hils_two_level_prefill_fwd(q, k, v, khat, chunk_idx, q_pos, C, scale_chunk, 
 
 
 # ----------------------------------------------------------------- measurement
-def hisa_gather_probe(table, ids, row_bytes, waves=4, depth=2):
+def hisa_gather_probe(table, ids, row_bytes, waves=4, depth=2, rot_ticks=0):
     """Stream the rows ids [nq, topk] name from table [n_rows, row_stride] (any
     dtype, rows contiguous) into on-chip memory the way the attention kernels
     gather them, and discard them (a gather-rate ceiling). Enqueued on the
@@ -380,7 +380,7 @@ def hisa_gather_probe(table, ids, row_bytes, waves=4, depth=2):
     stride = table.stride(0) * table.element_size()
     nq, topk = ids.shape
     _check(lib().hisa_gather_probe(_ptr(table), stride, int(row_bytes), n_rows, _ptr(ids), nq,
-                                   topk, int(waves), int(depth), _stream()))
+                                   topk, int(waves), int(depth), int(rot_ticks), _stream()))
 
 
 # ----------------------------------------------------------------- pipelines

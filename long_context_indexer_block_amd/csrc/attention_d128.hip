@@ -110,6 +110,7 @@ struct Item {
   const uint16_t* vb;   // V rows of this kv head
   const int32_t* tix;   // this query's token ids
   int64_t kst, vst;     // row strides (elements)
+  uint32_t kbytes, vbytes;  // row strides in bytes (32-bit offset form)
   int topk, L, w;
 };
 
@@ -138,21 +139,37 @@ __device__ __forceinline__ int4 read_ids(const Item& it, int t, int l) {
 // lane l taking row 4u + l/16 and logical chunk (l%16) ^ swz(row), so 16
 // adjacent lanes read one 256-byte row. Returns the tile's valid-token mask
 // (bit r: token r of the tile is in the list and its id is in [0, L)).
+// OFF32: the row offsets fit 32 bits (the launch checks), so each address is
+// the wave's base plus one 24-bit multiply-add (the load takes the base from
+// scalar registers); otherwise they are formed in 64 bits.
+template <bool OFF32>
 __device__ __forceinline__ uint32_t gather(const Item& it, int t, uint4* kd, uint4* vd, int l) {
   const int4 ids = read_ids(it, t, l);
   const int g = l >> 4, p = l & 15;
   uint32_t mask = 0;
   const int idv[4] = {ids.x, ids.y, ids.z, ids.w};
+  const int left = it.topk - NT * t;  // rows of the tile inside the list
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int r = 4 * u + g;
-    const bool ok = NT * t + r < it.topk && static_cast<unsigned>(idv[u]) < static_cast<unsigned>(it.L);
+    const bool ok = r < left && static_cast<unsigned>(idv[u]) < static_cast<unsigned>(it.L);
     const int row = ok ? idv[u] : 0;
     const int c = p ^ swz(r);
-    __builtin_amdgcn_global_load_lds((glb_ptr)(it.kb + static_cast<int64_t>(row) * it.kst + 8 * c),
-                                     (lds_ptr)(kd + 64 * u), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((glb_ptr)(it.vb + static_cast<int64_t>(row) * it.vst + 8 * c),
-                                     (lds_ptr)(vd + 64 * u), 16, 0, 0);
+    if constexpr (OFF32) {
+      const uint32_t ko = __umul24(static_cast<uint32_t>(row), it.kbytes) + 16u * c;
+      const uint32_t vo = __umul24(static_cast<uint32_t>(row), it.vbytes) + 16u * c;
+      __builtin_amdgcn_global_load_lds(
+          (glb_ptr)(reinterpret_cast<const unsigned char*>(it.kb) + ko), (lds_ptr)(kd + 64 * u),
+          16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (glb_ptr)(reinterpret_cast<const unsigned char*>(it.vb) + vo), (lds_ptr)(vd + 64 * u),
+          16, 0, 0);
+    } else {
+      __builtin_amdgcn_global_load_lds((glb_ptr)(it.kb + static_cast<int64_t>(row) * it.kst + 8 * c),
+                                       (lds_ptr)(kd + 64 * u), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((glb_ptr)(it.vb + static_cast<int64_t>(row) * it.vst + 8 * c),
+                                       (lds_ptr)(vd + 64 * u), 16, 0, 0);
+    }
     const uint64_t b = __ballot(ok);
 #pragma unroll
     for (int gg = 0; gg < 4; ++gg)
@@ -210,9 +227,8 @@ __device__ __forceinline__ void tile(State& st, const Item& it, int t, float sca
 #pragma unroll
   for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(sv[e] + mneg);
   st.lsum += (p[0] + p[1]) + (p[2] + p[3]);
-  v4s pa;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) pa[e] = static_cast<short>(f32_to_bf16(p[e]));
+  const uint2 pp = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+  const v4s pa = __builtin_bit_cast(v4s, pp);
   // ---- O += P V: V^T fragment of dv block dvb: lane l (group g, sl = l%16)
   // addresses row 4g + sl/4, columns 16dvb + 4(sl%4) .. +3 and receives
   // column 16dvb + sl of rows 4g .. 4g+3
@@ -230,9 +246,9 @@ __device__ __forceinline__ void tile(State& st, const Item& it, int t, float sca
 
 // Iteration t: gather tile t+2 (and the ids of tile t+5), then tile t; wait
 // until tile t+1 has landed.
-template <int I>
+template <int I, bool OFF32>
 __device__ __forceinline__ void iter(State& st, const Item& it, int t, float scale_log2, int l) {
-  const uint32_t m2 = gather(it, t + 2, kbuf<I + 2>(it.w), vbuf<I + 2>(it.w), l);
+  const uint32_t m2 = gather<OFF32>(it, t + 2, kbuf<I + 2>(it.w), vbuf<I + 2>(it.w), l);
   ids_issue(it, t + 5, l);
   tile<I>(st, it, t, scale_log2, l);
   st.m0 = st.m1;
@@ -244,6 +260,7 @@ __device__ __forceinline__ void iter(State& st, const Item& it, int t, float sca
 
 using namespace d128;
 
+template <bool OFF32>
 __global__ __launch_bounds__(128) void sparse_attn_d128_kernel(
     const uint16_t* __restrict__ q, Str3 qs, const uint16_t* __restrict__ k, Str3 ks,
     const uint16_t* __restrict__ v, Str3 vs, int nq, int L, int Hkv, int G,
@@ -265,6 +282,8 @@ __global__ __launch_bounds__(128) void sparse_attn_d128_kernel(
   it.vb = v + b * vs.b + gk * vs.h;
   it.kst = ks.t;
   it.vst = vs.t;
+  it.kbytes = static_cast<uint32_t>(2 * ks.t);
+  it.vbytes = static_cast<uint32_t>(2 * vs.t);
   it.tix = token_idx + qrow * topk + tok0;
   it.topk = min(topk - tok0, split_tiles * NT);  // >= 1: no split is empty
   it.L = L;
@@ -289,14 +308,14 @@ __global__ __launch_bounds__(128) void sparse_attn_d128_kernel(
 #pragma unroll
   for (int t = 0; t < 5; ++t) ids_issue(it, t, l);
   __builtin_amdgcn_s_waitcnt(0x0070);  // Q and the ids of tiles 0..4
-  st.m0 = gather(it, 0, kbuf<0>(w), vbuf<0>(w), l);
-  st.m1 = gather(it, 1, kbuf<1>(w), vbuf<1>(w), l);
+  st.m0 = gather<OFF32>(it, 0, kbuf<0>(w), vbuf<0>(w), l);
+  st.m1 = gather<OFF32>(it, 1, kbuf<1>(w), vbuf<1>(w), l);
   __builtin_amdgcn_s_waitcnt(0x0078);  // vmcnt(8): tile 0 has landed
   int t = 0;
   for (; t + 3 <= nt3; t += 3) {
-    iter<0>(st, it, t, scale_log2, l);
-    iter<1>(st, it, t + 1, scale_log2, l);
-    iter<2>(st, it, t + 2, scale_log2, l);
+    iter<0, OFF32>(st, it, t, scale_log2, l);
+    iter<1, OFF32>(st, it, t + 1, scale_log2, l);
+    iter<2, OFF32>(st, it, t + 2, scale_log2, l);
   }
   __builtin_amdgcn_s_waitcnt(0x0070);  // the loads past the end
 
@@ -425,9 +444,21 @@ hipError_t launch_attn_d128(const uint16_t* q, Str3 qs, const uint16_t* k, Str3 
   }
   const int64_t waves = nitems * ns;
   const unsigned blocks = static_cast<unsigned>((waves + WAVES - 1) / WAVES);
-  hipLaunchKernelGGL(sparse_attn_d128_kernel, dim3(blocks), dim3(64 * WAVES), 0, s, q, qs, k, ks,
-                     v, vs, nq, L, Hkv, G, token_idx, topk, scale * 1.44269504088896340736f, out,
-                     os, lse, nitems, ns, tps, part_o, part_rl);
+  // 32-bit row offsets when every row of the cache lies within 4 GB of its
+  // base and the byte strides fit the 24-bit multiply
+  const int64_t span = (static_cast<int64_t>(L) - 1) * std::max(ks.t, vs.t) * 2 + 2 * D;
+  const bool off32 = span < (int64_t{1} << 32) && L < (1 << 24) && 2 * ks.t < (1 << 24) &&
+                     2 * vs.t < (1 << 24);
+  if (off32)
+    hipLaunchKernelGGL(sparse_attn_d128_kernel<true>, dim3(blocks), dim3(64 * WAVES), 0, s, q, qs,
+                       k, ks, v, vs, nq, L, Hkv, G, token_idx, topk,
+                       scale * 1.44269504088896340736f, out, os, lse, nitems, ns, tps, part_o,
+                       part_rl);
+  else
+    hipLaunchKernelGGL(sparse_attn_d128_kernel<false>, dim3(blocks), dim3(64 * WAVES), 0, s, q,
+                       qs, k, ks, v, vs, nq, L, Hkv, G, token_idx, topk,
+                       scale * 1.44269504088896340736f, out, os, lse, nitems, ns, tps, part_o,
+                       part_rl);
   if (ns > 1)
     hipLaunchKernelGGL(attn_d128_combine_kernel,
                        dim3(static_cast<unsigned>(nitems), static_cast<unsigned>((G + 1) / 2)),

@@ -43,6 +43,9 @@
 // The last two iterations gather nothing (there is no tile past the end),
 // and the value waves store the normalised O straight from registers, so a
 // workgroup's end overlaps little with the start of the next one on its CU.
+#include <algorithm>
+#include <cstdlib>
+
 #include "common.hpp"
 #include "internal.h"
 
@@ -57,6 +60,7 @@ constexpr int KS = DK / 32;     // k steps of S (18)
 constexpr int PCH = NT / 8;     // 16-byte chunks per P row (4)
 constexpr int NBLK = RCH / 8;   // 1 KB blocks per 8-row group (9)
 constexpr float kRedo = 64.0f;
+constexpr int kRotTicks = 96;   // clock ticks per tile of the rotated sweep (measured best)
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef __attribute__((address_space(1))) void* glb_ptr;
@@ -151,10 +155,11 @@ __device__ __forceinline__ int slot(int r, int c) {
 __device__ __forceinline__ int pslot(int h, int c) { return h * PCH + (c ^ ((h >> 2) & 3)); }
 
 // Ids outside [0, L) (padding, or past the end of the list) load row 0; such
-// tokens are masked out of the softmax.
-__device__ __forceinline__ void ids_issue(const int32_t* tix, int topk, int tile, int l) {
+// tokens are masked out of the softmax. Iteration `it` reads list tile
+// `tile` into ring slot it % 8.
+__device__ __forceinline__ void ids_issue(const int32_t* tix, int topk, int it, int tile, int l) {
   __builtin_amdgcn_global_load_lds((glb_ptr)(tix + min(tile * NT + (l & 31), topk - 1)),
-                                   (lds_ptr)(&g_ids[tile & 7][0]), 4, 0, 0);
+                                   (lds_ptr)(&g_ids[it & 7][0]), 4, 0, 0);
 }
 __device__ __forceinline__ uint32_t id_addr(int tile, int t) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int*)(&g_ids[tile & 7][t]);
@@ -201,6 +206,14 @@ struct Ctx {
   int topk, L;
   float scale_log2, inv_scale_log2;
   int w;
+  int first, ntiles;  // the list tile of iteration 0, the list's tiles
+  // list tile of iteration i: the tiles in cyclic order from `first`; the
+  // padding iterations past the list keep their own index (fully masked)
+  __device__ __forceinline__ int tile(int i) const {
+    if (i >= ntiles) return i;
+    const int t = first + i;
+    return t < ntiles ? t : t - ntiles;
+  }
 };
 
 // ------------------------------------------------------------- score waves
@@ -384,10 +397,10 @@ __device__ __forceinline__ int v_ids(VState& st, const Ctx& cx, int i, int q4, i
   const int4 fl = *reinterpret_cast<const int4*>(flagbuf<J>());
   const int2 id = read_ids(i + 2, 8 * q4 + (l >> 3), i + 1, l & 31);
   st.gsrc = gather_src(cx.kvb, cx.kst, cx.L, id.x, q4, l);
-  const uint32_t m = tile_mask(id.y, cx.topk, cx.L, i + 1, l);
+  const uint32_t m = tile_mask(id.y, cx.topk, cx.L, cx.tile(i + 1), l);
   if (q4 == 0 && l == 0) g_mask[(i + 1) & 1] = m;
   __builtin_amdgcn_sched_barrier(0);
-  ids_issue(cx.tix, cx.topk, i + 5, l);
+  ids_issue(cx.tix, cx.topk, i + 5, cx.tile(i + 5), l);
   __builtin_amdgcn_sched_barrier(0);
   return __builtin_amdgcn_readfirstlane(fl.x | fl.y | fl.z | fl.w);
 }
@@ -474,11 +487,13 @@ __device__ __forceinline__ void v_iter(VState& st, const Ctx& cx, int i, int l) 
   __builtin_amdgcn_s_barrier();
 }
 
+__shared__ int g_first;          // the list tile of iteration 0
+
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mla_attn_kernel(const uint16_t* __restrict__ q, Str3 qs, const uint16_t* __restrict__ kv,
                      Str3 ks, int nq, int L, int Hkv, const int32_t* __restrict__ token_idx,
                      int topk, float scale_log2, uint16_t* __restrict__ out, Str3 os,
-                     float* __restrict__ lse) {
+                     float* __restrict__ lse, int rot_ticks) {
   const int per = (nq + 7) / 8;
   const int qi = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
   if (qi >= nq) return;
@@ -489,6 +504,18 @@ void mla_attn_kernel(const uint16_t* __restrict__ q, Str3 qs, const uint16_t* __
   const int32_t* tix = token_idx + qrow * topk;
   const int ntiles = (topk + NT - 1) / NT;
   const int nt4 = (ntiles + 3) & ~3;  // tiles processed: a multiple of 4, extra ones fully masked
+  // Sweep order. With rot_ticks > 0 the query starts at list tile
+  // (clock / rot_ticks) mod ntiles and wraps around: every query in flight
+  // then reads the same part of its ascending list (the same region of the
+  // cache) at the same time, whenever it started, so rows that neighbouring
+  // queries share are fetched into L2 once. The softmax is the same for any
+  // order (the reference comes from the first tile processed); only the fp32
+  // summation order follows the clock. One clock read per workgroup, shared.
+  if (tid == 0)
+    g_first = rot_ticks > 0
+                  ? static_cast<int>((__builtin_amdgcn_s_memrealtime() / rot_ticks) % ntiles)
+                  : 0;
+  __syncthreads();
 
   Ctx cx;
   cx.kvb = kv + b * ks.b + g * ks.h;
@@ -499,6 +526,8 @@ void mla_attn_kernel(const uint16_t* __restrict__ q, Str3 qs, const uint16_t* __
   cx.scale_log2 = scale_log2;
   cx.inv_scale_log2 = 1.0f / scale_log2;
   cx.w = w;
+  cx.first = __builtin_amdgcn_readfirstlane(g_first);
+  cx.ntiles = ntiles;
 
   float* lsum_x = &g_mx[0][0];  // reused after the loop for the row sums
   if (w < 4) {
@@ -544,7 +573,7 @@ void mla_attn_kernel(const uint16_t* __restrict__ q, Str3 qs, const uint16_t* __
     const int q4 = w - 4;
     VState st;
 #pragma unroll
-    for (int t = 0; t < 5; ++t) ids_issue(tix, topk, t, l);
+    for (int t = 0; t < 5; ++t) ids_issue(tix, topk, t, cx.tile(t), l);
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
 #pragma unroll
@@ -555,7 +584,7 @@ void mla_attn_kernel(const uint16_t* __restrict__ q, Str3 qs, const uint16_t* __
     {
       const int2 id = read_ids(0, 8 * q4 + (l >> 3), 1, 8 * q4 + (l >> 3));
       const int2 idm = read_ids(0, l & 31, 0, l & 31);
-      const uint32_t m0 = tile_mask(idm.x, topk, L, 0, l);
+      const uint32_t m0 = tile_mask(idm.x, topk, L, cx.tile(0), l);
       if (q4 == 0 && l == 0) g_mask[0] = m0;
       const uint16_t* s0 = gather_src(cx.kvb, cx.kst, L, id.x, q4, l);
 #pragma unroll
@@ -624,13 +653,22 @@ void mla_attn_kernel(const uint16_t* __restrict__ q, Str3 qs, const uint16_t* __
 
 }  // namespace mla
 
+// The clock period (ticks of the 100 MHz real-time counter) per tile of the
+// rotated sweep; HISA_MLA_ROT_TICKS overrides it, 0 giving the list order
+// (bit-reproducible outputs).
+static int mla_rot_ticks() {
+  const char* e = getenv("HISA_MLA_ROT_TICKS");
+  if (e != nullptr && *e != '\0') return std::max(0, atoi(e));
+  return mla::kRotTicks;
+}
+
 hipError_t launch_mla_attn(const uint16_t* q, Str3 qs, const uint16_t* kv, Str3 ks, int batch,
                            int nq, int L, int Hkv, const int32_t* token_idx, int topk, float scale,
                            uint16_t* out, Str3 os, float* lse, hipStream_t s) {
   const int per = (nq + 7) / 8;
   hipLaunchKernelGGL(mla::mla_attn_kernel, dim3(8 * per, batch * Hkv), dim3(512), 0, s, q, qs,
                      kv, ks, nq, L, Hkv, token_idx, topk, scale * 1.44269504088896340736f, out,
-                     os, lse);
+                     os, lse, mla_rot_ticks());
   return hipGetLastError();
 }
 

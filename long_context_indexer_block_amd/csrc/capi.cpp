@@ -434,12 +434,13 @@ hisa_status_t hils_two_level_prefill_fwd(const void* q, hisa_strides_t qs, const
 
 hisa_status_t hisa_gather_probe(const void* table, int64_t row_stride_bytes, int row_bytes,
                                 int n_rows, const int32_t* ids, int nq, int topk, int waves,
-                                int depth, hisa_stream_t stream) {
+                                int depth, int rot_ticks, hisa_stream_t stream) {
   CHECK(table && ids, HISA_ERR_NULL, "table and ids are required");
   CHECK(row_bytes == 256 || row_bytes == 1152, HISA_ERR_UNSUPPORTED,
         "row_bytes=%d unsupported (256 or 1152)", row_bytes);
   CHECK(waves == 4 || waves == 8, HISA_ERR_UNSUPPORTED, "waves=%d unsupported (4 or 8)", waves);
   CHECK(depth >= 1 && depth <= 4, HISA_ERR_UNSUPPORTED, "depth=%d must be in [1, 4]", depth);
+  CHECK(rot_ticks >= 0, HISA_ERR_SHAPE, "rot_ticks=%d must be >= 0", rot_ticks);
   CHECK(n_rows >= 1 && nq >= 1 && topk >= 1, HISA_ERR_SHAPE, "sizes must be >= 1");
   CHECK(topk <= 4096, HISA_ERR_UNSUPPORTED, "topk=%d above 4096", topk);
   CHECK(nq <= 2147483647 - 7, HISA_ERR_UNSUPPORTED, "grid too large");
@@ -448,7 +449,7 @@ hisa_status_t hisa_gather_probe(const void* table, int64_t row_stride_bytes, int
         "row_stride_bytes=%lld must be a multiple of 16 and >= row_bytes",
         static_cast<long long>(row_stride_bytes));
   return hip_status(hisa::launch_gather_probe(table, row_stride_bytes, row_bytes, n_rows, ids, nq,
-                                              topk, waves, depth,
+                                              topk, waves, depth, rot_ticks,
                                               static_cast<hipStream_t>(stream)),
                     "hisa_gather_probe");
 }

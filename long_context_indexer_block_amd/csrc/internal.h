@@ -105,7 +105,7 @@ size_t hils_prefill_workspace(int batch, int nq, int L, int H, int D, int C, int
 // probe.hip: row_bytes 256 or 1152, waves 4 or 8, depth 1..4, topk <= 4096
 hipError_t launch_gather_probe(const void* table, int64_t row_stride, int row_bytes, int n_rows,
                                const int32_t* ids, int nq, int topk, int waves, int depth,
-                               hipStream_t s);
+                               int rot_ticks, hipStream_t s);
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 

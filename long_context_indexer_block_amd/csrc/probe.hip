@@ -28,16 +28,21 @@ constexpr int kMaxIds = 4096;  // ids per query staged in LDS
 // LPR: 128-byte lines per row; W: waves; DEPTH: tiles in flight per wave.
 // The ring holds min(DEPTH + 1, NBUF) tiles; nothing reads it, so a tile may
 // land on a slot whose previous loads are still in flight.
+// rot_ticks > 0: each query starts its sweep at tile (clock / rot_ticks) mod
+// ntiles and wraps around, the clock being the constant-rate real-time
+// counter read once per workgroup; queries running at the same time then read
+// the same region of their (ascending) lists together whatever their start.
 template <int LPR, int W, int DEPTH, int NBUF>
 __global__ __launch_bounds__(64 * W) void gather_probe_kernel(const uint8_t* __restrict__ table,
                                                               int64_t row_stride, int n_rows,
                                                               const int32_t* __restrict__ ids,
-                                                              int nq, int topk) {
+                                                              int nq, int topk, int rot_ticks) {
   constexpr int IPT = NT * LPR / 8;       // 1 KB load instructions per tile
   constexpr int PER = (IPT + W - 1) / W;  // per wave (the last wave may issue fewer)
   static_assert(DEPTH * PER <= 62, "load counter range");
   __shared__ uint4 ring[NBUF][IPT * 64];
   __shared__ int sid[kMaxIds];
+  __shared__ int s_first;
   const int per = (nq + 7) / 8;
   const int qi = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
   if (qi >= nq) return;
@@ -47,10 +52,16 @@ __global__ __launch_bounds__(64 * W) void gather_probe_kernel(const uint8_t* __r
     const int id = qids[i];
     sid[i] = static_cast<unsigned>(id) < static_cast<unsigned>(n_rows) ? id : 0;
   }
-  __syncthreads();
   const int ntiles = (topk + NT - 1) / NT;
-  for (int t = 0; t < ntiles; ++t) {
-    uint4* dst = ring[t % NBUF];
+  if (threadIdx.x == 0)
+    s_first = rot_ticks > 0
+                  ? static_cast<int>((__builtin_amdgcn_s_memrealtime() / rot_ticks) % ntiles)
+                  : 0;
+  __syncthreads();
+  const int first = s_first;
+  for (int i = 0; i < ntiles; ++i) {
+    const int t = first + i < ntiles ? first + i : first + i - ntiles;
+    uint4* dst = ring[i % NBUF];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int j = w + W * k;  // instruction of the tile
@@ -70,11 +81,11 @@ __global__ __launch_bounds__(64 * W) void gather_probe_kernel(const uint8_t* __r
 
 template <int LPR, int W, int DEPTH>
 hipError_t launch(const uint8_t* table, int64_t stride, int n_rows, const int32_t* ids, int nq,
-                  int topk, hipStream_t s) {
+                  int topk, int rot, hipStream_t s) {
   constexpr int NBUF = (LPR == 9) ? ((DEPTH + 1) < 3 ? (DEPTH + 1) : 3) : (DEPTH + 1);
   const int per = (nq + 7) / 8;
   hipLaunchKernelGGL((gather_probe_kernel<LPR, W, DEPTH, NBUF>), dim3(8 * per), dim3(64 * W), 0,
-                     s, table, stride, n_rows, ids, nq, topk);
+                     s, table, stride, n_rows, ids, nq, topk, rot);
   return hipGetLastError();
 }
 
@@ -83,30 +94,30 @@ hipError_t launch(const uint8_t* table, int64_t stride, int n_rows, const int32_
 // row_bytes 256 (two lines) or 1152 (nine lines); waves 4 or 8; depth 1..4
 hipError_t launch_gather_probe(const void* table, int64_t row_stride, int row_bytes, int n_rows,
                                const int32_t* ids, int nq, int topk, int waves, int depth,
-                               hipStream_t s) {
+                               int rot_ticks, hipStream_t s) {
   const uint8_t* t = static_cast<const uint8_t*>(table);
   if (row_bytes == 1152) {
     if (waves == 4) {
-      if (depth == 1) return probe::launch<9, 4, 1>(t, row_stride, n_rows, ids, nq, topk, s);
-      if (depth == 2) return probe::launch<9, 4, 2>(t, row_stride, n_rows, ids, nq, topk, s);
-      if (depth == 3) return probe::launch<9, 4, 3>(t, row_stride, n_rows, ids, nq, topk, s);
-      return probe::launch<9, 4, 4>(t, row_stride, n_rows, ids, nq, topk, s);
+      if (depth == 1) return probe::launch<9, 4, 1>(t, row_stride, n_rows, ids, nq, topk, rot_ticks, s);
+      if (depth == 2) return probe::launch<9, 4, 2>(t, row_stride, n_rows, ids, nq, topk, rot_ticks, s);
+      if (depth == 3) return probe::launch<9, 4, 3>(t, row_stride, n_rows, ids, nq, topk, rot_ticks, s);
+      return probe::launch<9, 4, 4>(t, row_stride, n_rows, ids, nq, topk, rot_ticks, s);
     }
-    if (depth == 1) return probe::launch<9, 8, 1>(t, row_stride, n_rows, ids, nq, topk, s);
-    if (depth == 2) return probe::launch<9, 8, 2>(t, row_stride, n_rows, ids, nq, topk, s);
-    if (depth == 3) return probe::launch<9, 8, 3>(t, row_stride, n_rows, ids, nq, topk, s);
-    return probe::launch<9, 8, 4>(t, row_stride, n_rows, ids, nq, topk, s);
+    if (depth == 1) return probe::launch<9, 8, 1>(t, row_stride, n_rows, ids, nq, topk, rot_ticks, s);
+    if (depth == 2) return probe::launch<9, 8, 2>(t, row_stride, n_rows, ids, nq, topk, rot_ticks, s);
+    if (depth == 3) return probe::launch<9, 8, 3>(t, row_stride, n_rows, ids, nq, topk, rot_ticks, s);
+    return probe::launch<9, 8, 4>(t, row_stride, n_rows, ids, nq, topk, rot_ticks, s);
   }
   if (waves == 4) {
-    if (depth == 1) return probe::launch<2, 4, 1>(t, row_stride, n_rows, ids, nq, topk, s);
-    if (depth == 2) return probe::launch<2, 4, 2>(t, row_stride, n_rows, ids, nq, topk, s);
-    if (depth == 3) return probe::launch<2, 4, 3>(t, row_stride, n_rows, ids, nq, topk, s);
-    return probe::launch<2, 4, 4>(t, row_stride, n_rows, ids, nq, topk, s);
+    if (depth == 1) return probe::launch<2, 4, 1>(t, row_stride, n_rows, ids, nq, topk, rot_ticks, s);
+    if (depth == 2) return probe::launch<2, 4, 2>(t, row_stride, n_rows, ids, nq, topk, rot_ticks, s);
+    if (depth == 3) return probe::launch<2, 4, 3>(t, row_stride, n_rows, ids, nq, topk, rot_ticks, s);
+    return probe::launch<2, 4, 4>(t, row_stride, n_rows, ids, nq, topk, rot_ticks, s);
   }
-  if (depth == 1) return probe::launch<2, 8, 1>(t, row_stride, n_rows, ids, nq, topk, s);
-  if (depth == 2) return probe::launch<2, 8, 2>(t, row_stride, n_rows, ids, nq, topk, s);
-  if (depth == 3) return probe::launch<2, 8, 3>(t, row_stride, n_rows, ids, nq, topk, s);
-  return probe::launch<2, 8, 4>(t, row_stride, n_rows, ids, nq, topk, s);
+  if (depth == 1) return probe::launch<2, 8, 1>(t, row_stride, n_rows, ids, nq, topk, rot_ticks, s);
+  if (depth == 2) return probe::launch<2, 8, 2>(t, row_stride, n_rows, ids, nq, topk, rot_ticks, s);
+  if (depth == 3) return probe::launch<2, 8, 3>(t, row_stride, n_rows, ids, nq, topk, rot_ticks, s);
+  return probe::launch<2, 8, 4>(t, row_stride, n_rows, ids, nq, topk, rot_ticks, s);
 }
 
 }  // namespace hisa

@@ -117,7 +117,7 @@ def test_attention_out_checks():
 
 def test_gather_probe_validation():
     L = H.lib()
-    args = [FAKE, 1152, 1152, 1024, FAKE, 16, 2048, 4, 2, NULL]
+    args = [FAKE, 1152, 1152, 1024, FAKE, 16, 2048, 4, 2, 0, NULL]
     a = list(args)
     a[0] = NULL
     assert L.hisa_gather_probe(*a) == 1
@@ -133,6 +133,9 @@ def test_gather_probe_validation():
     a = list(args)
     a[6] = 4097                                                      # topk
     assert L.hisa_gather_probe(*a) == 3
+    a = list(args)
+    a[9] = -1                                                        # rotation period
+    assert L.hisa_gather_probe(*a) == 2
     a = list(args)
     a[1] = 1144                                                      # stride below the row
     assert L.hisa_gather_probe(*a) == 2 and "row_stride" in _err()
@@ -150,7 +153,7 @@ def test_launch_error_is_hip_status():
     # every check passes, so the call reaches the HIP launch, which fails for
     # want of a device: HISA_ERR_HIP with HIP's own text, prefixed by the entry
     L = H.lib()
-    st = L.hisa_gather_probe(FAKE, 1152, 1152, 1024, FAKE, 16, 2048, 4, 2, NULL)
+    st = L.hisa_gather_probe(FAKE, 1152, 1152, 1024, FAKE, 16, 2048, 4, 2, 0, NULL)
     assert st == 4
     msg = _err()
     assert msg.startswith("hisa_gather_probe: ") and len(msg) > len("hisa_gather_probe: ")
@@ -159,7 +162,7 @@ def test_launch_error_is_hip_status():
                            FAKE, s, NULL, NULL, 0, NULL)
     assert st == 4 and _err().startswith("sparse_attn_fwd: ")
     # a later failing check replaces the text
-    assert L.hisa_gather_probe(NULL, 1152, 1152, 1024, FAKE, 16, 2048, 4, 2, NULL) == 1
+    assert L.hisa_gather_probe(NULL, 1152, 1152, 1024, FAKE, 16, 2048, 4, 2, 0, NULL) == 1
     assert "required" in _err()
 
 

@@ -6,6 +6,7 @@ max-abs 2e-2 and mean-abs 2e-3 of the oracle (plus a 1e-2 relative-norm
 check). Small shapes are checked on every query; the full-size workloads on
 sampled queries that include the edge positions."""
 import math
+import os
 
 import numpy as np
 import pytest
@@ -428,10 +429,24 @@ def test_workload_prefill_64k_mla_timed_step(inputs_64k):
     ti = ti_all[0, ridx].cpu().numpy()
     aidx = torch.tensor(arows, device=DEV)
     go = out_all[0, aidx].float().cpu().numpy()
-    # the one-stream step on the same buffers gives the same ids and outputs
+    # the one-stream step on the same buffers gives the same ids; the outputs
+    # agree up to the fp32 summation order (the latent kernel sums a query's
+    # tiles starting from a clock-chosen tile), and bit for bit in list order
     p.run()
     torch.cuda.synchronize()
-    assert torch.equal(p.token_idx, ti_all) and torch.equal(p.out, out_all)
+    assert torch.equal(p.token_idx, ti_all)
+    check_attention(p.out[0, aidx].float().cpu().numpy(), go, "64k one-stream vs overlapped")
+    os.environ["HISA_MLA_ROT_TICKS"] = "0"
+    try:
+        p.run_overlapped()
+        torch.cuda.synchronize()
+        o_list = p.out.clone()
+        p.run()
+        torch.cuda.synchronize()
+        assert torch.equal(p.out, o_list)
+        check_attention(o_list[0, aidx].float().cpu().numpy(), go, "64k list order vs rotated")
+    finally:
+        del os.environ["HISA_MLA_ROT_TICKS"]
     kidx = inp["kidx"][0].float().cpu().numpy()
     qidx = inp["qidx"][0].float().cpu().numpy()
     pos = inp["q_pos"][0].cpu().numpy()
