@@ -331,10 +331,19 @@ def bench_prefill(w, a, inp):
     res["graph"] = {"ms_per_step": g_ms, "queries_per_s": nq / (g_ms * 1e-3)}
     traffic = measured_traffic() if (w.mla and w.name == "prefill_64k_mla") else None
     res["roofline"] = {"kernel": f"sparse_attn ({w.Hq} heads, Dk {w.Dk}, Dv {w.Dv})",
+                       "scope": "the dominant kernel, one launch over all queries; the whole "
+                                "step against its roofline is path_roofline",
                        "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                        "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                        "traffic": traffic, "alg_flop_per_launch": attn_flop,
                        "kept_tokens": n_sel}
+    # the measured memory-side ceiling: the same rows gathered and discarded
+    g_ms, g_w, g_d = gather_ceiling(w, inp, p.token_idx[0].contiguous(), max(3, a.steps // 3))
+    res["gather_ceiling"] = {
+        "probe_ms": g_ms, "attention_ms": stage_ms["attention"],
+        "frac": g_ms / stage_ms["attention"], "probe_waves": g_w, "probe_depth": g_d,
+        "note": "hisa_gather_probe on the attention's own id lists (list order): the time the "
+                "row gathers alone take; frac = that / the attention launch"}
     idx_flop = indexer_flop(w)
     t_roof = (attn_flop + idx_flop) / (PEAK_BF16_TFLOPS * 1e12)
     res["path_roofline"] = {"bound": "mfma", "alg_flop": attn_flop + idx_flop,
@@ -383,15 +392,18 @@ def time_launch(fn, steps, warmup=1):
     return e0.elapsed_time(e1) / steps
 
 
-def gather_ceiling(w, inp, ids, steps, configs=((4, 2), (8, 2), (4, 3), (8, 3))):
+def gather_ceiling(w, inp, ids, steps, configs=((4, 2), (8, 1), (8, 2), (4, 3))):
     """Best time of the gather-rate probe over `configs` (waves, depth) on the
-    id lists the attention reads: the ceiling that gathering those rows alone
-    allows. Returns (ms, waves, depth)."""
+    id lists the attention reads, in list order: the time that gathering those
+    rows alone takes (twice the K-row time when K and V are separate rows).
+    Returns (ms, waves, depth)."""
     import long_context_indexer_block_amd as H
     table, row_bytes = attn_table(w, inp)
+    rows_per_token = 1 if w.mla else 2
     best = None
     for wv, dp in configs:
-        ms = time_launch(lambda: H.hisa_gather_probe(table, ids, row_bytes, wv, dp, 0), steps)
+        ms = rows_per_token * time_launch(
+            lambda: H.hisa_gather_probe(table, ids, row_bytes, wv, dp, 0), steps)
         if best is None or ms < best[0]:
             best = (ms, wv, dp)
     return best
