@@ -134,6 +134,19 @@ __device__ __forceinline__ int4 read_ids(const Item& it, int t, int l) {
   asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(a) : "memory");
   return v;
 }
+// The same read issued without waiting: the ids may be used only after
+// ids_wait, which waits for every LDS read of this wave and takes the
+// registers as operands so that no use can be placed before it.
+__device__ __forceinline__ int4 read_ids_issue(const Item& it, int t, int l) {
+  const uint32_t a =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int*)(&g_ids[it.w][t & 7][4 * (l >> 4)]);
+  int4 v;
+  asm volatile("ds_read_b128 %0, %1" : "=&v"(v) : "v"(a) : "memory");
+  return v;
+}
+__device__ __forceinline__ void ids_wait(int4& v) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w) : : "memory");
+}
 
 // Gather of tile t into K and V slots: instruction u fills rows 4u .. 4u+3,
 // lane l taking row 4u + l/16 and logical chunk (l%16) ^ swz(row), so 16
@@ -143,8 +156,8 @@ __device__ __forceinline__ int4 read_ids(const Item& it, int t, int l) {
 // the wave's base plus one 24-bit multiply-add (the load takes the base from
 // scalar registers); otherwise they are formed in 64 bits.
 template <bool OFF32>
-__device__ __forceinline__ uint32_t gather(const Item& it, int t, uint4* kd, uint4* vd, int l) {
-  const int4 ids = read_ids(it, t, l);
+__device__ __forceinline__ uint32_t gather_ids(const Item& it, int t, uint4* kd, uint4* vd,
+                                               const int4 ids, int l) {
   const int g = l >> 4, p = l & 15;
   uint32_t mask = 0;
   const int idv[4] = {ids.x, ids.y, ids.z, ids.w};
@@ -178,6 +191,11 @@ __device__ __forceinline__ uint32_t gather(const Item& it, int t, uint4* kd, uin
   return mask;
 }
 
+template <bool OFF32>
+__device__ __forceinline__ uint32_t gather(const Item& it, int t, uint4* kd, uint4* vd, int l) {
+  return gather_ids<OFF32>(it, t, kd, vd, read_ids(it, t, l), l);
+}
+
 struct State {
   bf16x8 qf[4];      // Q^T fragments: head l%16, k 32s + 8(l/16) .. +8
   f32x4 o[8];        // O block dvb: dv 16dvb + l%16, heads 4(l/16) + (0..3)
@@ -186,24 +204,44 @@ struct State {
   uint32_t m0, m1;   // valid masks of tiles t and t+1
 };
 
-// Tile t (slot I = t % 3): S^T, the softmax update, O += P V.
+// The fragments of tile t (slot I = t % 3) this lane needs: K fragments
+// (row l%16, chunks 4k + l/16) and V^T fragments of the 8 blocks of 16 value
+// columns (row 4(l/16) + (l%16)/4, columns 16dvb + 4(l%4) .. +3).
+struct Frags {
+  uint4 k[4];
+  v4s v[8];
+};
 template <int I>
-__device__ __forceinline__ void tile(State& st, const Item& it, int t, float scale_log2, int l) {
-  const int g = l >> 4;
-  // ---- S^T of the tile: lane l gets head l%16, tokens 4g + (0..3)
+__device__ __forceinline__ void read_frags(Frags& f, const Item& it, int l) {
+  const int g = l >> 4, r = l & 15;
   const uint4* kt = kbuf<I>(it.w);
-  const int r = l & 15;
-  f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
-  uint4 kf[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) kf[k] = kt[r * 16 + ((4 * k + g) ^ swz(r))];
+  for (int k = 0; k < 4; ++k) f.k[k] = kt[r * 16 + ((4 * k + g) ^ swz(r))];
+  const unsigned char* vt = reinterpret_cast<const unsigned char*>(vbuf<I>(it.w));
+  const int vrow = 4 * g + (r >> 2);
+  const int vbase = vrow * 256 + 8 * (r & 1);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) s = mfma16(as_bf16x8(kf[k]), st.qf[k], s);
+  for (int dvb = 0; dvb < 8; ++dvb) {
+    const int chunk = 2 * dvb + ((r & 3) >> 1);
+    f.v[dvb] = tr16(vt + vbase + 16 * (chunk ^ swz(vrow)));
+  }
+}
+
+// Tile t: S^T, the softmax update, O += P V, from fragments already read.
+__device__ __forceinline__ void tile(State& st, const Frags& f, int t, float scale_log2, int l) {
+  const int g = l >> 4;
+  // ---- S^T of the tile: lane l gets head l%16, tokens 4g + (0..3); two
+  // accumulation chains over the k steps, added at the end
+  f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
+  s0 = mfma16(as_bf16x8(f.k[0]), st.qf[0], s0);
+  s1 = mfma16(as_bf16x8(f.k[1]), st.qf[1], s1);
+  s0 = mfma16(as_bf16x8(f.k[2]), st.qf[2], s0);
+  s1 = mfma16(as_bf16x8(f.k[3]), st.qf[3], s1);
   float sv[4];
   float tmax = -INFINITY;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    sv[e] = ((st.m0 >> (4 * g + e)) & 1u) ? s[e] * scale_log2 : -INFINITY;
+    sv[e] = ((st.m0 >> (4 * g + e)) & 1u) ? (s0[e] + s1[e]) * scale_log2 : -INFINITY;
     tmax = fmaxf(tmax, sv[e]);
   }
   tmax = max_x16_x32(tmax);
@@ -229,30 +267,28 @@ __device__ __forceinline__ void tile(State& st, const Item& it, int t, float sca
   st.lsum += (p[0] + p[1]) + (p[2] + p[3]);
   const uint2 pp = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
   const v4s pa = __builtin_bit_cast(v4s, pp);
-  // ---- O += P V: V^T fragment of dv block dvb: lane l (group g, sl = l%16)
-  // addresses row 4g + sl/4, columns 16dvb + 4(sl%4) .. +3 and receives
-  // column 16dvb + sl of rows 4g .. 4g+3
-  const unsigned char* vt = reinterpret_cast<const unsigned char*>(vbuf<I>(it.w));
-  const int sl = l & 15;
-  const int vrow = 4 * g + (sl >> 2);
-  const int vbase = vrow * 256 + 8 * (sl & 1);
+  // ---- O += P V
 #pragma unroll
-  for (int dvb = 0; dvb < 8; ++dvb) {
-    const int chunk = 2 * dvb + ((sl & 3) >> 1);
-    const v4s vb = tr16(vt + vbase + 16 * (chunk ^ swz(vrow)));
-    st.o[dvb] = mfma16k16(pa, vb, st.o[dvb]);
-  }
+  for (int dvb = 0; dvb < 8; ++dvb) st.o[dvb] = mfma16k16(pa, f.v[dvb], st.o[dvb]);
 }
 
 // Iteration t: gather tile t+2 (and the ids of tile t+5), then tile t; wait
 // until tile t+1 has landed.
+// Iteration t: every LDS read of the iteration at once (the ids of tile t+2,
+// the K and V fragments of tile t) and one wait for them; then gather tile t+2
+// (and the ids of tile t+5), then tile t; wait until tile t+1 has landed.
 template <int I, bool OFF32>
 __device__ __forceinline__ void iter(State& st, const Item& it, int t, float scale_log2, int l) {
-  const uint32_t m2 = gather<OFF32>(it, t + 2, kbuf<I + 2>(it.w), vbuf<I + 2>(it.w), l);
+  int4 ids = read_ids_issue(it, t + 2, l);
+  Frags f;
+  read_frags<I>(f, it, l);
+  ids_wait(ids);
+  const uint32_t m2 = gather_ids<OFF32>(it, t + 2, kbuf<I + 2>(it.w), vbuf<I + 2>(it.w), ids, l);
   ids_issue(it, t + 5, l);
-  tile<I>(st, it, t, scale_log2, l);
+  tile(st, f, t, scale_log2, l);
   st.m0 = st.m1;
   st.m1 = m2;
+  __builtin_amdgcn_sched_barrier(0);   // the tile's work stays ahead of the wait
   __builtin_amdgcn_s_waitcnt(0x0079);  // vmcnt(9): all but this iteration's 9 loads
 }
 
