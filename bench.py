@@ -70,7 +70,17 @@ def parse():
     ap.add_argument("--counters-out", default="")
     ap.add_argument("--counters-kernel", default="attn")
     ap.add_argument("--counters-title", default="")
+    ap.add_argument("--counters-note", default="",
+                    help="a paragraph placed under the title of a written summary")
     ap.add_argument("--counters-command", default="")
+    ap.add_argument("--write-trace-md", default="",
+                    help="only summarise a rocprofv3 --kernel-trace csv folder into a markdown "
+                         "table of the library's kernels, split by grid size (--counters-out, "
+                         "--counters-title, --counters-command)")
+    ap.add_argument("--write-bytes-md", default="",
+                    help="only summarise the FETCH_SIZE / WRITE_SIZE passes of a traffic "
+                         "folder (fetch/, write/, cfetch/, cwrite/) per kernel and grid size "
+                         "into markdown (--counters-out, --counters-title, --counters-command)")
     ap.add_argument("--write-traffic", default="",
                     help="only summarise rocprofv3 byte counters found under this folder "
                          "(fetch/, write/, cfetch/, cwrite/) into the traffic record")
@@ -481,10 +491,87 @@ def bench_gather_probe(w, a, inp):
     return out
 
 
+def _short(name):
+    return name.split("(")[0].replace("void ", "")
+
+
+def write_trace_md(folder, out_path, title, command, note=""):
+    """Per (kernel, grid size) of the library's kernels (namespace hisa) in a
+    rocprofv3 kernel trace: calls, mean / min / max duration in us and share
+    of the GPU time of all dispatches in the trace."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(folder, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel trace under {folder}")
+    per, total = {}, 0.0
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            total += d
+            if "hisa::" not in r["Kernel_Name"]:
+                continue
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            per.setdefault((_short(r["Kernel_Name"]), grid), []).append(d)
+    rows = sorted(per.items(), key=lambda kv: -sum(kv[1]))
+    lines = [f"# {title}", ""] + ([note.strip(), ""] if note else []) + [
+             "Command (repository root, on the GPU host):", "", "```",
+             command.strip(), "```", "",
+             "Durations in microseconds (rocprofv3 kernel trace); rows split by grid size "
+             "(threads); the share is of all GPU time in the trace (input generation included).",
+             "", "| kernel | grid (threads) | calls | avg us | min us | max us | % of GPU time |",
+             "|---|---|---|---|---|---|---|"]
+    for (name, grid), ds in rows:
+        lines.append(f"| `{name}` | {grid:,} | {len(ds)} | {sum(ds) / len(ds):.1f} | "
+                     f"{min(ds):.1f} | {max(ds):.1f} | {100 * sum(ds) / total:.2f} |")
+    text = "\n".join(lines) + "\n"
+    if out_path:
+        with open(out_path, "w") as fh:
+            fh.write(text)
+    print(text)
+
+
+def write_bytes_md(folder, out_path, title, command, note="", copy_bytes=1 << 30):
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the library's kernels
+    per (kernel, grid size), scaled to bytes by the factors a plain copy of
+    `copy_bytes` gives (its fetch and write counts against its size)."""
+    def rows(sub, counter):
+        out = {}
+        for name, v, grid in counter_rows(os.path.join(folder, sub), counter):
+            out.setdefault((_short(name), grid), []).append(v)
+        return out
+    copy = lambda n: "copyBuffer" in n or ("copy" in n.lower() and "Fill" not in n)
+    cf = max(v for (n, _), vs in rows("cfetch", "FETCH_SIZE").items() if copy(n) for v in vs)
+    cw = max(v for (n, _), vs in rows("cwrite", "WRITE_SIZE").items() if copy(n) for v in vs)
+    fs, ws = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    fe, wr = rows("fetch", "FETCH_SIZE"), rows("write", "WRITE_SIZE")
+    lines = [f"# {title}", ""] + ([note.strip(), ""] if note else []) + [
+             "Commands (repository root, each a run of its own):", "", "```",
+             command.strip(), "```", "",
+             f"Calibration: a plain {copy_bytes:,}-byte device copy reads FETCH_SIZE = "
+             f"{cf:,.2f} KiB and WRITE_SIZE = {cw:,.2f} KiB, so fetch counts are scaled by "
+             f"{fs:.5f} and write counts by {ws:.5f}. The counters sit between L2 and the "
+             "memory fabric: reads the Infinity Cache serves count as well.", "",
+             "| kernel | grid (threads) | FETCH_SIZE KiB | WRITE_SIZE KiB | read GB (scaled) | "
+             "written GB (scaled) |", "|---|---|---|---|---|---|"]
+    for key in fe:
+        if "hisa::" not in key[0] or key not in wr:
+            continue
+        f_kib = sum(fe[key]) / len(fe[key])
+        w_kib = sum(wr[key]) / len(wr[key])
+        lines.append(f"| `{key[0]}` | {key[1]:,} | {f_kib:,.1f} | {w_kib:,.1f} | "
+                     f"{f_kib * 1024 * fs / 1e9:.3f} | {w_kib * 1024 * ws / 1e9:.3f} |")
+    text = "\n".join(lines) + "\n"
+    if out_path:
+        with open(out_path, "w") as fh:
+            fh.write(text)
+    print(text)
+
+
 N_XCD, N_CU, N_SIMD, CLOCK_GHZ = 8, 256, 1024, 2.4   # MI355X
 
 
-def write_counters(folder, out_path, kernel_sub, title="", command=""):
+def write_counters(folder, out_path, kernel_sub, title="", command="", note=""):
     """Summarise rocprofv3 --pmc csv folders (one per pass, any names) for the
     dispatches of kernels whose name holds `kernel_sub`, largest grid only:
     the mean of every counter per dispatch and the figures derived from them.
@@ -516,6 +603,8 @@ def write_counters(folder, out_path, kernel_sub, title="", command=""):
             dur.setdefault(key, {})[(f, r["Dispatch_Id"])] = (
                 int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     lines = [f"# {title}", ""] if title else []
+    if note:
+        lines += [note.strip(), ""]
     if command:
         lines += ["Commands (repository root, each pass a run of its own):", "", "```",
                   command.strip(), "```", ""]
@@ -848,7 +937,15 @@ def main():
         return
     if a.write_counters:
         write_counters(a.write_counters, a.counters_out, a.counters_kernel,
-                       a.counters_title, a.counters_command)
+                       a.counters_title, a.counters_command, a.counters_note)
+        return
+    if a.write_trace_md:
+        write_trace_md(a.write_trace_md, a.counters_out, a.counters_title, a.counters_command,
+                       a.counters_note)
+        return
+    if a.write_bytes_md:
+        write_bytes_md(a.write_bytes_md, a.counters_out, a.counters_title, a.counters_command,
+                       a.counters_note)
         return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the path has no "
