@@ -6,10 +6,13 @@
 //
 // One wave per (sequence, query, kv head), two independent waves per
 // workgroup, no workgroup barrier. The kept tokens stream through the wave's
-// own LDS ring of three 16-token tiles (K and V, 4 KB each), gathered
-// HBM/L2 -> LDS with 16-byte direct loads two tiles ahead; token ids take
-// the same path into a ring of their own, so the loop issues no other global
-// load and each load-counter wait covers exactly the loads it names.
+// own LDS ring of two 16-token tiles (K and V, 4 KB each), gathered
+// HBM/L2 -> LDS with 16-byte direct loads two tiles ahead: a tile's K and V
+// fragments are all read into registers under one wait before the gathers
+// of the tile two ahead are issued into the same slot, so two slots carry a
+// two-tile prefetch (18 KB of LDS per wave, eight waves per CU). Token ids
+// take the same path into a ring of their own, so the loop issues no other
+// global load and each load-counter wait covers exactly the loads it names.
 //
 // Per tile: S^T = K Q^T on 16x16x32 bf16 MFMA (K fragments from LDS, the
 // group's Q rows in registers). Its accumulator holds, in lane l, head l%16
@@ -51,23 +54,20 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short v4s;
 // one slot is never mistaken for a read of the slot being gathered into.
 __shared__ uint4 g_k0[WAVES][TCH];
 __shared__ uint4 g_k1[WAVES][TCH];
-__shared__ uint4 g_k2[WAVES][TCH];
 __shared__ uint4 g_v0[WAVES][TCH];
 __shared__ uint4 g_v1[WAVES][TCH];
-__shared__ uint4 g_v2[WAVES][TCH];
 __shared__ int g_ids[WAVES][8][64];  // ids of eight tiles (lanes 16..63 repeat)
 
+// Slot of tile I (mod 2).
 template <int I>
 __device__ __forceinline__ uint4* kbuf(int w) {
-  if constexpr (I % 3 == 0) return g_k0[w];
-  else if constexpr (I % 3 == 1) return g_k1[w];
-  else return g_k2[w];
+  if constexpr (I % 2 == 0) return g_k0[w];
+  else return g_k1[w];
 }
 template <int I>
 __device__ __forceinline__ uint4* vbuf(int w) {
-  if constexpr (I % 3 == 0) return g_v0[w];
-  else if constexpr (I % 3 == 1) return g_v1[w];
-  else return g_v2[w];
+  if constexpr (I % 2 == 0) return g_v0[w];
+  else return g_v1[w];
 }
 
 // Tile layout: row r (a token) holds its 16 chunks of 16 bytes permuted by
@@ -126,7 +126,11 @@ __device__ __forceinline__ void ids_issue(const Item& it, int t, int l) {
 }
 // The four ids of this lane's gather rows for tile t (landed by an earlier
 // load-counter wait). Written out because the compiler cannot tell the ring
-// slots apart and would otherwise drain every load in flight first.
+// slots apart and would otherwise drain every load in flight first. The wait
+// stays in the same statement as the read: the compiler takes an asm output
+// as written when its statement ends, so after a read without its wait it may
+// copy the destination registers before the data has arrived. The wait also
+// covers every LDS read the wave issued before.
 __device__ __forceinline__ int4 read_ids(const Item& it, int t, int l) {
   const uint32_t a =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int*)(&g_ids[it.w][t & 7][4 * (l >> 4)]);
@@ -134,20 +138,6 @@ __device__ __forceinline__ int4 read_ids(const Item& it, int t, int l) {
   asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(a) : "memory");
   return v;
 }
-// The same read issued without waiting: the ids may be used only after
-// ids_wait, which waits for every LDS read of this wave and takes the
-// registers as operands so that no use can be placed before it.
-__device__ __forceinline__ int4 read_ids_issue(const Item& it, int t, int l) {
-  const uint32_t a =
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int*)(&g_ids[it.w][t & 7][4 * (l >> 4)]);
-  int4 v;
-  asm volatile("ds_read_b128 %0, %1" : "=&v"(v) : "v"(a) : "memory");
-  return v;
-}
-__device__ __forceinline__ void ids_wait(int4& v) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w) : : "memory");
-}
-
 // Gather of tile t into K and V slots: instruction u fills rows 4u .. 4u+3,
 // lane l taking row 4u + l/16 and logical chunk (l%16) ^ swz(row), so 16
 // adjacent lanes read one 256-byte row. Returns the tile's valid-token mask
@@ -272,24 +262,25 @@ __device__ __forceinline__ void tile(State& st, const Frags& f, int t, float sca
   for (int dvb = 0; dvb < 8; ++dvb) st.o[dvb] = mfma16k16(pa, f.v[dvb], st.o[dvb]);
 }
 
-// Iteration t: gather tile t+2 (and the ids of tile t+5), then tile t; wait
-// until tile t+1 has landed.
-// Iteration t: every LDS read of the iteration at once (the ids of tile t+2,
-// the K and V fragments of tile t) and one wait for them; then gather tile t+2
-// (and the ids of tile t+5), then tile t; wait until tile t+1 has landed.
+// Iteration t (slot t % 2): the K and V fragments of tile t and the gather
+// ids of tile t+2, all under one wait; then the gathers of tile t+2 into the
+// slot tile t has just left (its data is in registers) and the id load of
+// tile t+5; then tile t's products, kept ahead of the wait that ends the
+// iteration: at most this iteration's 9 loads (8 gathers, 1 id load) remain,
+// so tile t+1 and the ids of tile t+3 have landed.
 template <int I, bool OFF32>
 __device__ __forceinline__ void iter(State& st, const Item& it, int t, float scale_log2, int l) {
-  int4 ids = read_ids_issue(it, t + 2, l);
   Frags f;
   read_frags<I>(f, it, l);
-  ids_wait(ids);
-  const uint32_t m2 = gather_ids<OFF32>(it, t + 2, kbuf<I + 2>(it.w), vbuf<I + 2>(it.w), ids, l);
+  // issued after the fragment reads: its wait covers them as well
+  const int4 ids = read_ids(it, t + 2, l);
+  const uint32_t m2 = gather_ids<OFF32>(it, t + 2, kbuf<I>(it.w), vbuf<I>(it.w), ids, l);
   ids_issue(it, t + 5, l);
   tile(st, f, t, scale_log2, l);
   st.m0 = st.m1;
   st.m1 = m2;
-  __builtin_amdgcn_sched_barrier(0);   // the tile's work stays ahead of the wait
-  __builtin_amdgcn_s_waitcnt(0x0079);  // vmcnt(9): all but this iteration's 9 loads
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0x0079);  // vmcnt(9) lgkmcnt(0)
 }
 
 }  // namespace d128
@@ -325,7 +316,7 @@ __global__ __launch_bounds__(128) void sparse_attn_d128_kernel(
   it.L = L;
   it.w = w;
   const int ntiles = (it.topk + NT - 1) / NT;
-  const int nt3 = (ntiles + 2) / 3 * 3;  // tiles processed: a multiple of 3, the extra ones masked
+  const int nt2 = (ntiles + 1) & ~1;  // tiles processed: even, the extra one masked
 
   State st;
   {
@@ -347,11 +338,9 @@ __global__ __launch_bounds__(128) void sparse_attn_d128_kernel(
   st.m0 = gather<OFF32>(it, 0, kbuf<0>(w), vbuf<0>(w), l);
   st.m1 = gather<OFF32>(it, 1, kbuf<1>(w), vbuf<1>(w), l);
   __builtin_amdgcn_s_waitcnt(0x0078);  // vmcnt(8): tile 0 has landed
-  int t = 0;
-  for (; t + 3 <= nt3; t += 3) {
+  for (int t = 0; t < nt2; t += 2) {
     iter<0, OFF32>(st, it, t, scale_log2, l);
     iter<1, OFF32>(st, it, t + 1, scale_log2, l);
-    iter<2, OFF32>(st, it, t + 2, scale_log2, l);
   }
   __builtin_amdgcn_s_waitcnt(0x0070);  // the loads past the end
 
