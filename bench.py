@@ -694,11 +694,20 @@ def bench_decode(w, a, inp):
         i = state["i"] = (state["i"] + 1) % 4
         p.qidx, p.q = qsets[i], qs[i]
 
-    stages = ["rotate_query_set", "block_score", "select_blocks", "token_select", "attention"]
-    calls = [
-        pick,
-        lambda: H.hisa_block_score(p.qidx, p.q_pos, p.split, p.B, out=p.block_scores),
-        lambda: H.hisa_select_blocks(p.block_scores, p.q_pos, p.B, p.m, out=p.block_idx),
+    # one query per sequence: block scores and top-m blocks in one call, the
+    # blocks of each query split over several workgroups (same block_idx)
+    n_rows = p.split.shape[1]
+    route_ws = H.route_workspace(w.batch, w.queries, n_rows, w.m, p.split.device)
+    if route_ws is not None:
+        stages = ["rotate_query_set", "route", "token_select", "attention"]
+        route = [lambda: H.hisa_route_blocks(p.qidx, p.q_pos, p.split, p.B, p.m, out=p.block_idx,
+                                             workspace=route_ws)]
+    else:
+        stages = ["rotate_query_set", "block_score", "select_blocks", "token_select", "attention"]
+        route = [lambda: H.hisa_block_score(p.qidx, p.q_pos, p.split, p.B, out=p.block_scores),
+                 lambda: H.hisa_select_blocks(p.block_scores, p.q_pos, p.B, p.m,
+                                              out=p.block_idx)]
+    calls = [pick] + route + [
         lambda: H.hisa_token_select(p.qidx, p.kidx, p.q_pos, p.block_idx, p.B, p.k_top,
                                     token_idx=p.token_idx, want_scores=False, workspace=p.ws),
         p.attend,

@@ -132,17 +132,28 @@ hisa_status_t hisa_select_blocks(const float* block_scores, const int32_t* q_pos
                                  int nq, int n_rows, int B, int m, int32_t* block_idx,
                                  hisa_stream_t stream);
 
-/* Steps 2 and 3 in one call, for many queries: the same block_idx as
- * hisa_block_score followed by hisa_select_blocks (bit for bit: the same
- * exact products and selection), without writing the block scores to memory.
- * For m <= 130 and n_rows <= 65537 the scores of 16 or 32 consecutive
- * queries are streamed through per-query candidate buffers on chip; otherwise
- * all of their scores are held on chip, which needs n_rows <= 1026
- * (HISA_ERR_UNSUPPORTED beyond both: use the two calls). Arguments as for
- * those two. */
+/* Steps 2 and 3 in one call: the same block_idx as hisa_block_score followed
+ * by hisa_select_blocks (bit for bit: the same exact products and
+ * selection), without writing the block scores to memory. For m <= 130 and
+ * n_rows <= 65537 the scores of 16 or 32 consecutive queries are streamed
+ * through per-query candidate buffers on chip; otherwise all of their scores
+ * are held on chip, which needs n_rows <= 1026 (HISA_ERR_UNSUPPORTED beyond
+ * both: use the two calls). Arguments as for those two, plus:
+ *   workspace  optional device scratch (NULL allowed), 256-byte aligned, of
+ *              hisa_route_blocks_workspace_bytes() bytes; its contents on
+ *              entry are ignored. When that size is non-zero (fewer than 1024
+ *              queries, m - 2 <= 64, at most 2048 survivors per query) the
+ *              candidate blocks of each query are scored and reduced to their
+ *              best m - 2 in parts of 256 over several workgroups and merged,
+ *              which keeps the chip busy for the few queries of a decode step;
+ *              with NULL the same result comes from one workgroup per query
+ *              group. A non-NULL workspace smaller than needed is
+ *              HISA_ERR_WORKSPACE; for shapes that need none it is ignored. */
+size_t hisa_route_blocks_workspace_bytes(int batch, int nq, int n_rows, int m);
 hisa_status_t hisa_route_blocks(const void* qidx, hisa_strides_t qs, const int32_t* q_pos,
                                 int batch, int nq, const void* split, int n_rows, int d, int B,
-                                int m, int32_t* block_idx, hisa_stream_t stream);
+                                int m, int32_t* block_idx, void* workspace,
+                                size_t workspace_bytes, hisa_stream_t stream);
 
 /* Step 4: token top-k inside the kept blocks (HISA explainer 1.2.2; HISA news
  * article, fine token selection). Candidates are the tokens j <= t of the

@@ -42,7 +42,8 @@ _SIGS = {
     "hisa_block_summary_update": (_I, [_P, Strides, _I, _I, _I, _I, _P, _P, _P, _I, _I, _P]),
     "hisa_block_score": (_I, [_P, Strides, _P, _I, _I, _P, _I, _I, _I, _P, _P]),
     "hisa_select_blocks": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P]),
-    "hisa_route_blocks": (_I, [_P, Strides, _P, _I, _I, _P, _I, _I, _I, _I, _P, _P]),
+    "hisa_route_blocks": (_I, [_P, Strides, _P, _I, _I, _P, _I, _I, _I, _I, _P, _P, _S, _P]),
+    "hisa_route_blocks_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "hisa_token_select": (_I, [_P, Strides, _P, Strides, _P, _P, _I, _I, _I, _I, _I, _I, _I,
                                _P, _P, _P, _S, _P]),
     "hisa_token_select_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I]),
@@ -172,16 +173,28 @@ def route_supported(n_rows, m):
     return n_rows <= ROUTE_MAX_ROWS or (m <= ROUTE_STREAM_MAX_M and n_rows <= ROUTE_STREAM_MAX_ROWS)
 
 
-def hisa_route_blocks(qidx, q_pos, split, B, m, out=None):
+def route_workspace(batch, nq, n_rows, m, device):
+    """Workspace for hisa_route_blocks on this shape (None when it needs none)."""
+    n = int(lib().hisa_route_blocks_workspace_bytes(batch, nq, n_rows, m))
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def hisa_route_blocks(qidx, q_pos, split, B, m, out=None, workspace="auto"):
     """Steps 2 and 3 fused: qidx [b, nq, d] bf16, q_pos [b, nq] int32, split
-    [b, n, 3, d] (route_supported(n, m)) -> block_idx [b, nq, m] int32."""
+    [b, n, 3, d] (route_supported(n, m)) -> block_idx [b, nq, m] int32.
+    workspace: "auto" allocates what the shape asks for (few queries split
+    their blocks over several workgroups), None runs without, or a uint8
+    tensor from route_workspace()."""
     _need(qidx, torch.bfloat16, "qidx")
     b, nq, d = qidx.shape
     n = split.shape[1]
     if out is None:
         out = torch.empty(b, nq, m, dtype=torch.int32, device=qidx.device)
+    if isinstance(workspace, str):
+        workspace = route_workspace(b, nq, n, m, qidx.device)
+    wsb = 0 if workspace is None else workspace.numel()
     _check(lib().hisa_route_blocks(_ptr(qidx), _str3(qidx, "bt"), _ptr(q_pos), b, nq, _ptr(split),
-                                   n, d, B, m, _ptr(out), _stream()))
+                                   n, d, B, m, _ptr(out), _ptr(workspace), wsb, _stream()))
     return out
 
 

@@ -67,7 +67,7 @@ extern "C" {
 
 const char* hisa_last_error(void) { return g_err.c_str(); }
 
-int hisa_abi_version(void) { return 2; }
+int hisa_abi_version(void) { return 3; }
 
 hisa_status_t hisa_block_summary(const void* kidx, hisa_strides_t ks, int batch, int L, int d,
                                  int B, const void* proj, float* summary, void* split,
@@ -155,9 +155,15 @@ hisa_status_t hisa_select_blocks(const float* block_scores, const int32_t* q_pos
                     "hisa_select_blocks");
 }
 
+size_t hisa_route_blocks_workspace_bytes(int batch, int nq, int n_rows, int m) {
+  if (batch < 1 || nq < 1 || n_rows < 1 || m < 2) return 0;
+  return hisa::route_split_workspace(batch, nq, n_rows, m);
+}
+
 hisa_status_t hisa_route_blocks(const void* qidx, hisa_strides_t qs, const int32_t* q_pos,
                                 int batch, int nq, const void* split, int n_rows, int d, int B,
-                                int m, int32_t* block_idx, hisa_stream_t stream) {
+                                int m, int32_t* block_idx, void* workspace, size_t workspace_bytes,
+                                hisa_stream_t stream) {
   CHECK(qidx && q_pos && split && block_idx, HISA_ERR_NULL,
         "qidx, q_pos, split and block_idx are required");
   CHECK(batch >= 1 && nq >= 1 && n_rows >= 1, HISA_ERR_SHAPE,
@@ -176,9 +182,17 @@ hisa_status_t hisa_route_blocks(const void* qidx, hisa_strides_t qs, const int32
   if ((st = check_block(B)) != HISA_OK) return st;
   if ((st = check_bf16(qidx, qs, "qidx")) != HISA_OK) return st;
   CHECK(aligned16(split), HISA_ERR_SHAPE, "split must be 16-byte aligned");
+  const size_t need = hisa::route_split_workspace(batch, nq, n_rows, m);
+  if (workspace != nullptr && need > 0) {
+    CHECK((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, HISA_ERR_WORKSPACE,
+          "workspace must be 256-byte aligned");
+    CHECK(workspace_bytes >= need, HISA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu",
+          workspace_bytes, need);
+  }
   return hip_status(hisa::launch_route_blocks(static_cast<const uint16_t*>(qidx), s3(qs), q_pos,
                                               batch, nq, static_cast<const uint16_t*>(split),
                                               n_rows, d, B, m, block_idx,
+                                              need > 0 ? workspace : nullptr,
                                               static_cast<hipStream_t>(stream)),
                     "hisa_route_blocks");
 }

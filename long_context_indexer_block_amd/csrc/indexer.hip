@@ -758,9 +758,222 @@ __global__ __launch_bounds__(64 * NW) void route_blocks_stream_kernel(
   }
 }
 
+// ----------------------------------------- steps 2 and 3 for few queries
+// Few queries over many blocks leave most of the chip idle when each query
+// is scored and selected by one workgroup. Here each query's candidate
+// positions are cut into parts of kPart: a workgroup of four waves scores
+// one part (the exact three-term products of block_score_kernel in its
+// summation order, so the scores are the same bits) into LDS, and its first
+// wave keeps the part's best K = m - 2 (wave_topk: ties to the lowest
+// position) in the workspace as (order key, position) pairs, in position
+// order. One wave per query then takes the best K of the parts' survivors:
+// every overall winner is a winner of its part under the same order, and
+// the survivors, part after part, are in position order, so ties again go to
+// the lowest position. It adds the first and the local block around them.
+constexpr int kPart = 256;
+constexpr int kSplitMaxK = 64;        // free slots: wave_topk's short path
+constexpr int kSplitMaxUnion = 2048;  // survivors per query the merge holds
+
+constexpr int kPartWaves = kPart / 32;  // each wave scores two 16-row tiles, one load round
+
+template <int D>
+__global__ __launch_bounds__(64 * kPartWaves) void route_part_kernel(
+    const uint16_t* __restrict__ qidx, int64_t qsb, int64_t qst, const int32_t* __restrict__ q_pos,
+    int nq, const uint16_t* __restrict__ split, int n_rows, int B, float invB, int m,
+    uint2* __restrict__ parts, int nparts) {
+  constexpr int KS = D / 32;
+  __shared__ __align__(16) float sc[kPart];
+  __shared__ uint32_t lkey[kSelSmall];
+  __shared__ int lpos[kSelSmall];
+  const int part = blockIdx.x;
+  const int64_t qi = blockIdx.y;
+  const int b = static_cast<int>(qi / nq), q = static_cast<int>(qi % nq);
+  const int bt = min(max(q_pos[qi], 0), n_rows * B - 1) / B;
+  const int n = max(bt - 1, 0);
+  const int K = m - 2;
+  const int p0 = part * kPart;
+  if (n <= K || p0 >= n) return;  // all blocks kept, or no candidate here: the merge
+  const int w = threadIdx.x >> 6, l = lane_id(), g = l / 16, r16 = l % 16;
+  const int cnt = min(kPart, n - p0);
+  if (32 * w < cnt) {
+    // every column of the products is this query (one column is stored)
+    const uint16_t* qrow = qidx + b * qsb + static_cast<int64_t>(q) * qst + 8 * g;
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int x = 0; x < KS; ++x) qf[x] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 32 * x));
+    // wave w: local positions 32w + 16u + (0..15), u = 0, 1 (position p is
+    // block p + 1), all loads of both tiles in flight before the products
+    uint4 sf[2][3 * KS];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int cc = min(1 + p0 + 32 * w + 16 * u + r16, n_rows - 1);
+      const uint16_t* srow = split + (static_cast<int64_t>(b) * n_rows + cc) * 3 * D + 8 * g;
+#pragma unroll
+      for (int x = 0; x < 3 * KS; ++x)
+        sf[u][x] = *reinterpret_cast<const uint4*>(srow + (x / KS) * D + 32 * (x % KS));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int x = 0; x < 3 * KS; ++x) acc = mfma16(as_bf16x8(sf[u][x]), qf[x % KS], acc);
+      // lane (g, column r16): local positions 32w + 16u + 4g + (0..3)
+      if (r16 == 0)
+        *reinterpret_cast<float4*>(&sc[32 * w + 16 * u + 4 * g]) =
+            make_float4(acc[0] * invB, acc[1] * invB, acc[2] * invB, acc[3] * invB);
+    }
+  }
+  __syncthreads();
+  if (w == 0) {
+    uint32_t key[kPart / 64];
+    uint32_t okm = 0;
+#pragma unroll
+    for (int i = 0; i < kPart / 64; ++i) {
+      const int p = 64 * i + l;
+      key[i] = p < cnt ? order_key(sc[p]) : 0u;
+      okm |= p < cnt ? (1u << i) : 0u;
+    }
+    uint2* dst = parts + (qi * nparts + part) * K;
+    wave_topk(key, okm, static_cast<uint32_t>(min(K, cnt)), lkey, lpos,
+              [&](uint32_t rank, int p) {
+                dst[rank] = make_uint2(order_key(sc[p]), static_cast<uint32_t>(p0 + p));
+              });
+  }
+}
+
+// Entry e = u*K + j is survivor j of part u; part u keeps min(K, its
+// candidates). With W waves, wave v reduces parts v*PW .. v*PW + PW - 1 to
+// their best K (in position order, into LDS), and wave 0 takes the best K of
+// those W*K; IT and IT2 items per lane hold the two stages.
+template <int W, int IT, int IT2>
+__global__ __launch_bounds__(64 * W) void route_merge_kernel(const int32_t* __restrict__ q_pos,
+                                                             int n_rows, int B, int m,
+                                                             const uint2* __restrict__ parts,
+                                                             int nparts, int PW,
+                                                             int32_t* __restrict__ block_idx) {
+  __shared__ uint32_t lkey[W][kSelSmall];
+  __shared__ int lpos[W][kSelSmall];
+  __shared__ uint32_t ukey[W > 1 ? W * kSplitMaxK : 1];
+  __shared__ int upos[W > 1 ? W * kSplitMaxK : 1];
+  __shared__ int ucnt[W];
+  const int64_t qi = blockIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = lane_id();
+  const int bt = min(max(q_pos[qi], 0), n_rows * B - 1) / B;
+  const int n = max(bt - 1, 0);
+  const int K = m - (bt == 0 ? 1 : 2);
+  int32_t* out = block_idx + qi * m;
+  if (n <= K) {
+    for (int i = threadIdx.x; i < m; i += 64 * W) out[i] = i <= bt ? i : -1;
+    return;
+  }
+  const int np = (n + kPart - 1) / kPart;
+  const uint2* src = parts + qi * nparts * K;
+  // this wave's entries: parts w*PW .. (their survivors, in position order)
+  const int u0 = w * PW;
+  const int nu = max(0, min(PW, np - u0));
+  uint32_t key[IT];
+  uint32_t okm = 0;
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int e = 64 * i + l;  // entry of this wave's range
+    const int u = e / K, j = e - u * K;
+    const bool ok = u < nu && j < min(K, n - (u0 + u) * kPart);
+    const uint32_t k = src[ok ? u0 * K + e : 0].x;  // entry 0 exists: the query has candidates
+    key[i] = ok ? k : 0u;
+    okm |= ok ? (1u << i) : 0u;
+  }
+  if constexpr (W == 1) {
+    wave_topk(key, okm, static_cast<uint32_t>(K), lkey[0], lpos[0],
+              [&](uint32_t rank, int e) { out[1 + rank] = static_cast<int32_t>(src[e].y) + 1; });
+  } else {
+    // this wave's best min(K, its entries) into LDS, in position order
+    uint32_t have = 0;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) have += static_cast<uint32_t>(__popcll(__ballot((okm >> i) & 1u)));
+    const uint32_t kv = min(static_cast<uint32_t>(K), have);
+    if (kv > 0)
+      wave_topk(key, okm, kv, lkey[w], lpos[w], [&](uint32_t rank, int e) {
+        ukey[w * kSplitMaxK + rank] = src[u0 * K + e].x;
+        upos[w * kSplitMaxK + rank] = static_cast<int>(src[u0 * K + e].y);
+      });
+    if (l == 0) ucnt[w] = static_cast<int>(kv);
+    __syncthreads();
+    if (w == 0) {
+      // entry f = v*kSplitMaxK + r: survivor r of wave v (position order)
+      uint32_t k2[IT2];
+      uint32_t ok2 = 0;
+#pragma unroll
+      for (int i = 0; i < IT2; ++i) {
+        const int f = 64 * i + l;
+        const int v = f / kSplitMaxK, r = f % kSplitMaxK;
+        const bool ok = v < W && r < ucnt[min(v, W - 1)];
+        k2[i] = ok ? ukey[min(f, W * kSplitMaxK - 1)] : 0u;
+        ok2 |= ok ? (1u << i) : 0u;
+      }
+      wave_topk(k2, ok2, static_cast<uint32_t>(K), lkey[0], lpos[0],
+                [&](uint32_t rank, int f) { out[1 + rank] = upos[f] + 1; });
+    }
+  }
+  if (threadIdx.x == 0) {
+    out[0] = 0;
+    out[1 + K] = bt;
+  }
+}
+
+// Parts per query for the split routing, or 0 when it does not apply.
+static int route_split_parts(int64_t nqueries, int n_rows, int m) {
+  if (nqueries >= 1024 || m < 3 || m - 2 > kSplitMaxK || n_rows > kRouteStreamMaxRows) return 0;
+  const int nmax = max(n_rows - 2, 0);  // candidates of the last block's queries
+  const int nparts = max(1, (nmax + kPart - 1) / kPart);
+  if (static_cast<int64_t>(nparts) * (m - 2) > kSplitMaxUnion) return 0;
+  return nparts;
+}
+
+size_t route_split_workspace(int batch, int nq, int n_rows, int m) {
+  const int64_t nqt = static_cast<int64_t>(batch) * nq;
+  const int nparts = route_split_parts(nqt, n_rows, m);
+  if (nparts == 0) return 0;
+  return align256(static_cast<size_t>(nqt) * nparts * (m - 2) * sizeof(uint2));
+}
+
+static hipError_t launch_route_split(const uint16_t* qidx, Str3 qs, const int32_t* q_pos,
+                                     int batch, int nq, const uint16_t* split, int n_rows, int d,
+                                     int B, int m, int32_t* block_idx, void* ws, hipStream_t s) {
+  const int64_t nqt = static_cast<int64_t>(batch) * nq;
+  const int nparts = route_split_parts(nqt, n_rows, m);
+  const float invB = 1.0f / static_cast<float>(B);
+  uint2* parts = static_cast<uint2*>(ws);
+  const dim3 g1(static_cast<unsigned>(nparts), static_cast<unsigned>(nqt));
+  if (d == 64)
+    hipLaunchKernelGGL(route_part_kernel<64>, g1, dim3(64 * kPartWaves), 0, s, qidx, qs.b, qs.t,
+                       q_pos, nq, split, n_rows, B, invB, m, parts, nparts);
+  else
+    hipLaunchKernelGGL(route_part_kernel<128>, g1, dim3(64 * kPartWaves), 0, s, qidx, qs.b,
+                       qs.t, q_pos, nq, split, n_rows, B, invB, m, parts, nparts);
+  // merge: one wave while the survivors fit four items per lane, else four
+  // waves, each over a quarter of the parts (ceil(nparts / 4) * K <= 560
+  // entries since nparts * K <= 2048 and K <= 64), then wave 0 over their
+  // best K each
+  const int K = m - 2;
+  const dim3 g2(static_cast<unsigned>(nqt));
+  if (nparts * K <= 256) {
+    hipLaunchKernelGGL((route_merge_kernel<1, 4, 1>), g2, dim3(64), 0, s, q_pos, n_rows, B, m,
+                       parts, nparts, nparts, block_idx);
+  } else {
+    const int pw = (nparts + 3) / 4;  // parts per wave
+    hipLaunchKernelGGL((route_merge_kernel<4, 9, 4>), g2, dim3(256), 0, s, q_pos, n_rows, B, m,
+                       parts, nparts, pw, block_idx);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_route_blocks(const uint16_t* qidx, Str3 qs, const int32_t* q_pos, int batch,
                                int nq, const uint16_t* split, int n_rows, int d, int B, int m,
-                               int32_t* block_idx, hipStream_t s) {
+                               int32_t* block_idx, void* ws, hipStream_t s) {
+  if (ws != nullptr && route_split_workspace(batch, nq, n_rows, m) > 0)
+    return launch_route_split(qidx, qs, q_pos, batch, nq, split, n_rows, d, B, m, block_idx, ws,
+                              s);
   const int ntq = (nq + kRouteQT - 1) / kRouteQT;
   const unsigned grid_wg =
       static_cast<unsigned>((static_cast<int64_t>(batch) * ntq + 7) / 8 * 8);

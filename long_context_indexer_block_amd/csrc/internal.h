@@ -65,9 +65,13 @@ hipError_t launch_mla_attn(const uint16_t* q, Str3 qs, const uint16_t* kv, Str3 
 constexpr int kRouteMaxRows = 64 * 16 + 2;
 constexpr int kRouteStreamMaxM = 130;
 constexpr int kRouteStreamMaxRows = 65537;  // candidate positions fit 16 bits
+// with ws (route_split_workspace() bytes, 0 when the shape does not split)
+// and fewer than 1024 queries, each query's blocks are scored and selected in
+// parts over several workgroups and merged
+size_t route_split_workspace(int batch, int nq, int n_rows, int m);
 hipError_t launch_route_blocks(const uint16_t* qidx, Str3 qs, const int32_t* q_pos, int batch,
                                int nq, const uint16_t* split, int n_rows, int d, int B, int m,
-                               int32_t* block_idx, hipStream_t s);
+                               int32_t* block_idx, void* ws, hipStream_t s);
 
 // tokens.hip: (query, slot) entries of a [batch][nq][m] block list bucketed by
 // (sequence, block), in tiles of kPairTile entries

@@ -17,7 +17,7 @@ import torch
 from . import (flat_indexer_topk, flat_indexer_topk_workspace_bytes, hils_two_level_attn_fwd,
                hils_prefill_workspace, hils_two_level_prefill_fwd, hils_workspace,
                hisa_auto_plan, route_supported, hisa_block_score, hisa_block_summary,
-               hisa_block_summary_update, hisa_route_blocks, hisa_select_blocks,
+               hisa_block_summary_update, hisa_route_blocks, hisa_select_blocks, route_workspace,
                hisa_token_select, hisa_token_select_workspace_bytes, sparse_attn_fwd,
                sparse_attn_workspace)
 
@@ -241,6 +241,9 @@ class DecodeSession:
         n = lib().sparse_attn_fwd_workspace_bytes(b, 1, Hq, Hkv, Dk, Dv, k_top)
         self.attn_ws = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
         self.out = torch.empty(b, 1, Hq, Dv, dtype=torch.bfloat16, device=dev)
+        # one query per sequence: blocks scored and selected in parts over
+        # several workgroups when the shape allows it (same block_idx)
+        self.route_ws = route_workspace(b, 1, cap, m, dev)
         self.L = 0
         self.grow(L)
 
@@ -256,8 +259,12 @@ class DecodeSession:
     def step(self, q, qidx):
         """q [b, 1, Hq, Dk], qidx [b, 1, d]: the queries at position L-1."""
         L = self.L
-        hisa_block_score(qidx, self.q_pos, self.split, self.B, out=self.block_scores)
-        hisa_select_blocks(self.block_scores, self.q_pos, self.B, self.m, out=self.block_idx)
+        if self.route_ws is not None:
+            hisa_route_blocks(qidx, self.q_pos, self.split, self.B, self.m, out=self.block_idx,
+                              workspace=self.route_ws)
+        else:
+            hisa_block_score(qidx, self.q_pos, self.split, self.B, out=self.block_scores)
+            hisa_select_blocks(self.block_scores, self.q_pos, self.B, self.m, out=self.block_idx)
         hisa_token_select(qidx, self.kidx[:, :L], self.q_pos, self.block_idx, self.B, self.k_top,
                           token_idx=self.token_idx, want_scores=False, workspace=self.ws)
         sparse_attn_fwd(q, self.kc[:, :L], self.vc[:, :L], self.token_idx, self.scale,
@@ -291,6 +298,9 @@ class HilsDecode:
         self.chunk_idx = torch.empty(b * H, 1, m, dtype=torch.int32, device=dev)
         self.out = torch.empty(b, H, D, dtype=torch.bfloat16, device=dev)
         self.ws = hils_workspace(b, H, D, m, dev)
+        # few (sequence, head) pairs over many chunks: routed in parts over
+        # several workgroups (same chunk_idx as score then select)
+        self.route_ws = route_workspace(b * H, 1, n, m, dev)
 
     def build_keys(self):
         # every (sequence, head) pair is one routed sequence: x[bi] viewed as
@@ -304,8 +314,12 @@ class HilsDecode:
     def route(self):
         b, H, D = self.q.shape
         qv = self.q.reshape(b * H, 1, D)
-        hisa_block_score(qv, self.q_pos, self.split, self.C, out=self.scores)
-        hisa_select_blocks(self.scores, self.q_pos, self.C, self.m, out=self.chunk_idx)
+        if self.route_ws is not None:
+            hisa_route_blocks(qv, self.q_pos, self.split, self.C, self.m, out=self.chunk_idx,
+                              workspace=self.route_ws)
+        else:
+            hisa_block_score(qv, self.q_pos, self.split, self.C, out=self.scores)
+            hisa_select_blocks(self.scores, self.q_pos, self.C, self.m, out=self.chunk_idx)
 
     def attend(self):
         hils_two_level_attn_fwd(self.q, self.k, self.v, self.khat, self.chunk_idx.view(-1, self.m),

@@ -27,12 +27,12 @@ def _declared():
 
 def test_exports_match_header():
     names = _declared()
-    assert len(names) == 20
+    assert len(names) == 21
     lib = ctypes.CDLL(H.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(H.EXPORTS) == names
-    assert H.lib().hisa_abi_version() == 2
+    assert H.lib().hisa_abi_version() == 3
 
 
 def _err():
@@ -229,7 +229,7 @@ def test_hils_validation():
 def test_route_validation():
     L = H.lib()
     s = S(0, 64, 0)
-    args = [FAKE, s, FAKE, 1, 4096, FAKE, 64, 64, 64, 32, FAKE, NULL]
+    args = [FAKE, s, FAKE, 1, 4096, FAKE, 64, 64, 64, 32, FAKE, NULL, 0, NULL]
     a = list(args)
     a[6], a[9] = 1027, 131                       # too many blocks for LDS, m too large to stream
     assert L.hisa_route_blocks(*a) == 3 and "hisa_block_score" in _err()
@@ -245,6 +245,27 @@ def test_route_validation():
     a = list(args)
     a[10] = NULL                                                     # no output
     assert L.hisa_route_blocks(*a) == 1
+
+
+def test_route_workspace():
+    L = H.lib()
+    # few queries over many blocks split their blocks over workgroups
+    need = L.hisa_route_blocks_workspace_bytes(64, 1, 1024, 64)      # 128K decode batch
+    assert need > 0 and need % 256 == 0
+    assert need >= 64 * 4 * 62 * 8
+    assert L.hisa_route_blocks_workspace_bytes(16, 1, 16384, 32) > 0  # 1M two-level decode
+    assert L.hisa_route_blocks_workspace_bytes(1, 4096, 1024, 64) == 0  # many queries
+    assert L.hisa_route_blocks_workspace_bytes(64, 1, 1024, 67) == 0    # m - 2 > 64
+    assert L.hisa_route_blocks_workspace_bytes(1, 1, 65537, 64) == 0    # too many survivors
+    assert L.hisa_route_blocks_workspace_bytes(0, 1, 1024, 64) == 0
+    s = S(0, 128, 0)
+    args = [FAKE, s, FAKE, 64, 1, FAKE, 1024, 128, 128, 64, FAKE, FAKE, need, NULL]
+    a = list(args)
+    a[12] = need - 1                                                 # too small
+    assert L.hisa_route_blocks(*a) == 5 and "needs" in _err()
+    a = list(args)
+    a[11] = ctypes.c_void_p(0x10010)                                 # not 256-byte aligned
+    assert L.hisa_route_blocks(*a) == 5 and "aligned" in _err()
 
 
 def test_hils_prefill_validation():

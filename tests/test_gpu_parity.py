@@ -862,13 +862,23 @@ ROUTE_CASES = [
     # scores held on chip (m above the streamed selection's limit of 130)
     (1, 300, 65600, 64, 64, 200, "random", 1),
     (2, 100, 40000, 128, 128, 140, "prefill", 8),
+    # one query per sequence (decode): with the workspace the blocks of each
+    # query are split over workgroups in parts of 256 and merged; a 1M-token
+    # cache in 64-token chunks (16384 blocks, 64 parts, 1920 survivors), mass
+    # ties, one free slot, queries with fewer candidates than slots
+    (16, 1, 131072, 128, 128, 64, "last", 8),
+    (4, 1, 1048576, 64, 64, 32, "last", 8),
+    (8, 1, 65536, 64, 64, 64, "random", 1),
+    (8, 1, 65536, 64, 64, 3, "random", 1),
+    (32, 1, 16384, 128, 64, 40, "random", 8),
 ]
 
 
+@pytest.mark.parametrize("split", [True, False], ids=["workspace", "no_workspace"])
 @pytest.mark.parametrize("case", ROUTE_CASES, ids=[f"n{c[2] // c[3]}_q{c[1]}" for c in ROUTE_CASES])
-def test_route_blocks_equals_score_then_select(case):
+def test_route_blocks_equals_score_then_select(case, split):
     b, nq, L, B, d, m, kind, vr = case
-    log(f"case fused route {case}")
+    log(f"case fused route {case} workspace={split}")
     g = torch.Generator(device=DEV).manual_seed(7)
     kidx = torch.randint(-vr, vr + 1, (b, L, d), generator=g, device=DEV).to(torch.bfloat16)
     qidx = torch.randint(-vr, vr + 1, (b, nq, d), generator=g, device=DEV).to(torch.bfloat16)
@@ -878,10 +888,14 @@ def test_route_blocks_equals_score_then_select(case):
         q_pos = torch.full((b, nq), L - 1, dtype=torch.int32, device=DEV)
     else:
         q_pos = torch.arange(L - nq, L, dtype=torch.int32, device=DEV).expand(b, nq).contiguous()
-    q_pos[:, :3] = torch.tensor([0, B - 1, B], dtype=torch.int32, device=DEV)
-    _, split = H.hisa_block_summary(kidx, B)
-    ref = H.hisa_select_blocks(H.hisa_block_score(qidx, q_pos, split, B), q_pos, B, m)
-    got = H.hisa_route_blocks(qidx, q_pos, split, B, m)
+    edges = torch.tensor([0, B - 1, B], dtype=torch.int32, device=DEV)
+    if nq >= 3:
+        q_pos[:, :3] = edges
+    elif b >= 8:
+        q_pos[:3, 0] = edges  # the first block's queries, one per sequence
+    _, split_t = H.hisa_block_summary(kidx, B)
+    ref = H.hisa_select_blocks(H.hisa_block_score(qidx, q_pos, split_t, B), q_pos, B, m)
+    got = H.hisa_route_blocks(qidx, q_pos, split_t, B, m, workspace="auto" if split else None)
     torch.cuda.synchronize()
     check_index_rows(got.view(-1, m).cpu().numpy(), ref.view(-1, m).cpu().numpy(), "fused route")
 
