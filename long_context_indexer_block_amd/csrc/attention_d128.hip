@@ -159,6 +159,7 @@ __device__ __forceinline__ uint32_t gather_ids(const Item& it, int t, uint4* kd,
     const int row = ok ? idv[u] : 0;
     const int c = p ^ swz(r);
     if constexpr (OFF32) {
+      __builtin_assume(static_cast<uint32_t>(row) < (1u << 24));  // row < L < 2^24
       const uint32_t ko = __umul24(static_cast<uint32_t>(row), it.kbytes) + 16u * c;
       const uint32_t vo = __umul24(static_cast<uint32_t>(row), it.vbytes) + 16u * c;
       __builtin_amdgcn_global_load_lds(
@@ -228,12 +229,13 @@ __device__ __forceinline__ void tile(State& st, const Frags& f, int t, float sca
   s0 = mfma16(as_bf16x8(f.k[2]), st.qf[2], s0);
   s1 = mfma16(as_bf16x8(f.k[3]), st.qf[3], s1);
   float sv[4];
-  float tmax = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    sv[e] = ((st.m0 >> (4 * g + e)) & 1u) ? (s0[e] + s1[e]) * scale_log2 : -INFINITY;
-    tmax = fmaxf(tmax, sv[e]);
+  for (int e = 0; e < 4; ++e) sv[e] = (s0[e] + s1[e]) * scale_log2;
+  if (st.m0 != 0xFFFFu) {  // holes or the list's end: drop the invalid tokens
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sv[e] = ((st.m0 >> (4 * g + e)) & 1u) ? sv[e] : -INFINITY;
   }
+  float tmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
   tmax = max_x16_x32(tmax);
   // ---- reference: set on the first tile, raised when exceeded by far
   const bool up = t == 0 || tmax > st.R + kRaise;
