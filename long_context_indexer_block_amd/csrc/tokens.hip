@@ -504,24 +504,254 @@ __global__ __launch_bounds__(256) void token_topk_kernel(
 // 64r + l of row r. Each row is one slot's 64 consecutive tokens (B is a
 // multiple of 64), so the slot's block id is uniform per row and the loads
 // are coalesced. Candidates that are not valid (empty slot, token after the
-// query) are held as NaN, which no comparison keeps. The threshold search is
-// the shared one; the compaction ranks each row with ballots and takes the
-// waves' offsets from one scan of their (kept, tied) counts.
-// row r of a candidate buffer (NaN past the last row); the loads are issued
-// together, before any of them is used
-__device__ __forceinline__ float r_load(const float* row, int r, int nrows, int l) {
-  return r < nrows ? row[r * 64 + l] : __uint_as_float(0x7fc00000u);
+// query) are held as the quiet NaN 0x7fc00000, which no comparison keeps.
+//
+// The threshold search is specialised for candidates held in registers:
+//   1. min, max and count of the valid candidates;
+//   2. a histogram of kRowBins linear bins over [min, max] (LDS atomics) and
+//      the bin beta holding the K-th largest value, with the count above it;
+//   3. if beta holds at most kRowList candidates they are copied to LDS and
+//      every wave ranks them (each against all of them) to find the
+//      (K - above)-th largest exactly; otherwise the range shrinks to the
+//      bin's own min and max and step 2 repeats (at most kRowLevels times),
+//      an exact bisection on order-preserving keys finishing a search that
+//      is still open.
+// The bins are a monotone function of the value, so every candidate of a
+// higher bin is larger than every candidate of bin beta, and the ranks
+// inside the bin decide the threshold T and the number of candidates equal
+// to T that are kept. The compaction ranks each row with ballots and takes
+// the waves' offsets from one exchange of their (kept, tied) counts.
+constexpr int kRowBins = 2048;
+constexpr int kRowList = 64;
+constexpr int kRowLevels = 3;
+
+template <int W>
+struct RowSelLds {
+  uint32_t hist[kRowBins];
+  float wmn[W], wmx[W];
+  uint32_t wn[W];
+  uint32_t part[W];
+  uint32_t wcnt[2][W];
+  float list[W][kRowList];
+  uint32_t nlist[W];
+  int beta;
+  uint32_t above, hbeta;
+};
+
+// min / max that pass over the non-candidates: with a quiet NaN operand the
+// instructions return the other operand. Written out because the library
+// forms first quieten each operand, an instruction per candidate.
+__device__ __forceinline__ float min_skip_nan(float a, float b) {
+  float r;
+  asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
+__device__ __forceinline__ float max_skip_nan(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+// An opaque copy of the candidates at the start of each pass: the
+// comparisons of a pass are recomputed instead of being kept from an earlier
+// pass as lane masks, which would take two scalar registers per row.
+template <int RW>
+__device__ __forceinline__ void new_pass(float (&v)[RW]) {
+#pragma unroll
+  for (int i = 0; i < RW; ++i) asm volatile("" : "+v"(v[i]));
+}
+// Lanes of the wave for which p holds. The count is taken in an ordered
+// (volatile) statement so that each row's lane mask dies at once: left to
+// the compiler, the compares of all rows are issued ahead of the counts and
+// their masks, two scalar registers each, spill.
+__device__ __forceinline__ uint32_t row_count(bool p) {
+  const uint64_t m = __ballot(p);
+  uint32_t c;
+  asm volatile("s_bcnt1_i32_b64 %0, %1" : "=s"(c) : "s"(m));
+  return c;
+}
+
+// Sum over the workgroup of a wave-uniform count (two barriers).
+template <int W>
+__device__ __forceinline__ uint32_t rows_block_sum(uint32_t c, RowSelLds<W>& sh, int wv, int l) {
+  if (l == 0) sh.wn[wv] = c;
+  __syncthreads();
+  uint32_t s = 0;
+#pragma unroll
+  for (int u = 0; u < W; ++u) s += sh.wn[u];
+  __syncthreads();
+  return s;
+}
+// Min and max over the workgroup of per-lane values (NaN-free).
+template <int W>
+__device__ __forceinline__ void rows_block_minmax(float& mn, float& mx, RowSelLds<W>& sh, int wv,
+                                                  int l) {
+  mn = wave_ext_dpp<false>(mn);
+  mx = wave_ext_dpp<true>(mx);
+  if (l == 0) {
+    sh.wmn[wv] = mn;
+    sh.wmx[wv] = mx;
+  }
+  __syncthreads();
+  mn = sh.wmn[0];
+  mx = sh.wmx[0];
+#pragma unroll
+  for (int u = 1; u < W; ++u) {
+    mn = fminf(mn, sh.wmn[u]);
+    mx = fmaxf(mx, sh.wmx[u]);
+  }
+  __syncthreads();
+}
+
+template <int RW, int W>
+__device__ Threshold rows_threshold(float (&v)[RW], float lo, float hi, int krem,
+                                    RowSelLds<W>& sh, int wv, int l) {
+  constexpr int NT = 64 * W, NB = kRowBins;
+  constexpr int BPT = NB / NT;  // bins per thread in the search for beta
+  static_assert(NB % NT == 0, "bins per thread");
+  for (int level = 0; level < kRowLevels; ++level) {
+    if (lo == hi) return Threshold{lo, krem};
+    const float half_w = hi * 0.5f - lo * 0.5f;
+    if (!(half_w > 0.0f)) break;
+    // bin of x in [lo, hi]: monotone in x, and (x/2 - lo/2) <= half_w keeps
+    // the product at most NB (1 + 2^-23) without overflow
+    const float scale = static_cast<float>(NB) / half_w;
+    const float lo_h = lo * 0.5f;
+    auto binof = [&](float x) {
+      const int b = static_cast<int>(__builtin_fmaf(x, 0.5f, -lo_h) * scale);
+      return b < NB - 1 ? b : NB - 1;
+    };
+    if (level > 0) {  // level 0 found the bins cleared at the start
+#pragma unroll
+      for (int b = 0; b < BPT; ++b) sh.hist[threadIdx.x * BPT + b] = 0u;
+      __syncthreads();
+    }
+    new_pass(v);
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const float x = v[i];
+      if (x >= lo && x <= hi) atomicAdd(&sh.hist[binof(x)], 1u);
+    }
+    __syncthreads();
+    // Thread t owns bins NB - BPT(t+1) .. NB - BPT t - 1: thread 0 the top
+    // ones. Candidates above a thread's bins: the counts of the threads
+    // before it (one scan per wave, one exchange of the wave totals).
+    const int b0 = NB - BPT * (static_cast<int>(threadIdx.x) + 1);
+    uint32_t h[BPT];
+    uint32_t local = 0;
+#pragma unroll
+    for (int b = 0; b < BPT; ++b) {
+      h[b] = sh.hist[b0 + b];
+      local += h[b];
+    }
+    const uint32_t inc = wave_scan_dpp(local);
+    if (l == 63) sh.part[wv] = inc;
+    __syncthreads();
+    uint32_t acc = inc - local;
+#pragma unroll
+    for (int u = 0; u < W; ++u) acc += u < wv ? sh.part[u] : 0u;
+    const uint32_t kr = static_cast<uint32_t>(krem);
+#pragma unroll
+    for (int b = BPT - 1; b >= 0; --b) {
+      if (acc < kr && acc + h[b] >= kr) {
+        sh.beta = b0 + b;
+        sh.above = acc;
+        sh.hbeta = h[b];
+      }
+      acc += h[b];
+    }
+    __syncthreads();
+    const int beta = sh.beta;
+    krem -= static_cast<int>(sh.above);
+    const uint32_t hbeta = sh.hbeta;
+    if (hbeta <= static_cast<uint32_t>(kRowList)) {
+      // ---- the bin's candidates to LDS, this wave's at list[wv]
+      uint32_t nl = 0;
+      new_pass(v);
+#pragma unroll
+      for (int i = 0; i < RW; ++i) {
+        const float x = v[i];
+        const bool in = x >= lo && x <= hi && binof(x) == beta;
+        const uint64_t bm = __ballot(in);
+        if (bm != 0ull) {
+          const uint32_t at = nl + lanes_below(bm);
+          if (in && at < static_cast<uint32_t>(kRowList)) sh.list[wv][at] = x;
+          nl += static_cast<uint32_t>(__popcll(bm));
+        }
+      }
+      if (l == 0) sh.nlist[wv] = min(nl, static_cast<uint32_t>(kRowList));
+      __syncthreads();
+      // ---- every wave: lane j takes candidate j of the bin, counts the
+      // candidates above it and equal to it; the krem-th largest is the one
+      // with gt < krem <= gt + eq
+      float x = __uint_as_float(0x7fc00000u);
+      int total = 0;
+#pragma unroll
+      for (int u = 0; u < W; ++u) {
+        const int nu = static_cast<int>(sh.nlist[u]);
+        if (l >= total && l < total + nu) x = sh.list[u][l - total];
+        total += nu;
+      }
+      total = min(total, kRowList);  // equal to the bin's count, at most kRowList
+      uint32_t gt = 0, eq = 0;
+      for (int j = 0; j < total; ++j) {
+        const float y = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), j));
+        gt += y > x ? 1u : 0u;
+        eq += y == x ? 1u : 0u;
+      }
+      const uint32_t kq = static_cast<uint32_t>(krem);
+      const uint64_t hit = __ballot(l < total && gt < kq && gt + eq >= kq);
+      const int ls = static_cast<int>(__builtin_ctzll(hit));
+      const float T = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), ls));
+      const int gts = __builtin_amdgcn_readlane(static_cast<int>(gt), ls);
+      return Threshold{T, krem - gts};
+    }
+    // ---- the bin's own range
+    float bmn = INFINITY, bmx = -INFINITY;
+    new_pass(v);
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const float x = v[i];
+      if (x >= lo && x <= hi && binof(x) == beta) {
+        bmn = fminf(bmn, x);
+        bmx = fmaxf(bmx, x);
+      }
+    }
+    rows_block_minmax<W>(bmn, bmx, sh, wv, l);
+    lo = bmn;
+    hi = bmx;
+  }
+  if (lo == hi) return Threshold{lo, krem};
+  // Exact bisection on order keys within [lo, hi]: the largest key x with
+  // count(values in [x, hi]) >= krem.
+  uint32_t klo = order_key(lo), khi = order_key(hi);
+  while (klo < khi) {
+    const uint32_t mid = klo + ((khi - klo + 1u) >> 1);
+    const float fm = key_value(mid);
+    uint32_t c = 0;
+    new_pass(v);
+#pragma unroll
+    for (int i = 0; i < RW; ++i) c += row_count(v[i] >= fm && v[i] <= hi);
+    const uint32_t tot = rows_block_sum<W>(c, sh, wv, l);
+    if (tot >= static_cast<uint32_t>(krem)) klo = mid; else khi = mid - 1u;
+  }
+  const float T = key_value(klo);
+  uint32_t c = 0;
+  new_pass(v);
+#pragma unroll
+  for (int i = 0; i < RW; ++i) c += row_count(v[i] > T && v[i] <= hi);
+  const uint32_t tgt = rows_block_sum<W>(c, sh, wv, l);
+  return Threshold{T, krem - static_cast<int>(tgt)};
+}
+
 // The register budget allows 5 waves per SIMD: the kernel is latency bound
 // (barriers, LDS atomics), so more resident workgroups hide more of it.
-template <int RW, int W, int NS>
+template <int RW, int W>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(5, 8))) void
 token_topk_rows_kernel(const float* __restrict__ scores, const int32_t* __restrict__ block_idx,
                        const int32_t* __restrict__ q_pos, int m, int B, int k, int L,
                        int32_t* __restrict__ token_idx, float* __restrict__ token_scores) {
-  constexpr int NT = 64 * W, NB = 2048;
-  __shared__ SelectLds<NT, NB> sh;
-  __shared__ uint32_t wcnt[2][W];
+  constexpr int NT = 64 * W, NB = kRowBins;
+  __shared__ RowSelLds<W> sh;
   extern __shared__ uint4 stage[];  // k ids, then k scores when asked for
   const int64_t qi = blockIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -532,91 +762,116 @@ token_topk_rows_kernel(const float* __restrict__ scores, const int32_t* __restri
   const int nrows = (m * B) >> 6;
   const float* row = scores + qi * static_cast<int64_t>(m) * B;
   const float qnan = __uint_as_float(0x7fc00000u);
-  // the slots' block ids, one per lane in NS registers (m <= 64*NS), read by
-  // row with readlane; a slot that is empty or past the end of the keys gets -1
-  int cv[NS];
 #pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    const int c = 64 * j + l < m ? block_idx[qi * m + 64 * j + l] : -1;
-    cv[j] = c >= 0 && c < nblk ? c : -1;
+  for (int b = 0; b < NB / NT; ++b) sh.hist[threadIdx.x * (NB / NT) + b] = 0u;
+  // this wave's rows lie in slots s0 .. s0 + RW - 1: their block ids, one
+  // per lane (-1 for an empty slot, one past the end of the keys or of m)
+  const int r0 = RW * wv;
+  const int s0 = r0 >> lrpb;
+  int cw;
+  {
+    const int s = s0 + l;
+    const int c = l < RW && s < m ? block_idx[qi * m + s] : -1;
+    cw = c >= 0 && c < nblk ? c : -1;
   }
-  auto slot_block = [&](int sl) {  // sl is wave-uniform
-    int v = cv[0];
-#pragma unroll
-    for (int j = 1; j < NS; ++j) v = sl >= 64 * j ? cv[j] : v;
-    return __builtin_amdgcn_readlane(v, sl & 63);
-  };
+  // the rows, all loads issued before any is used (a row past the last one
+  // loads the last one again and is masked below)
   float v[RW];
 #pragma unroll
-  for (int i = 0; i < RW; ++i) v[i] = r_load(row, RW * wv + i, nrows, l);
+  for (int i = 0; i < RW; ++i) v[i] = row[min(r0 + i, nrows - 1) * 64 + l];
+  // first token of row r0 + i (wave-uniform), or -1 for a row without
+  // candidates; r0 is passed in so that the compaction can recompute it
+  auto row_base = [&](int r0x, int i) {
+    const int r = r0x + i;
+    const int c = __builtin_amdgcn_readlane(cw, (r >> lrpb) - (r0x >> lrpb));
+    return r < nrows && c >= 0 ? c * B + (r & ((1 << lrpb) - 1)) * 64 : -1;
+  };
+  // tokens after the query are not candidates: lane l of row r is one iff
+  // base + l <= t
 #pragma unroll
   for (int i = 0; i < RW; ++i) {
-    const int r = RW * wv + i;
-    if (r < nrows) {
-      const int sl = r >> lrpb;
-      const int c = slot_block(sl);
-      const int j = c * B + (r & ((1 << lrpb) - 1)) * 64 + l;
-      if (c < 0 || j > t) v[i] = qnan;
-    }
+    const int base = row_base(r0, i);
+    const int lim = base >= 0 ? t - base : -1;
+    v[i] = l <= lim ? v[i] : qnan;
   }
-  auto get = [&](int, int i, float& x) -> bool {
-    x = v[i];
-    return x == x;
-  };
-  const Threshold th = select_threshold<NT, RW, NB>(get, 1, k, sh);
+  // ---- count, min and max of the candidates
+  float mn = INFINITY, mx = -INFINITY;
+  uint32_t nw = 0;
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    mn = min_skip_nan(mn, v[i]);
+    mx = max_skip_nan(mx, v[i]);
+    nw += row_count(v[i] == v[i]);
+  }
+  mn = wave_ext_dpp<false>(mn);
+  mx = wave_ext_dpp<true>(mx);
+  if (l == 0) {
+    sh.wmn[wv] = mn;
+    sh.wmx[wv] = mx;
+    sh.wn[wv] = nw;
+  }
+  __syncthreads();
+  uint32_t n = 0;
+  float lo = sh.wmn[0], hi = sh.wmx[0];
+#pragma unroll
+  for (int u = 0; u < W; ++u) {
+    n += sh.wn[u];
+    lo = fminf(lo, sh.wmn[u]);
+    hi = fmaxf(hi, sh.wmx[u]);
+  }
+  __syncthreads();
+  const Threshold th = n <= static_cast<uint32_t>(k)
+                           ? Threshold{-INFINITY, 0x7fffffff}
+                           : rows_threshold<RW, W>(v, lo, hi, k, sh, wv, l);
   // ---- compaction: this wave's counts, then the waves before it; the kept
   // ids (and scores) are ranked into LDS and written out with 16-byte stores
   const uint32_t need = static_cast<uint32_t>(th.need);
   uint32_t gtw = 0, eqw = 0;
+  new_pass(v);
 #pragma unroll
   for (int i = 0; i < RW; ++i) {
-    gtw += static_cast<uint32_t>(__popcll(__ballot(v[i] > th.T)));
-    eqw += static_cast<uint32_t>(__popcll(__ballot(v[i] == th.T)));
+    gtw += row_count(v[i] > th.T);
+    eqw += row_count(v[i] == th.T);
   }
   if (l == 0) {
-    wcnt[0][wv] = gtw;
-    wcnt[1][wv] = eqw;
+    sh.wcnt[0][wv] = gtw;
+    sh.wcnt[1][wv] = eqw;
   }
   __syncthreads();
   uint32_t gtb = 0, ties = 0, gta = 0, tia = 0;
 #pragma unroll
   for (int u = 0; u < W; ++u) {
-    gtb += u < wv ? wcnt[0][u] : 0u;
-    ties += u < wv ? wcnt[1][u] : 0u;
-    gta += wcnt[0][u];
-    tia += wcnt[1][u];
+    gtb += u < wv ? sh.wcnt[0][u] : 0u;
+    ties += u < wv ? sh.wcnt[1][u] : 0u;
+    gta += sh.wcnt[0][u];
+    tia += sh.wcnt[1][u];
   }
   const uint32_t kept_all = gta + min(tia, need);
   uint32_t kept = gtb + min(ties, need);
   int32_t* sid = reinterpret_cast<int32_t*>(stage);
   float* ssc = token_scores ? reinterpret_cast<float*>(stage) + k : nullptr;
-  uint32_t kept0 = kept, ties0 = ties;
-  // the masks of the counting pass are recomputed, not kept in scalar registers
-#pragma unroll
-  for (int i = 0; i < RW; ++i) asm volatile("" : "+v"(v[i]));
+  new_pass(v);
+  int r0c = r0;  // the row bases are recomputed too
+  asm volatile("" : "+v"(cw), "+s"(r0c));
 #pragma unroll
   for (int i = 0; i < RW; ++i) {
-    const int r = RW * wv + i;
-    const uint64_t em = __ballot(v[i] == th.T);
-    const bool keep = v[i] > th.T || (v[i] == th.T && ties + lanes_below(em) < need);
+    const float x = v[i];
+    const uint64_t em = __ballot(x == th.T);
+    bool keep;
+    if (em == 0ull) {
+      keep = x > th.T;
+    } else {
+      keep = x > th.T || (x == th.T && ties + lanes_below(em) < need);
+      ties += static_cast<uint32_t>(__popcll(em));
+    }
     const uint64_t km = __ballot(keep);
-    const int id = slot_block(r >> lrpb) * B + (r & ((1 << lrpb) - 1)) * 64 + l;
-    if (keep) sid[kept + lanes_below(km)] = id;
-    ties += static_cast<uint32_t>(__popcll(em));
-    kept += static_cast<uint32_t>(__popcll(km));
-  }
-  if (ssc) {
-    // the same ranks for the scores
-#pragma unroll
-    for (int i = 0; i < RW; ++i) asm volatile("" : "+v"(v[i]));
-#pragma unroll
-    for (int i = 0; i < RW; ++i) {
-      const uint64_t em = __ballot(v[i] == th.T);
-      const bool keep = v[i] > th.T || (v[i] == th.T && ties0 + lanes_below(em) < need);
-      const uint64_t km = __ballot(keep);
-      if (keep) ssc[kept0 + lanes_below(km)] = v[i];
-      ties0 += static_cast<uint32_t>(__popcll(em));
-      kept0 += static_cast<uint32_t>(__popcll(km));
+    if (km != 0ull) {
+      const uint32_t pos = kept + lanes_below(km);
+      if (keep && pos < static_cast<uint32_t>(k)) {
+        sid[pos] = row_base(r0c, i) + l;
+        if (ssc) ssc[pos] = x;
+      }
+      kept += static_cast<uint32_t>(__popcll(km));
     }
   }
   __syncthreads();
@@ -697,12 +952,8 @@ hipError_t launch_token_select(const uint16_t* qidx, Str3 qs, const uint16_t* ki
     const dim3 gr(static_cast<unsigned>(nq_total));
 #define HISA_TR(R_, W_)                                                                        \
   do {                                                                                        \
-    if (m <= 128)                                                                             \
-      hipLaunchKernelGGL((token_topk_rows_kernel<R_, W_, 2>), gr, dim3(64 * W_), stage_bytes,   \
-                         s, w.scores, block_idx, q_pos, m, B, k, L, token_idx, token_scores);  \
-    else                                                                                      \
-      hipLaunchKernelGGL((token_topk_rows_kernel<R_, W_, 4>), gr, dim3(64 * W_), stage_bytes,   \
-                         s, w.scores, block_idx, q_pos, m, B, k, L, token_idx, token_scores);  \
+    hipLaunchKernelGGL((token_topk_rows_kernel<R_, W_>), gr, dim3(64 * W_), stage_bytes, s,    \
+                       w.scores, block_idx, q_pos, m, B, k, L, token_idx, token_scores);      \
   } while (0)
     if (nq_total < kFewQueries) {
       // few queries (decode): kWideW waves per query, so that the CUs that get
