@@ -505,9 +505,10 @@ __global__ __launch_bounds__(256) void token_topk_kernel(
 // multiple of 64), so the slot's block id is uniform per row and the loads
 // are coalesced. Candidates that are not valid (empty slot, token after the
 // query) are held as the quiet NaN 0x7fc00000, which no comparison keeps.
+// Scores of valid candidates are finite (products of finite bf16 rows).
 //
 // The threshold search is specialised for candidates held in registers:
-//   1. min, max and count of the valid candidates;
+//   1. min and max of the candidates (the count comes from the row bounds);
 //   2. a histogram of kRowBins linear bins over [min, max] (LDS atomics) and
 //      the bin beta holding the K-th largest value, with the count above it;
 //   3. if beta holds at most kRowList candidates they are copied to LDS and
@@ -520,7 +521,7 @@ __global__ __launch_bounds__(256) void token_topk_kernel(
 // higher bin is larger than every candidate of bin beta, and the ranks
 // inside the bin decide the threshold T and the number of candidates equal
 // to T that are kept. The compaction ranks each row with ballots and takes
-// the waves' offsets from one exchange of their (kept, tied) counts.
+// the waves' offsets from one exchange of their counts.
 constexpr int kRowBins = 2048;
 constexpr int kRowList = 64;
 constexpr int kRowLevels = 3;
@@ -538,6 +539,12 @@ struct RowSelLds {
   uint32_t above, hbeta;
 };
 
+struct RowThreshold {
+  float T;    // values > T are kept
+  int need;   // plus the first `need` values == T
+  bool all;   // every value == T is kept: keep exactly the values >= T
+};
+
 // min / max that pass over the non-candidates: with a quiet NaN operand the
 // instructions return the other operand. Written out because the library
 // forms first quieten each operand, an instruction per candidate.
@@ -549,6 +556,13 @@ __device__ __forceinline__ float min_skip_nan(float a, float b) {
 __device__ __forceinline__ float max_skip_nan(float a, float b) {
   float r;
   asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+// float -> int32 rounding towards zero, saturating, NaN -> 0 (the
+// instruction's defined behaviour, which the C++ conversion leaves undefined)
+__device__ __forceinline__ int cvt_i32_nan0(float x) {
+  int r;
+  asm("v_cvt_i32_f32 %0, %1" : "=v"(r) : "v"(x));
   return r;
 }
 // An opaque copy of the candidates at the start of each pass: the
@@ -602,14 +616,17 @@ __device__ __forceinline__ void rows_block_minmax(float& mn, float& mx, RowSelLd
   __syncthreads();
 }
 
+// K-th largest of the candidates v (NaN: not a candidate), given their min
+// lo < max hi and 1 <= K < their count. The histogram bins are cleared on
+// entry.
 template <int RW, int W>
-__device__ Threshold rows_threshold(float (&v)[RW], float lo, float hi, int krem,
-                                    RowSelLds<W>& sh, int wv, int l) {
+__device__ RowThreshold rows_threshold(float (&v)[RW], float lo, float hi, int krem,
+                                       RowSelLds<W>& sh, int wv, int l) {
   constexpr int NT = 64 * W, NB = kRowBins;
   constexpr int BPT = NB / NT;  // bins per thread in the search for beta
   static_assert(NB % NT == 0, "bins per thread");
   for (int level = 0; level < kRowLevels; ++level) {
-    if (lo == hi) return Threshold{lo, krem};
+    if (lo == hi) return RowThreshold{lo, krem, false};
     const float half_w = hi * 0.5f - lo * 0.5f;
     if (!(half_w > 0.0f)) break;
     // bin of x in [lo, hi]: monotone in x, and (x/2 - lo/2) <= half_w keeps
@@ -617,19 +634,23 @@ __device__ Threshold rows_threshold(float (&v)[RW], float lo, float hi, int krem
     const float scale = static_cast<float>(NB) / half_w;
     const float lo_h = lo * 0.5f;
     auto binof = [&](float x) {
-      const int b = static_cast<int>(__builtin_fmaf(x, 0.5f, -lo_h) * scale);
+      const int b = cvt_i32_nan0(__builtin_fmaf(x, 0.5f, -lo_h) * scale);
       return b < NB - 1 ? b : NB - 1;
     };
-    if (level > 0) {  // level 0 found the bins cleared at the start
-#pragma unroll
-      for (int b = 0; b < BPT; ++b) sh.hist[threadIdx.x * BPT + b] = 0u;
-      __syncthreads();
-    }
     new_pass(v);
+    if (level == 0) {
+      // every candidate is in [lo, hi]; a non-candidate (NaN) lands in bin 0,
+      // which is only ever the bin of the K-th largest when all candidates
+      // above it number fewer than K: then the exact passes below, which
+      // skip NaN, take over (see the count check)
 #pragma unroll
-    for (int i = 0; i < RW; ++i) {
-      const float x = v[i];
-      if (x >= lo && x <= hi) atomicAdd(&sh.hist[binof(x)], 1u);
+      for (int i = 0; i < RW; ++i) atomicAdd(&sh.hist[binof(v[i])], 1u);
+    } else {
+#pragma unroll
+      for (int i = 0; i < RW; ++i) {
+        const float x = v[i];
+        if (x >= lo && x <= hi) atomicAdd(&sh.hist[binof(x)], 1u);
+      }
     }
     __syncthreads();
     // Thread t owns bins NB - BPT(t+1) .. NB - BPT t - 1: thread 0 the top
@@ -663,47 +684,62 @@ __device__ Threshold rows_threshold(float (&v)[RW], float lo, float hi, int krem
     const int beta = sh.beta;
     krem -= static_cast<int>(sh.above);
     const uint32_t hbeta = sh.hbeta;
+    // candidates of bin beta: x in [lo, hi] with binof(x) == beta
+    auto in_beta = [&](float x) { return x >= lo && x <= hi && binof(x) == beta; };
     if (hbeta <= static_cast<uint32_t>(kRowList)) {
-      // ---- the bin's candidates to LDS, this wave's at list[wv]
+      // ---- the bin's candidates to LDS, this wave's at list[wv]. A value
+      // window of the bin widened by two bins on each side (far more than
+      // the rounding of its ends) selects the rows that need the exact test.
+      const float wbin = 2.0f * half_w / static_cast<float>(NB);
+      const float wa = lo + static_cast<float>(beta - 2) * wbin;
+      const float wb = lo + static_cast<float>(beta + 3) * wbin;
       uint32_t nl = 0;
       new_pass(v);
 #pragma unroll
       for (int i = 0; i < RW; ++i) {
         const float x = v[i];
-        const bool in = x >= lo && x <= hi && binof(x) == beta;
-        const uint64_t bm = __ballot(in);
-        if (bm != 0ull) {
+        if (__ballot(x >= wa && x <= wb) != 0ull) {
+          const bool in = in_beta(x);
+          const uint64_t bm = __ballot(in);
           const uint32_t at = nl + lanes_below(bm);
           if (in && at < static_cast<uint32_t>(kRowList)) sh.list[wv][at] = x;
           nl += static_cast<uint32_t>(__popcll(bm));
         }
       }
-      if (l == 0) sh.nlist[wv] = min(nl, static_cast<uint32_t>(kRowList));
+      if (l == 0) sh.nlist[wv] = nl;
       __syncthreads();
-      // ---- every wave: lane j takes candidate j of the bin, counts the
-      // candidates above it and equal to it; the krem-th largest is the one
-      // with gt < krem <= gt + eq
-      float x = __uint_as_float(0x7fc00000u);
       int total = 0;
 #pragma unroll
-      for (int u = 0; u < W; ++u) {
-        const int nu = static_cast<int>(sh.nlist[u]);
-        if (l >= total && l < total + nu) x = sh.list[u][l - total];
-        total += nu;
+      for (int u = 0; u < W; ++u) total += static_cast<int>(sh.nlist[u]);
+      // All of the bin's candidates were found (a NaN counted in bin 0, or
+      // a window too narrow for the rounding of values far from zero, would
+      // leave fewer; all waves see the same total): rank them.
+      if (total == static_cast<int>(hbeta)) {
+        // lane j takes candidate j of the bin and counts the candidates above
+        // it and equal to it; the krem-th largest has gt < krem <= gt + eq
+        float x = __uint_as_float(0x7fc00000u);
+        int off = 0;
+#pragma unroll
+        for (int u = 0; u < W; ++u) {
+          const int nu = static_cast<int>(sh.nlist[u]);
+          if (l >= off && l < off + nu) x = sh.list[u][l - off];
+          off += nu;
+        }
+        uint32_t gt = 0, eq = 0;
+        for (int j = 0; j < total; ++j) {
+          const float y = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), j));
+          gt += y > x ? 1u : 0u;
+          eq += y == x ? 1u : 0u;
+        }
+        const uint32_t kq = static_cast<uint32_t>(krem);
+        const uint64_t hit = __ballot(l < total && gt < kq && gt + eq >= kq);
+        const int ls = static_cast<int>(__builtin_ctzll(hit));
+        const float T = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), ls));
+        const int gts = __builtin_amdgcn_readlane(static_cast<int>(gt), ls);
+        const int eqs = __builtin_amdgcn_readlane(static_cast<int>(eq), ls);
+        // every candidate equal to T is in this bin: eqs of them in all
+        return RowThreshold{T, krem - gts, krem - gts == eqs};
       }
-      total = min(total, kRowList);  // equal to the bin's count, at most kRowList
-      uint32_t gt = 0, eq = 0;
-      for (int j = 0; j < total; ++j) {
-        const float y = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), j));
-        gt += y > x ? 1u : 0u;
-        eq += y == x ? 1u : 0u;
-      }
-      const uint32_t kq = static_cast<uint32_t>(krem);
-      const uint64_t hit = __ballot(l < total && gt < kq && gt + eq >= kq);
-      const int ls = static_cast<int>(__builtin_ctzll(hit));
-      const float T = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), ls));
-      const int gts = __builtin_amdgcn_readlane(static_cast<int>(gt), ls);
-      return Threshold{T, krem - gts};
     }
     // ---- the bin's own range
     float bmn = INFINITY, bmx = -INFINITY;
@@ -711,7 +747,7 @@ __device__ Threshold rows_threshold(float (&v)[RW], float lo, float hi, int krem
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
       const float x = v[i];
-      if (x >= lo && x <= hi && binof(x) == beta) {
+      if (in_beta(x)) {
         bmn = fminf(bmn, x);
         bmx = fmaxf(bmx, x);
       }
@@ -719,8 +755,13 @@ __device__ Threshold rows_threshold(float (&v)[RW], float lo, float hi, int krem
     rows_block_minmax<W>(bmn, bmx, sh, wv, l);
     lo = bmn;
     hi = bmx;
+    // clear the bins for the next level (every read of them is behind the
+    // barriers of the min/max exchange)
+#pragma unroll
+    for (int b = 0; b < BPT; ++b) sh.hist[threadIdx.x * BPT + b] = 0u;
+    __syncthreads();
   }
-  if (lo == hi) return Threshold{lo, krem};
+  if (lo == hi) return RowThreshold{lo, krem, false};
   // Exact bisection on order keys within [lo, hi]: the largest key x with
   // count(values in [x, hi]) >= krem.
   uint32_t klo = order_key(lo), khi = order_key(hi);
@@ -740,7 +781,7 @@ __device__ Threshold rows_threshold(float (&v)[RW], float lo, float hi, int krem
 #pragma unroll
   for (int i = 0; i < RW; ++i) c += row_count(v[i] > T && v[i] <= hi);
   const uint32_t tgt = rows_block_sum<W>(c, sh, wv, l);
-  return Threshold{T, krem - static_cast<int>(tgt)};
+  return RowThreshold{T, krem - static_cast<int>(tgt), false};
 }
 
 // The register budget allows 5 waves per SIMD: the kernel is latency bound
@@ -764,44 +805,32 @@ token_topk_rows_kernel(const float* __restrict__ scores, const int32_t* __restri
   const float qnan = __uint_as_float(0x7fc00000u);
 #pragma unroll
   for (int b = 0; b < NB / NT; ++b) sh.hist[threadIdx.x * (NB / NT) + b] = 0u;
-  // this wave's rows lie in slots s0 .. s0 + RW - 1: their block ids, one
-  // per lane (-1 for an empty slot, one past the end of the keys or of m)
+  // Row r0 + j of this wave, in lane j < RW: its first token rbase (-1 for a
+  // row without candidates: past the last row, an empty slot, a block past
+  // the end of the keys) and rlim, the last lane that is a candidate (token
+  // rbase + lane <= t), -1 for none.
   const int r0 = RW * wv;
-  const int s0 = r0 >> lrpb;
-  int cw;
+  int rbase = -1;
   {
-    const int s = s0 + l;
-    const int c = l < RW && s < m ? block_idx[qi * m + s] : -1;
-    cw = c >= 0 && c < nblk ? c : -1;
+    const int r = r0 + l;
+    const int c = l < RW && r < nrows ? block_idx[qi * m + (r >> lrpb)] : -1;
+    if (c >= 0 && c < nblk) rbase = c * B + (r & ((1 << lrpb) - 1)) * 64;
   }
+  const int rlim = rbase >= 0 ? min(t - rbase, 63) : -1;
   // the rows, all loads issued before any is used (a row past the last one
-  // loads the last one again and is masked below)
+  // loads the last one again and is masked)
   float v[RW];
 #pragma unroll
   for (int i = 0; i < RW; ++i) v[i] = row[min(r0 + i, nrows - 1) * 64 + l];
-  // first token of row r0 + i (wave-uniform), or -1 for a row without
-  // candidates; r0 is passed in so that the compaction can recompute it
-  auto row_base = [&](int r0x, int i) {
-    const int r = r0x + i;
-    const int c = __builtin_amdgcn_readlane(cw, (r >> lrpb) - (r0x >> lrpb));
-    return r < nrows && c >= 0 ? c * B + (r & ((1 << lrpb) - 1)) * 64 : -1;
-  };
-  // tokens after the query are not candidates: lane l of row r is one iff
-  // base + l <= t
 #pragma unroll
-  for (int i = 0; i < RW; ++i) {
-    const int base = row_base(r0, i);
-    const int lim = base >= 0 ? t - base : -1;
-    v[i] = l <= lim ? v[i] : qnan;
-  }
+  for (int i = 0; i < RW; ++i) v[i] = l <= __builtin_amdgcn_readlane(rlim, i) ? v[i] : qnan;
   // ---- count, min and max of the candidates
+  const uint32_t nw = wave_sum_dpp(static_cast<uint32_t>(max(rlim + 1, 0)));
   float mn = INFINITY, mx = -INFINITY;
-  uint32_t nw = 0;
 #pragma unroll
   for (int i = 0; i < RW; ++i) {
     mn = min_skip_nan(mn, v[i]);
     mx = max_skip_nan(mx, v[i]);
-    nw += row_count(v[i] == v[i]);
   }
   mn = wave_ext_dpp<false>(mn);
   mx = wave_ext_dpp<true>(mx);
@@ -820,58 +849,90 @@ token_topk_rows_kernel(const float* __restrict__ scores, const int32_t* __restri
     hi = fmaxf(hi, sh.wmx[u]);
   }
   __syncthreads();
-  const Threshold th = n <= static_cast<uint32_t>(k)
-                           ? Threshold{-INFINITY, 0x7fffffff}
-                           : rows_threshold<RW, W>(v, lo, hi, k, sh, wv, l);
+  const RowThreshold th = n <= static_cast<uint32_t>(k)
+                              ? RowThreshold{-INFINITY, 0x7fffffff, true}
+                              : rows_threshold<RW, W>(v, lo, hi, k, sh, wv, l);
   // ---- compaction: this wave's counts, then the waves before it; the kept
   // ids (and scores) are ranked into LDS and written out with 16-byte stores
-  const uint32_t need = static_cast<uint32_t>(th.need);
-  uint32_t gtw = 0, eqw = 0;
-  new_pass(v);
-#pragma unroll
-  for (int i = 0; i < RW; ++i) {
-    gtw += row_count(v[i] > th.T);
-    eqw += row_count(v[i] == th.T);
-  }
-  if (l == 0) {
-    sh.wcnt[0][wv] = gtw;
-    sh.wcnt[1][wv] = eqw;
-  }
-  __syncthreads();
-  uint32_t gtb = 0, ties = 0, gta = 0, tia = 0;
-#pragma unroll
-  for (int u = 0; u < W; ++u) {
-    gtb += u < wv ? sh.wcnt[0][u] : 0u;
-    ties += u < wv ? sh.wcnt[1][u] : 0u;
-    gta += sh.wcnt[0][u];
-    tia += sh.wcnt[1][u];
-  }
-  const uint32_t kept_all = gta + min(tia, need);
-  uint32_t kept = gtb + min(ties, need);
   int32_t* sid = reinterpret_cast<int32_t*>(stage);
   float* ssc = token_scores ? reinterpret_cast<float*>(stage) + k : nullptr;
+  uint32_t kept_all, kept;
   new_pass(v);
-  int r0c = r0;  // the row bases are recomputed too
-  asm volatile("" : "+v"(cw), "+s"(r0c));
+  if (th.all) {
+    // every candidate >= T is kept
+    uint32_t gew = 0;
 #pragma unroll
-  for (int i = 0; i < RW; ++i) {
-    const float x = v[i];
-    const uint64_t em = __ballot(x == th.T);
-    bool keep;
-    if (em == 0ull) {
-      keep = x > th.T;
-    } else {
-      keep = x > th.T || (x == th.T && ties + lanes_below(em) < need);
-      ties += static_cast<uint32_t>(__popcll(em));
+    for (int i = 0; i < RW; ++i) gew += row_count(v[i] >= th.T);
+    if (l == 0) sh.wcnt[0][wv] = gew;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int u = 0; u < W; ++u) {
+      before += u < wv ? sh.wcnt[0][u] : 0u;
+      all += sh.wcnt[0][u];
     }
-    const uint64_t km = __ballot(keep);
-    if (km != 0ull) {
-      const uint32_t pos = kept + lanes_below(km);
-      if (keep && pos < static_cast<uint32_t>(k)) {
-        sid[pos] = row_base(r0c, i) + l;
-        if (ssc) ssc[pos] = x;
+    kept_all = all;
+    kept = before;
+    new_pass(v);
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const float x = v[i];
+      const bool keep = x >= th.T;
+      const uint64_t km = __ballot(keep);
+      if (km != 0ull) {
+        const uint32_t pos = kept + lanes_below(km);
+        if (keep && pos < static_cast<uint32_t>(k)) {
+          sid[pos] = __builtin_amdgcn_readlane(rbase, i) + l;
+          if (ssc) ssc[pos] = x;
+        }
+        kept += static_cast<uint32_t>(__popcll(km));
       }
-      kept += static_cast<uint32_t>(__popcll(km));
+    }
+  } else {
+    // only the first `need` candidates equal to T (in position order)
+    const uint32_t need = static_cast<uint32_t>(th.need);
+    uint32_t gtw = 0, eqw = 0;
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      gtw += row_count(v[i] > th.T);
+      eqw += row_count(v[i] == th.T);
+    }
+    if (l == 0) {
+      sh.wcnt[0][wv] = gtw;
+      sh.wcnt[1][wv] = eqw;
+    }
+    __syncthreads();
+    uint32_t gtb = 0, ties = 0, gta = 0, tia = 0;
+#pragma unroll
+    for (int u = 0; u < W; ++u) {
+      gtb += u < wv ? sh.wcnt[0][u] : 0u;
+      ties += u < wv ? sh.wcnt[1][u] : 0u;
+      gta += sh.wcnt[0][u];
+      tia += sh.wcnt[1][u];
+    }
+    kept_all = gta + min(tia, need);
+    kept = gtb + min(ties, need);
+    new_pass(v);
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const float x = v[i];
+      const uint64_t em = __ballot(x == th.T);
+      bool keep;
+      if (em == 0ull) {
+        keep = x > th.T;
+      } else {
+        keep = x > th.T || (x == th.T && ties + lanes_below(em) < need);
+        ties += static_cast<uint32_t>(__popcll(em));
+      }
+      const uint64_t km = __ballot(keep);
+      if (km != 0ull) {
+        const uint32_t pos = kept + lanes_below(km);
+        if (keep && pos < static_cast<uint32_t>(k)) {
+          sid[pos] = __builtin_amdgcn_readlane(rbase, i) + l;
+          if (ssc) ssc[pos] = x;
+        }
+        kept += static_cast<uint32_t>(__popcll(km));
+      }
     }
   }
   __syncthreads();
