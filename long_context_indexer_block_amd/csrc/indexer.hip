@@ -686,16 +686,19 @@ __global__ __launch_bounds__(64 * NW) void route_blocks_stream_kernel(
 #pragma unroll
     for (int u = 0; u < QW; ++u) {
       const int j = w + NW * u;
+      // key > th as a float compare: the key order is the float order (with
+      // -0 == +0), and th = 0 (no cut yet) passes every score, as NaN does
+      const float thf = th[u] == 0u ? __uint_as_float(0x7fc00000u) : key_value(th[u]);
 #pragma unroll
       for (int h = 0; h < SB / 64; ++h) {
         const int p = SB * step + 64 * h + l;
-        const uint32_t key = p < nc[u] ? order_key(sg[j * SB + 64 * h + l]) : 0u;
-        const bool pass = p < nc[u] && key > th[u];
+        const float x = sg[j * SB + 64 * h + l];
+        const bool pass = p < nc[u] && !(x <= thf);
         const uint64_t pm = __ballot(pass);
         if (pm == 0ull) continue;
         if (pass) {
           const int e = cnt[u] + static_cast<int>(lanes_below(pm));
-          bkey[j][e] = key;
+          bkey[j][e] = order_key(x);
           bpos[j][e] = p;
         }
         cnt[u] += static_cast<int>(__popcll(pm));

@@ -50,6 +50,12 @@ struct TokWs : PairBuckets {
   float* scores;        // [batch*nq*m*B]
 };
 
+// The row top-k loads whole waves of 64-score rows from a query's first row,
+// up to 256 rows (W * RW), whether or not the query has that many: rows past
+// its own are masked, and the buffer ends with this much slack so that the
+// last query's loads stay inside it.
+constexpr size_t kScoreTailPad = static_cast<size_t>(256) * 64 * 4;
+
 static TokWs carve(void* ws, int batch, int nq, int L, int B, int m, size_t* bytes) {
   const int nblk = (L + B - 1) / B;
   const size_t npairs = static_cast<size_t>(batch) * nq * m;
@@ -57,7 +63,7 @@ static TokWs carve(void* ws, int batch, int nq, int L, int B, int m, size_t* byt
   TokWs w;
   static_cast<PairBuckets&>(w) = carve_pair_buckets(ws, batch, nq, m, nblk, &off);
   w.scores = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + off) : nullptr;
-  off += align256(npairs * B * 4);
+  off += align256(npairs * B * 4 + kScoreTailPad);
   if (bytes) *bytes = off;
   return w;
 }
@@ -565,13 +571,16 @@ __device__ __forceinline__ int cvt_i32_nan0(float x) {
   asm("v_cvt_i32_f32 %0, %1" : "=v"(r) : "v"(x));
   return r;
 }
-// An opaque copy of the candidates at the start of each pass: the
-// comparisons of a pass are recomputed instead of being kept from an earlier
-// pass as lane masks, which would take two scalar registers per row.
-template <int RW>
-__device__ __forceinline__ void new_pass(float (&v)[RW]) {
-#pragma unroll
-  for (int i = 0; i < RW; ++i) asm volatile("" : "+v"(v[i]));
+// An opaque copy of a pass's parameter: each pass compares the candidates
+// against its own copy, so that no pass reuses the compares of an earlier
+// one, which would keep them as lane masks, two scalar registers per row.
+__device__ __forceinline__ float fresh(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+__device__ __forceinline__ int fresh(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 // Lanes of the wave for which p holds. The count is taken in an ordered
 // (volatile) statement so that each row's lane mask dies at once: left to
@@ -620,7 +629,7 @@ __device__ __forceinline__ void rows_block_minmax(float& mn, float& mx, RowSelLd
 // lo < max hi and 1 <= K < their count. The histogram bins are cleared on
 // entry.
 template <int RW, int W>
-__device__ RowThreshold rows_threshold(float (&v)[RW], float lo, float hi, int krem,
+__device__ RowThreshold rows_threshold(const float (&v)[RW], float lo, float hi, int krem,
                                        RowSelLds<W>& sh, int wv, int l) {
   constexpr int NT = 64 * W, NB = kRowBins;
   constexpr int BPT = NB / NT;  // bins per thread in the search for beta
@@ -633,11 +642,11 @@ __device__ RowThreshold rows_threshold(float (&v)[RW], float lo, float hi, int k
     // the product at most NB (1 + 2^-23) without overflow
     const float scale = static_cast<float>(NB) / half_w;
     const float lo_h = lo * 0.5f;
-    auto binof = [&](float x) {
+    auto binof_at = [](float x, float lo_h, float scale) {
       const int b = cvt_i32_nan0(__builtin_fmaf(x, 0.5f, -lo_h) * scale);
       return b < NB - 1 ? b : NB - 1;
     };
-    new_pass(v);
+    auto binof = [&](float x) { return binof_at(x, lo_h, scale); };
     if (level == 0) {
       // every candidate is in [lo, hi]; a non-candidate (NaN) lands in bin 0,
       // which is only ever the bin of the K-th largest when all candidates
@@ -684,8 +693,13 @@ __device__ RowThreshold rows_threshold(float (&v)[RW], float lo, float hi, int k
     const int beta = sh.beta;
     krem -= static_cast<int>(sh.above);
     const uint32_t hbeta = sh.hbeta;
-    // candidates of bin beta: x in [lo, hi] with binof(x) == beta
-    auto in_beta = [&](float x) { return x >= lo && x <= hi && binof(x) == beta; };
+    // candidates of bin beta: x in [lo, hi] with binof(x) == beta, each
+    // pass with its own copies of the parameters
+    auto in_beta_fn = [&]() {
+      const float clo = fresh(lo), chi = fresh(hi), clh = fresh(lo_h), csc = fresh(scale);
+      const int cb = fresh(beta);
+      return [=](float x) { return x >= clo && x <= chi && binof_at(x, clh, csc) == cb; };
+    };
     if (hbeta <= static_cast<uint32_t>(kRowList)) {
       // ---- the bin's candidates to LDS, this wave's at list[wv]. A value
       // window of the bin widened by two bins on each side (far more than
@@ -694,7 +708,7 @@ __device__ RowThreshold rows_threshold(float (&v)[RW], float lo, float hi, int k
       const float wa = lo + static_cast<float>(beta - 2) * wbin;
       const float wb = lo + static_cast<float>(beta + 3) * wbin;
       uint32_t nl = 0;
-      new_pass(v);
+      const auto in_beta = in_beta_fn();
 #pragma unroll
       for (int i = 0; i < RW; ++i) {
         const float x = v[i];
@@ -743,7 +757,7 @@ __device__ RowThreshold rows_threshold(float (&v)[RW], float lo, float hi, int k
     }
     // ---- the bin's own range
     float bmn = INFINITY, bmx = -INFINITY;
-    new_pass(v);
+    const auto in_beta = in_beta_fn();
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
       const float x = v[i];
@@ -769,25 +783,27 @@ __device__ RowThreshold rows_threshold(float (&v)[RW], float lo, float hi, int k
     const uint32_t mid = klo + ((khi - klo + 1u) >> 1);
     const float fm = key_value(mid);
     uint32_t c = 0;
-    new_pass(v);
+    const float chi = fresh(hi);
 #pragma unroll
-    for (int i = 0; i < RW; ++i) c += row_count(v[i] >= fm && v[i] <= hi);
+    for (int i = 0; i < RW; ++i) c += row_count(v[i] >= fm && v[i] <= chi);
     const uint32_t tot = rows_block_sum<W>(c, sh, wv, l);
     if (tot >= static_cast<uint32_t>(krem)) klo = mid; else khi = mid - 1u;
   }
   const float T = key_value(klo);
   uint32_t c = 0;
-  new_pass(v);
+  const float chi = fresh(hi);
 #pragma unroll
-  for (int i = 0; i < RW; ++i) c += row_count(v[i] > T && v[i] <= hi);
+  for (int i = 0; i < RW; ++i) c += row_count(v[i] > T && v[i] <= chi);
   const uint32_t tgt = rows_block_sum<W>(c, sh, wv, l);
   return RowThreshold{T, krem - static_cast<int>(tgt), false};
 }
 
-// The register budget allows 5 waves per SIMD: the kernel is latency bound
-// (barriers, LDS atomics), so more resident workgroups hide more of it.
+// The register budget allows 6 waves per SIMD (80 VGPRs; 78 used at RW =
+// 32): the kernel waits on loads, barriers and LDS atomics, so more resident
+// workgroups hide more of it (64K: 1.567 -> 1.499 ms for the token select
+// at 5 -> 6; at 7 the 32-row form spills).
 template <int RW, int W>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(5, 8))) void
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(6, 8))) void
 token_topk_rows_kernel(const float* __restrict__ scores, const int32_t* __restrict__ block_idx,
                        const int32_t* __restrict__ q_pos, int m, int B, int k, int L,
                        int32_t* __restrict__ token_idx, float* __restrict__ token_scores) {
@@ -817,13 +833,21 @@ token_topk_rows_kernel(const float* __restrict__ scores, const int32_t* __restri
     if (c >= 0 && c < nblk) rbase = c * B + (r & ((1 << lrpb) - 1)) * 64;
   }
   const int rlim = rbase >= 0 ? min(t - rbase, 63) : -1;
-  // the rows, all loads issued before any is used (a row past the last one
-  // loads the last one again and is masked)
+  // the rows, all loads issued before any is used, from one lane address
+  // with immediate row offsets (rows past the query's last are read from the
+  // buffer's slack or the next query and masked)
+  static_assert(RW * W <= 256, "rows per query within the buffer's slack");
   float v[RW];
+  {
+    const float* lrow = row + static_cast<int64_t>(r0) * 64 + l;
 #pragma unroll
-  for (int i = 0; i < RW; ++i) v[i] = row[min(r0 + i, nrows - 1) * 64 + l];
+    for (int i = 0; i < RW; ++i) v[i] = lrow[i * 64];
+  }
+  // rows that are not whole candidates (usually only the query's own block)
+  if (__ballot(l < RW && rlim < 63) != 0ull) {
 #pragma unroll
-  for (int i = 0; i < RW; ++i) v[i] = l <= __builtin_amdgcn_readlane(rlim, i) ? v[i] : qnan;
+    for (int i = 0; i < RW; ++i) v[i] = l <= __builtin_amdgcn_readlane(rlim, i) ? v[i] : qnan;
+  }
   // ---- count, min and max of the candidates
   const uint32_t nw = wave_sum_dpp(static_cast<uint32_t>(max(rlim + 1, 0)));
   float mn = INFINITY, mx = -INFINITY;
@@ -857,7 +881,6 @@ token_topk_rows_kernel(const float* __restrict__ scores, const int32_t* __restri
   int32_t* sid = reinterpret_cast<int32_t*>(stage);
   float* ssc = token_scores ? reinterpret_cast<float*>(stage) + k : nullptr;
   uint32_t kept_all, kept;
-  new_pass(v);
   if (th.all) {
     // every candidate >= T is kept
     uint32_t gew = 0;
@@ -873,11 +896,11 @@ token_topk_rows_kernel(const float* __restrict__ scores, const int32_t* __restri
     }
     kept_all = all;
     kept = before;
-    new_pass(v);
+    const float T = fresh(th.T);
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
       const float x = v[i];
-      const bool keep = x >= th.T;
+      const bool keep = x >= T;
       const uint64_t km = __ballot(keep);
       if (km != 0ull) {
         const uint32_t pos = kept + lanes_below(km);
@@ -912,16 +935,16 @@ token_topk_rows_kernel(const float* __restrict__ scores, const int32_t* __restri
     }
     kept_all = gta + min(tia, need);
     kept = gtb + min(ties, need);
-    new_pass(v);
+    const float T = fresh(th.T);
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
       const float x = v[i];
-      const uint64_t em = __ballot(x == th.T);
+      const uint64_t em = __ballot(x == T);
       bool keep;
       if (em == 0ull) {
-        keep = x > th.T;
+        keep = x > T;
       } else {
-        keep = x > th.T || (x == th.T && ties + lanes_below(em) < need);
+        keep = x > T || (x == T && ties + lanes_below(em) < need);
         ties += static_cast<uint32_t>(__popcll(em));
       }
       const uint64_t km = __ballot(keep);
