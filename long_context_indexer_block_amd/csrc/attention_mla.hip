@@ -410,9 +410,8 @@ __device__ __forceinline__ int v_ids(VState& st, const Ctx& cx, int i, int q4, i
 // issued between the matrix-core operations
 template <int J, bool GATHER>
 __device__ __forceinline__ void v_accumulate(VState& st, int q4, int l, uint4* gdst) {
-  // Opaque copy of the lane id: the fragment addresses derived from it are
-  // recomputed per tile instead of being kept live across the loop.
-  asm volatile("" : "+v"(l));
+  // The fragment addresses derived from the lane id stay in registers across
+  // the loop (216 VGPRs, still two waves per SIMD).
   bf16x8 pb[2][2];
   {
     const uint4* pp = pbuf<J>();
@@ -439,7 +438,7 @@ __device__ __forceinline__ void v_accumulate(VState& st, int q4, int l, uint4* g
     const uint2 hi = tr16(tb + vb[1][dt & 1] + off);
     return make_uint4(lo.x, lo.y, hi.x, hi.y);
   };
-  constexpr int AHEAD = 3;
+  constexpr int AHEAD = 4;
   uint4 vf[8];
 #pragma unroll
   for (int x = 0; x < AHEAD; ++x) vf[x] = vfrag(x >> 2, x & 3);
