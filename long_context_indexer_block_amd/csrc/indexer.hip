@@ -269,7 +269,17 @@ __device__ __forceinline__ WaveSel wave_select(const uint32_t (&key)[IT], uint32
     uint32_t c = 0;
 #pragma unroll
     for (int i = 0; i < IT; ++i) c += static_cast<uint32_t>(__popcll(__ballot(key[i] >= mid)));
-    if (c >= K) lo = mid; else hi = mid - 1u;
+    if (c == K) {
+      // exactly the K largest keys are >= mid: the K-th largest is their
+      // minimum (usually reached after a third of the steps, once mid falls
+      // in the gap between the K-th and the next key)
+      uint32_t m = 0xffffffffu;
+#pragma unroll
+      for (int i = 0; i < IT; ++i) m = key[i] >= mid ? min(m, key[i]) : m;
+      lo = hi = wave_min_u32(m);
+      break;
+    }
+    if (c > K) lo = mid; else hi = mid - 1u;
   }
   uint32_t gt = 0;
 #pragma unroll
