@@ -240,6 +240,57 @@ def test_token_select_16k_candidates(B, m):
     _check_hier(w, inp, p, rows, attn_rows=rows[-3:], what=w.name)
 
 
+@pytest.mark.parametrize("cluster", ["spread", "three_values", "near_k"])
+def test_token_select_wide_range_scores(cluster):
+    # token scores crafted to defeat the value-range histogram: the query is
+    # the unit vector e0, so a token's score is its key's first element. Six
+    # tokens hold +-2^100, +-2^66, +-2^33 and all others lie in [-1, 1], so
+    # each of the three histogram levels finds the K-th largest value in one
+    # bin holding nearly every candidate and the exact bisection on order
+    # keys decides; every block is kept (m*B covers the prefix), 1024 queries
+    # take the 32-row, 4-wave select over 8192 candidates
+    # (near_k: no outliers, the queries at positions 1536..2559, so around t =
+    # k the K-th largest value is among the smallest, in the histogram's
+    # lowest bins, where the masked tokens of the query's own block and the
+    # empty slots are counted too)
+    L = 2560 if cluster == "near_k" else 8192
+    w = _mk(f"wide_range_{cluster}", L=L, nq=1024, B=128, m=64, k=2048, d_idx=64, Hq=1, Hkv=1)
+    log(f"case {w}")
+    inp = make_inputs(w, DEV, seed=21)
+    g = torch.Generator().manual_seed(22)
+    # values on a grid of 1/64; block 0 holds the outliers, whose fp32 block
+    # mean depends on the summation order, so block scores are not compared
+    # here (every block is kept either way); token ids and scores are exact
+    if cluster == "three_values":
+        vals = torch.tensor([-0.5, 0.25, 0.75])[torch.randint(0, 3, (w.L,), generator=g)]
+    else:
+        vals = torch.randint(-64, 65, (w.L,), generator=g).float() / 64.0
+    if cluster != "near_k":
+        for j, x in zip((5, 6, 7, 8, 9, 10), (2.0 ** 100, -(2.0 ** 100), 2.0 ** 66, -(2.0 ** 66),
+                                              2.0 ** 33, -(2.0 ** 33))):
+            vals[j] = x
+    kidx = torch.zeros(w.batch, w.L, w.d_idx)
+    kidx[:, :, 0] = vals
+    qidx = torch.zeros(w.batch, w.queries, w.d_idx)
+    qidx[:, :, 0] = 1.0
+    inp["kidx"].copy_(kidx.to(torch.bfloat16))
+    inp["qidx"].copy_(qidx.to(torch.bfloat16))
+    p = _run_hier(w, inp)
+    if cluster == "near_k":
+        rows = [t - (L - 1024) for t in (1600, 2046, 2047, 2048, 2049, 2050, 2100, 2175, 2176,
+                                         2559)]
+    else:
+        rows = list(range(0, 1024, 127)) + [1023]
+    so = SeqOracle(inp, 0, w.B, with_attention=False)
+    ref = [so.hier(r, w.m, w.k) for r in rows]
+    check_index_rows(p.block_idx[0, rows].cpu().numpy(), np.stack([x[0] for x in ref]),
+                     f"{w.name} block_idx")
+    check_index_rows(p.token_idx[0, rows].cpu().numpy(), np.stack([x[2] for x in ref]),
+                     f"{w.name} token_idx")
+    check_score_rows(p.token_scores[0, rows].cpu().numpy(), np.stack([x[3] for x in ref]),
+                     f"{w.name} token scores")
+
+
 @pytest.mark.parametrize("L,hier", [(4096, False), (12288, True)])
 def test_auto_pipeline(L, hier):
     # the runtime policy: the flat indexer below 8192 keys, else the
