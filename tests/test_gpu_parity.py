@@ -240,7 +240,7 @@ def test_token_select_16k_candidates(B, m):
     _check_hier(w, inp, p, rows, attn_rows=rows[-3:], what=w.name)
 
 
-@pytest.mark.parametrize("cluster", ["spread", "three_values", "near_k"])
+@pytest.mark.parametrize("cluster", ["spread", "three_values", "near_k", "spread_few"])
 def test_token_select_wide_range_scores(cluster):
     # token scores crafted to defeat the value-range histogram: the query is
     # the unit vector e0, so a token's score is its key's first element. Six
@@ -253,8 +253,10 @@ def test_token_select_wide_range_scores(cluster):
     # k the K-th largest value is among the smallest, in the histogram's
     # lowest bins, where the masked tokens of the query's own block and the
     # empty slots are counted too)
+    # (spread_few: 64 queries, the 16-wave form of the select)
     L = 2560 if cluster == "near_k" else 8192
-    w = _mk(f"wide_range_{cluster}", L=L, nq=1024, B=128, m=64, k=2048, d_idx=64, Hq=1, Hkv=1)
+    nq = 64 if cluster == "spread_few" else 1024
+    w = _mk(f"wide_range_{cluster}", L=L, nq=nq, B=128, m=64, k=2048, d_idx=64, Hq=1, Hkv=1)
     log(f"case {w}")
     inp = make_inputs(w, DEV, seed=21)
     g = torch.Generator().manual_seed(22)
@@ -280,7 +282,7 @@ def test_token_select_wide_range_scores(cluster):
         rows = [t - (L - 1024) for t in (1600, 2046, 2047, 2048, 2049, 2050, 2100, 2175, 2176,
                                          2559)]
     else:
-        rows = list(range(0, 1024, 127)) + [1023]
+        rows = sorted(set(range(0, nq, nq // 8 - 1)) | {nq - 1})
     so = SeqOracle(inp, 0, w.B, with_attention=False)
     ref = [so.hier(r, w.m, w.k) for r in rows]
     check_index_rows(p.block_idx[0, rows].cpu().numpy(), np.stack([x[0] for x in ref]),
