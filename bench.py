@@ -48,6 +48,9 @@ def parse():
                          "the slab before (0: stages one after another; default: 16 from 32768 "
                          "queries on)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--bw-probe", type=int, default=0,
+                    help="time a plain fill of this many bytes and a copy of half of them "
+                         "(the HBM rates the selection kernels are compared with)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
     ap.add_argument("--sweep", action="store_true",
@@ -240,6 +243,30 @@ def copy_probe(nbytes):
     b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": nbytes}))
+
+
+def bw_probe(nbytes, reps=20):
+    """HIP-event times of a plain fill of `nbytes` and of a copy of nbytes/2
+    (read and write): the rates of simple streaming kernels on this chip."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty(nbytes // 8, dtype=torch.float32, device="cuda")
+    c = torch.empty_like(b)
+    def ms(f):
+        for _ in range(3):
+            f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+    fill = ms(lambda: a.fill_(1.0))
+    copy = ms(lambda: c.copy_(b))
+    print(json.dumps({"bw_probe_bytes": nbytes, "fill_ms": fill, "fill_TBps": nbytes / fill / 1e9,
+                      "copy_bytes": nbytes // 2, "copy_ms": copy,
+                      "copy_TBps_read_plus_write": nbytes / copy / 1e9}))
 
 
 def timed(calls, steps, warmup):
@@ -980,6 +1007,9 @@ def main():
 
     if a.copy_probe:
         copy_probe(a.copy_probe)
+        return
+    if a.bw_probe:
+        bw_probe(a.bw_probe)
         return
     w = WORKLOADS[a.workload]
     torch.cuda.set_device(0)
