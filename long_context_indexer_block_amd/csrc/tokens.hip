@@ -626,7 +626,7 @@ __device__ __forceinline__ void rows_block_minmax(float& mn, float& mx, RowSelLd
 }
 
 // K-th largest of the candidates v (NaN: not a candidate), given their min
-// lo < max hi and 1 <= K < their count. The histogram bins are cleared on
+// lo and max hi and 1 <= K < their count. The histogram bins are cleared on
 // entry.
 template <int RW, int W>
 __device__ RowThreshold rows_threshold(const float (&v)[RW], float lo, float hi, int krem,
