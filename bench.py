@@ -524,8 +524,10 @@ def _short(name):
 
 def write_trace_md(folder, out_path, title, command, note=""):
     """Per (kernel, grid size) of the library's kernels (namespace hisa) in a
-    rocprofv3 kernel trace: calls, mean / min / max duration in us and share
-    of the GPU time of all dispatches in the trace."""
+    rocprofv3 kernel trace: calls, mean / median / min / max duration in us
+    and share of the GPU time of all dispatches in the trace. The median
+    leaves out the first, cold call of a short run (the bench's timed region
+    excludes its warm-up calls)."""
     import csv
     import glob
     files = glob.glob(os.path.join(folder, "**", "*kernel_trace.csv"), recursive=True)
@@ -546,10 +548,13 @@ def write_trace_md(folder, out_path, title, command, note=""):
              command.strip(), "```", "",
              "Durations in microseconds (rocprofv3 kernel trace); rows split by grid size "
              "(threads); the share is of all GPU time in the trace (input generation included).",
-             "", "| kernel | grid (threads) | calls | avg us | min us | max us | % of GPU time |",
-             "|---|---|---|---|---|---|---|"]
+             "", "| kernel | grid (threads) | calls | avg us | median us | min us | max us | "
+             "% of GPU time |",
+             "|---|---|---|---|---|---|---|---|"]
     for (name, grid), ds in rows:
-        lines.append(f"| `{name}` | {grid:,} | {len(ds)} | {sum(ds) / len(ds):.1f} | "
+        sd = sorted(ds)
+        med = sd[len(sd) // 2] if len(sd) % 2 else 0.5 * (sd[len(sd) // 2 - 1] + sd[len(sd) // 2])
+        lines.append(f"| `{name}` | {grid:,} | {len(ds)} | {sum(ds) / len(ds):.1f} | {med:.1f} | "
                      f"{min(ds):.1f} | {max(ds):.1f} | {100 * sum(ds) / total:.2f} |")
     text = "\n".join(lines) + "\n"
     if out_path:
