@@ -123,6 +123,16 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
   x = min(x, dpp_move<0x143, 0xc>(x, x));  // row_bcast:31 into rows 2, 3
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 63));
 }
+// maximum of an unsigned value across the 64 lanes, the same for every lane
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, dpp_move<0x111, 0xf>(x, x));  // row_shr:1
+  x = max(x, dpp_move<0x112, 0xf>(x, x));  // row_shr:2
+  x = max(x, dpp_move<0x114, 0xf>(x, x));  // row_shr:4
+  x = max(x, dpp_move<0x118, 0xf>(x, x));  // row_shr:8
+  x = max(x, dpp_move<0x142, 0xa>(x, x));  // row_bcast:15 into rows 1, 3
+  x = max(x, dpp_move<0x143, 0xc>(x, x));  // row_bcast:31 into rows 2, 3
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 63));
+}
 // number of set bits of `mask` in the lanes below this one
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),

@@ -253,16 +253,16 @@ struct WaveSel {
 template <int IT>
 __device__ __forceinline__ WaveSel wave_select(const uint32_t (&key)[IT], uint32_t okm,
                                                uint32_t K) {
-  float mn = INFINITY, mx = -INFINITY;
+  // the smallest and largest key of the candidates, on the keys themselves
+  // (their order is the scores' order); with no candidate lo > hi
+  uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
   for (int i = 0; i < IT; ++i) {
-    if ((okm >> i) & 1u) {
-      const float f = key_value(key[i]);
-      mn = fminf(mn, f);
-      mx = fmaxf(mx, f);
-    }
+    const bool ok = ((okm >> i) & 1u) && key[i] != 0u;
+    mn = min(mn, ok ? key[i] : 0xffffffffu);
+    mx = max(mx, ok ? key[i] : 0u);
   }
-  uint32_t lo = order_key(wave_ext_dpp<false>(mn)), hi = order_key(wave_ext_dpp<true>(mx));
+  uint32_t lo = wave_min_u32(mn), hi = wave_max_u32(mx);
   // the largest key x with count(key >= x) >= K (keys of no candidate are 0 < lo)
   while (lo < hi) {
     const uint32_t mid = lo + ((hi - lo + 1u) >> 1);
