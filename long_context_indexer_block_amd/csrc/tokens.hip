@@ -361,21 +361,27 @@ hipError_t launch_pair_buckets(const int32_t* block_idx, int batch, int nq, int 
 // accumulator lane layout (column = pair, 4 consecutive tokens) is stored
 // as one 16-byte write per pair.
 // DIRECT (one query per sequence, so no key block has two pairs): workgroup
-// x scores pair x on its own, and the bucket tables are not used.
-template <int D, int BS, bool DIRECT>
+// x scores pair x on its own, and the bucket tables are not used. PAIRWAVE
+// (with DIRECT): each wave scores a pair of its own, 4 pairs per workgroup,
+// for small blocks where a pair split over four waves leaves each wave a
+// single 16-token tile and the launch's workgroup count dominates.
+template <int D, int BS, bool DIRECT, bool PAIRWAVE = false>
 __global__ __launch_bounds__(256) void token_score_kernel(
     const uint16_t* __restrict__ qidx, int64_t qsb, int64_t qst, const uint16_t* __restrict__ kidx,
     int64_t ksb, int64_t kst, int L, int nq, int m, int nblk, const uint32_t* __restrict__ tiles,
     const uint32_t* __restrict__ total, const uint32_t* __restrict__ tile_off,
     const uint32_t* __restrict__ offs, const uint32_t* __restrict__ cnt,
     const uint32_t* __restrict__ pairs, const int32_t* __restrict__ block_idx,
-    float* __restrict__ scores) {
+    float* __restrict__ scores, uint32_t npairs_direct) {
   constexpr int KS = D / 32;
-  constexpr int MT = BS / 64;  // 16-token tiles per wave
-  const uint32_t tile = blockIdx.x;
+  static_assert(DIRECT || !PAIRWAVE, "one pair per wave needs the direct form");
+  constexpr int MT = PAIRWAVE ? BS / 16 : BS / 64;  // 16-token tiles per wave
+  constexpr int TPW = PAIRWAVE ? 0 : BS / 4;        // first token of wave w: w * TPW
+  const uint32_t tile = PAIRWAVE ? blockIdx.x * 4 + threadIdx.x / kWave : blockIdx.x;
   uint32_t p0, np;
   int b, c;
   if constexpr (DIRECT) {
+    if (PAIRWAVE && tile >= npairs_direct) return;
     c = block_idx[tile];
     if (c < 0 || c >= nblk) return;  // empty slot: never a candidate
     p0 = tile;
@@ -407,7 +413,7 @@ __global__ __launch_bounds__(256) void token_score_kernel(
   }
 
   bf16x8 a[MT][KS];
-  const int tok0 = c * BS + wave * (BS / 4);
+  const int tok0 = c * BS + wave * TPW;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int j = min(tok0 + mt * 16 + r16, L - 1);
@@ -440,7 +446,7 @@ __global__ __launch_bounds__(256) void token_score_kernel(
 #pragma unroll
       for (int s = 0; s < KS; ++s) acc = mfma16(a[mt][s], bq[s], acc);
       if (nt * 16 + r16 < static_cast<int>(np)) {
-        const int tk = wave * (BS / 4) + mt * 16 + 4 * g;
+        const int tk = wave * TPW + mt * 16 + 4 * g;
         *reinterpret_cast<f32x4*>(scores + static_cast<int64_t>(pid) * BS + tk) = acc;
       }
     }
@@ -1010,18 +1016,24 @@ hipError_t launch_token_select(const uint16_t* qidx, Str3 qs, const uint16_t* ki
     const hipError_t e = launch_pair_buckets(block_idx, batch, nq, m, nblk, w, s);
     if (e != hipSuccess) return e;
   }
+  const uint32_t np32 = static_cast<uint32_t>(npairs);
 #define HISA_TS(D_, B_)                                                                       \
   do {                                                                                        \
-    if (direct)                                                                               \
+    if (direct && B_ == 64)                                                                   \
+      hipLaunchKernelGGL((token_score_kernel<D_, B_, true, true>),                            \
+                         dim3(static_cast<unsigned>((npairs + 3) / 4)), dim3(256), 0, s, qidx, \
+                         qs.b, qs.t, kidx, ks.b, ks.t, L, nq, m, nblk, w.tiles, w.total,      \
+                         w.tile_off, w.offs, w.cnt, w.pairs, block_idx, w.scores, np32);      \
+    else if (direct)                                                                          \
       hipLaunchKernelGGL((token_score_kernel<D_, B_, true>), dim3(static_cast<unsigned>(npairs)), \
                          dim3(256), 0, s, qidx, qs.b, qs.t, kidx, ks.b, ks.t, L, nq, m, nblk, \
                          w.tiles, w.total, w.tile_off, w.offs, w.cnt, w.pairs, block_idx,     \
-                         w.scores);                                                           \
+                         w.scores, np32);                                                     \
     else                                                                                      \
       hipLaunchKernelGGL((token_score_kernel<D_, B_, false>),                                 \
                          dim3(static_cast<unsigned>(max_tiles)), dim3(256), 0, s, qidx, qs.b,  \
                          qs.t, kidx, ks.b, ks.t, L, nq, m, nblk, w.tiles, w.total, w.tile_off, \
-                         w.offs, w.cnt, w.pairs, block_idx, w.scores);                        \
+                         w.offs, w.cnt, w.pairs, block_idx, w.scores, np32);                  \
   } while (0)
   if (d == 64) {
     if (B == 64) HISA_TS(64, 64); else if (B == 128) HISA_TS(64, 128); else HISA_TS(64, 256);
