@@ -240,7 +240,7 @@ def test_token_select_16k_candidates(B, m):
     _check_hier(w, inp, p, rows, attn_rows=rows[-3:], what=w.name)
 
 
-@pytest.mark.parametrize("cluster", ["spread", "three_values", "near_k", "spread_few"])
+@pytest.mark.parametrize("cluster", ["spread", "three_values", "near_k", "spread_few", "near_n"])
 def test_token_select_wide_range_scores(cluster):
     # token scores crafted to defeat the value-range histogram: the query is
     # the unit vector e0, so a token's score is its key's first element. Six
@@ -253,10 +253,14 @@ def test_token_select_wide_range_scores(cluster):
     # k the K-th largest value is among the smallest, in the histogram's
     # lowest bins, where the masked tokens of the query's own block and the
     # empty slots are counted too)
-    # (spread_few: 64 queries, the 16-wave form of the select)
+    # (spread_few: 64 queries, the 16-wave form of the select; near_n: k just
+    # below the candidate count, so the K-th largest value lies in the
+    # lowest bin together with the masked tokens of the query's own block,
+    # and the bin's copy finds fewer candidates than the histogram counted)
     L = 2560 if cluster == "near_k" else 8192
     nq = 64 if cluster == "spread_few" else 1024
-    w = _mk(f"wide_range_{cluster}", L=L, nq=nq, B=128, m=64, k=2048, d_idx=64, Hq=1, Hkv=1)
+    k = 8162 if cluster == "near_n" else 2048
+    w = _mk(f"wide_range_{cluster}", L=L, nq=nq, B=128, m=64, k=k, d_idx=64, Hq=1, Hkv=1)
     log(f"case {w}")
     inp = make_inputs(w, DEV, seed=21)
     g = torch.Generator().manual_seed(22)
@@ -267,7 +271,7 @@ def test_token_select_wide_range_scores(cluster):
         vals = torch.tensor([-0.5, 0.25, 0.75])[torch.randint(0, 3, (w.L,), generator=g)]
     else:
         vals = torch.randint(-64, 65, (w.L,), generator=g).float() / 64.0
-    if cluster != "near_k":
+    if cluster not in ("near_k", "near_n"):
         for j, x in zip((5, 6, 7, 8, 9, 10), (2.0 ** 100, -(2.0 ** 100), 2.0 ** 66, -(2.0 ** 66),
                                               2.0 ** 33, -(2.0 ** 33))):
             vals[j] = x
@@ -281,6 +285,8 @@ def test_token_select_wide_range_scores(cluster):
     if cluster == "near_k":
         rows = [t - (L - 1024) for t in (1600, 2046, 2047, 2048, 2049, 2050, 2100, 2175, 2176,
                                          2559)]
+    elif cluster == "near_n":
+        rows = [t - (L - 1024) for t in (8000, 8160, 8161, 8162, 8163, 8170, 8191)]
     else:
         rows = sorted(set(range(0, nq, nq // 8 - 1)) | {nq - 1})
     so = SeqOracle(inp, 0, w.B, with_attention=False)
