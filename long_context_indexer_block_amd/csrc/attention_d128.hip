@@ -81,10 +81,6 @@ __device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) ^ (r & 8); }
 __device__ __forceinline__ f32x4 mfma16k16(const v4s& a, const v4s& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ v4s tr16(const unsigned char* lds_byte) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4s*)(lds_byte));
-}
 __device__ __forceinline__ float max_x16_x32(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
                                                   false);
@@ -195,27 +191,61 @@ struct State {
   uint32_t m0, m1;   // valid masks of tiles t and t+1
 };
 
-// The fragments of tile t (slot I = t % 3) this lane needs: K fragments
+// The fragments of tile t (slot I = t % 2) this lane needs: K fragments
 // (row l%16, chunks 4k + l/16) and V^T fragments of the 8 blocks of 16 value
 // columns (row 4(l/16) + (l%16)/4, columns 16dvb + 4(l%4) .. +3).
 struct Frags {
   uint4 k[4];
   v4s v[8];
 };
+// With them, the gather ids of tile tid (as read_ids returns them), all in
+// one statement that ends with the wait for every LDS read of the wave. The
+// reads are written out so that the compiler's load-counter bookkeeping does
+// not see them: it cannot tell the ring slots apart from the slot just
+// gathered into, and would drain every load in flight (the prefetch of the
+// tile two ahead) before the second tile of each loop trip. The slot a read
+// names has landed by the load-counter wait that ended the iteration before.
 template <int I>
-__device__ __forceinline__ void read_frags(Frags& f, const Item& it, int l) {
+__device__ __forceinline__ int4 read_frags_ids(Frags& f, const Item& it, int tid, int l) {
   const int g = l >> 4, r = l & 15;
-  const uint4* kt = kbuf<I>(it.w);
+  typedef __attribute__((address_space(3))) const unsigned char* lds_byte;
+  const uint32_t kt = (uint32_t)(uintptr_t)(lds_byte)(kbuf<I>(it.w));
+  const uint32_t vt = (uint32_t)(uintptr_t)(lds_byte)(vbuf<I>(it.w));
+  uint32_t ka[4], va[8];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) f.k[k] = kt[r * 16 + ((4 * k + g) ^ swz(r))];
-  const unsigned char* vt = reinterpret_cast<const unsigned char*>(vbuf<I>(it.w));
+  for (int k = 0; k < 4; ++k) ka[k] = kt + 16u * (r * 16 + ((4 * k + g) ^ swz(r)));
   const int vrow = 4 * g + (r >> 2);
-  const int vbase = vrow * 256 + 8 * (r & 1);
+  const uint32_t vbase = vt + vrow * 256 + 8 * (r & 1);
 #pragma unroll
   for (int dvb = 0; dvb < 8; ++dvb) {
     const int chunk = 2 * dvb + ((r & 3) >> 1);
-    f.v[dvb] = tr16(vt + vbase + 16 * (chunk ^ swz(vrow)));
+    va[dvb] = vbase + 16u * (chunk ^ swz(vrow));
   }
+  const uint32_t ia = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int*)(
+      &g_ids[it.w][tid & 7][4 * (l >> 4)]);
+  int4 ids;
+  asm volatile(
+      "ds_read_b128 %0, %13\n\t"
+      "ds_read_b128 %1, %14\n\t"
+      "ds_read_b128 %2, %15\n\t"
+      "ds_read_b128 %3, %16\n\t"
+      "ds_read_b64_tr_b16 %4, %17\n\t"
+      "ds_read_b64_tr_b16 %5, %18\n\t"
+      "ds_read_b64_tr_b16 %6, %19\n\t"
+      "ds_read_b64_tr_b16 %7, %20\n\t"
+      "ds_read_b64_tr_b16 %8, %21\n\t"
+      "ds_read_b64_tr_b16 %9, %22\n\t"
+      "ds_read_b64_tr_b16 %10, %23\n\t"
+      "ds_read_b64_tr_b16 %11, %24\n\t"
+      "ds_read_b128 %12, %25\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f.k[0]), "=&v"(f.k[1]), "=&v"(f.k[2]), "=&v"(f.k[3]), "=&v"(f.v[0]),
+        "=&v"(f.v[1]), "=&v"(f.v[2]), "=&v"(f.v[3]), "=&v"(f.v[4]), "=&v"(f.v[5]),
+        "=&v"(f.v[6]), "=&v"(f.v[7]), "=&v"(ids)
+      : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va[0]), "v"(va[1]), "v"(va[2]),
+        "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7]), "v"(ia)
+      : "memory");
+  return ids;
 }
 
 // Tile t: S^T, the softmax update, O += P V, from fragments already read.
@@ -273,9 +303,7 @@ __device__ __forceinline__ void tile(State& st, const Frags& f, int t, float sca
 template <int I, bool OFF32>
 __device__ __forceinline__ void iter(State& st, const Item& it, int t, float scale_log2, int l) {
   Frags f;
-  read_frags<I>(f, it, l);
-  // issued after the fragment reads: its wait covers them as well
-  const int4 ids = read_ids(it, t + 2, l);
+  const int4 ids = read_frags_ids<I>(f, it, t + 2, l);
   const uint32_t m2 = gather_ids<OFF32>(it, t + 2, kbuf<I>(it.w), vbuf<I>(it.w), ids, l);
   ids_issue(it, t + 5, l);
   tile(st, f, t, scale_log2, l);
