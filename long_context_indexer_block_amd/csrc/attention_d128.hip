@@ -81,13 +81,20 @@ __device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) ^ (r & 8); }
 __device__ __forceinline__ f32x4 mfma16k16(const v4s& a, const v4s& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
+// The larger of two scores. Written out: fmaxf first quiets each operand
+// (one extra instruction per operand), and no score is a NaN.
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ float max_x16_x32(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
                                                   false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
                                                   false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float sum_x16_x32(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
@@ -145,13 +152,16 @@ template <bool OFF32>
 __device__ __forceinline__ uint32_t gather_ids(const Item& it, int t, uint4* kd, uint4* vd,
                                                const int4 ids, int l) {
   const int g = l >> 4, p = l & 15;
-  uint32_t mask = 0;
   const int idv[4] = {ids.x, ids.y, ids.z, ids.w};
   const int left = it.topk - NT * t;  // rows of the tile inside the list
+  bool okv[4];
+  bool allok = true;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int r = 4 * u + g;
     const bool ok = r < left && static_cast<unsigned>(idv[u]) < static_cast<unsigned>(it.L);
+    okv[u] = ok;
+    allok = allok && ok;
     const int row = ok ? idv[u] : 0;
     const int c = p ^ swz(r);
     if constexpr (OFF32) {
@@ -170,7 +180,13 @@ __device__ __forceinline__ uint32_t gather_ids(const Item& it, int t, uint4* kd,
       __builtin_amdgcn_global_load_lds((glb_ptr)(it.vb + static_cast<int64_t>(row) * it.vst + 8 * c),
                                        (lds_ptr)(vd + 64 * u), 16, 0, 0);
     }
-    const uint64_t b = __ballot(ok);
+  }
+  // every row valid (all but a list's last tile, unless it has holes)
+  if (__ballot(!allok) == 0ull) return 0xFFFFu;
+  uint32_t mask = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint64_t b = __ballot(okv[u]);
 #pragma unroll
     for (int gg = 0; gg < 4; ++gg)
       mask |= static_cast<uint32_t>((b >> (16 * gg)) & 1u) << (4 * u + gg);
@@ -258,15 +274,17 @@ __device__ __forceinline__ void tile(State& st, const Frags& f, int t, float sca
   s1 = mfma16(as_bf16x8(f.k[1]), st.qf[1], s1);
   s0 = mfma16(as_bf16x8(f.k[2]), st.qf[2], s0);
   s1 = mfma16(as_bf16x8(f.k[3]), st.qf[3], s1);
+  // raw scores q.k; the scale (positive, checked by the host) is applied to
+  // the tile maximum and inside the numerators' multiply-add
   float sv[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) sv[e] = (s0[e] + s1[e]) * scale_log2;
+  for (int e = 0; e < 4; ++e) sv[e] = s0[e] + s1[e];
   if (st.m0 != 0xFFFFu) {  // holes or the list's end: drop the invalid tokens
 #pragma unroll
     for (int e = 0; e < 4; ++e) sv[e] = ((st.m0 >> (4 * g + e)) & 1u) ? sv[e] : -INFINITY;
   }
-  float tmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-  tmax = max_x16_x32(tmax);
+  float tmax = vmax(vmax(sv[0], sv[1]), vmax(sv[2], sv[3]));
+  tmax = max_x16_x32(tmax) * scale_log2;
   // ---- reference: set on the first tile, raised when exceeded by far
   const bool up = t == 0 || tmax > st.R + kRaise;
   if (__ballot(up) != 0ull) {
@@ -285,7 +303,7 @@ __device__ __forceinline__ void tile(State& st, const Frags& f, int t, float sca
   const float mneg = st.R == -INFINITY ? 0.0f : -st.R;
   float p[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(sv[e] + mneg);
+  for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], scale_log2, mneg));
   st.lsum += (p[0] + p[1]) + (p[2] + p[3]);
   const uint2 pp = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
   const v4s pa = __builtin_bit_cast(v4s, pp);
