@@ -360,56 +360,36 @@ hipError_t launch_pair_buckets(const int32_t* block_idx, int batch, int nq, int 
 // select 2.25 -> 2.07 ms). The
 // accumulator lane layout (column = pair, 4 consecutive tokens) is stored
 // as one 16-byte write per pair.
-// DIRECT (one query per sequence, so no key block has two pairs): workgroup
-// x scores pair x on its own, and the bucket tables are not used. PAIRWAVE
-// (with DIRECT): each wave scores a pair of its own, 4 pairs per workgroup,
-// for small blocks where a pair split over four waves leaves each wave a
-// single 16-token tile and the launch's workgroup count dominates.
-template <int D, int BS, bool DIRECT, bool PAIRWAVE = false>
+template <int D, int BS>
 __global__ __launch_bounds__(256) void token_score_kernel(
     const uint16_t* __restrict__ qidx, int64_t qsb, int64_t qst, const uint16_t* __restrict__ kidx,
     int64_t ksb, int64_t kst, int L, int nq, int m, int nblk, const uint32_t* __restrict__ tiles,
     const uint32_t* __restrict__ total, const uint32_t* __restrict__ tile_off,
     const uint32_t* __restrict__ offs, const uint32_t* __restrict__ cnt,
-    const uint32_t* __restrict__ pairs, const int32_t* __restrict__ block_idx,
-    float* __restrict__ scores, uint32_t npairs_direct) {
+    const uint32_t* __restrict__ pairs, float* __restrict__ scores) {
   constexpr int KS = D / 32;
-  static_assert(DIRECT || !PAIRWAVE, "one pair per wave needs the direct form");
-  constexpr int MT = PAIRWAVE ? BS / 16 : BS / 64;  // 16-token tiles per wave
-  constexpr int TPW = PAIRWAVE ? 0 : BS / 4;        // first token of wave w: w * TPW
-  const uint32_t tile = PAIRWAVE ? blockIdx.x * 4 + threadIdx.x / kWave : blockIdx.x;
-  uint32_t p0, np;
-  int b, c;
-  if constexpr (DIRECT) {
-    if (PAIRWAVE && tile >= npairs_direct) return;
-    c = block_idx[tile];
-    if (c < 0 || c >= nblk) return;  // empty slot: never a candidate
-    p0 = tile;
-    np = 1;
-    b = static_cast<int>(tile / (static_cast<uint32_t>(nq) * m));
-  } else {
-    if (tile >= total[1]) return;
-    const uint32_t key = tiles[tile];
-    const uint32_t sub = tile - tile_off[key];
-    p0 = offs[key] + sub * kTQ;
-    np = min(static_cast<uint32_t>(kTQ), cnt[key] - sub * kTQ);
-    b = key / nblk;
-    c = key % nblk;
-  }
+  constexpr int MT = BS / 64;  // 16-token tiles per wave
+  constexpr int TPW = BS / 4;  // first token of wave w: w * TPW
+  const uint32_t tile = blockIdx.x;
+  if (tile >= total[1]) return;
+  const uint32_t key = tiles[tile];
+  const uint32_t sub = tile - tile_off[key];
+  const uint32_t p0 = offs[key] + sub * kTQ;
+  const uint32_t np = min(static_cast<uint32_t>(kTQ), cnt[key] - sub * kTQ);
+  const int b = key / nblk;
+  const int c = key % nblk;
   const int wave = threadIdx.x / kWave, lane = lane_id();
   const int g = lane / 16, r16 = lane % 16;
   // the tile's query rows, gathered once into LDS (every wave needs all of them)
   constexpr int QRS = 2 * D + 16;  // padded row stride (bytes)
-  __shared__ __align__(16) unsigned char qs_lds[DIRECT ? 16 : kTQ * QRS];
-  if constexpr (!DIRECT) {
-    for (int x = threadIdx.x; x < kTQ * (D / 8); x += 256) {
-      const int pr = x / (D / 8), ch = x % (D / 8);
-      const uint32_t pl = min(static_cast<uint32_t>(pr), np - 1);
-      const uint32_t qrow = pairs[p0 + pl] / m;
-      const int qq = qrow % nq;
-      *reinterpret_cast<uint4*>(qs_lds + pr * QRS + 16 * ch) = *reinterpret_cast<const uint4*>(
-          qidx + b * qsb + static_cast<int64_t>(qq) * qst + 8 * ch);
-    }
+  __shared__ __align__(16) unsigned char qs_lds[kTQ * QRS];
+  for (int x = threadIdx.x; x < kTQ * (D / 8); x += 256) {
+    const int pr = x / (D / 8), ch = x % (D / 8);
+    const uint32_t pl = min(static_cast<uint32_t>(pr), np - 1);
+    const uint32_t qrow = pairs[p0 + pl] / m;
+    const int qq = qrow % nq;
+    *reinterpret_cast<uint4*>(qs_lds + pr * QRS + 16 * ch) = *reinterpret_cast<const uint4*>(
+        qidx + b * qsb + static_cast<int64_t>(qq) * qst + 8 * ch);
   }
 
   bf16x8 a[MT][KS];
@@ -425,21 +405,13 @@ __global__ __launch_bounds__(256) void token_score_kernel(
   for (int nt = 0; nt < 4; ++nt) {
     if (nt * 16 >= static_cast<int>(np)) break;
     const uint32_t pl = min(static_cast<uint32_t>(nt * 16 + r16), np - 1);
-    const uint32_t pid = DIRECT ? p0 : pairs[p0 + pl];
+    const uint32_t pid = pairs[p0 + pl];
     bf16x8 bq[KS];
-    if constexpr (DIRECT) {
-      const uint32_t qrow = pid / m;  // b*nq + q
-      const int qq = qrow % nq;
-      const uint16_t* qr = qidx + b * qsb + static_cast<int64_t>(qq) * qst + 8 * g;
+    if (nt == 0) __syncthreads();  // query rows staged
 #pragma unroll
-      for (int s = 0; s < KS; ++s) bq[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + 32 * s));
-    } else {
-      if (nt == 0) __syncthreads();  // query rows staged
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-        bq[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qs_lds + (nt * 16 + r16) * QRS +
-                                                           64 * s + 16 * g));
-    }
+    for (int s = 0; s < KS; ++s)
+      bq[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qs_lds + (nt * 16 + r16) * QRS + 64 * s +
+                                                         16 * g));
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -450,6 +422,78 @@ __global__ __launch_bounds__(256) void token_score_kernel(
         *reinterpret_cast<f32x4*>(scores + static_cast<int64_t>(pid) * BS + tk) = acc;
       }
     }
+  }
+}
+
+// The direct form on the VALU: one query against one key block, with no
+// other query to share the block's rows (a matrix-core tile would use one
+// of its 16 columns). Wave gw scores tokens 32(gw mod BS/32) .. +31 of pair
+// gw / (BS/32). A key row is read by D/8 adjacent lanes, 16 bytes each, so
+// every load instruction reads whole 128-byte lines (64 / (D/8) rows); each
+// lane takes the dot product of its 8 key elements with the matching 8
+// query elements (fp32 multiply-adds in element order) and the row's lanes
+// are summed with in-row lane moves. All loads are issued before any
+// arithmetic. Integer-valued keys and queries give exact scores in any order.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __uint_as_float(static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(__float_as_uint(x)), CTRL, 0xf, 0xf, false)));
+}
+// Sum over each group of LPR adjacent lanes (8 or 16), in every lane of it.
+template <int LPR>
+__device__ __forceinline__ float row_lanes_sum(float v) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);  // row_half_mirror: lane i <-> 7 - i of each 8
+  if constexpr (LPR == 16) v += dpp_f<0x140>(v);  // row_mirror: lane i <-> 15 - i
+  return v;
+}
+
+template <int D, int BS>
+__global__ __launch_bounds__(256) void token_score_direct_kernel(
+    const uint16_t* __restrict__ qidx, int64_t qsb, int64_t qst, const uint16_t* __restrict__ kidx,
+    int64_t ksb, int64_t kst, int L, int nq, int m, int nblk,
+    const int32_t* __restrict__ block_idx, float* __restrict__ scores, uint32_t npairs) {
+  constexpr int LPR = D / 8;     // lanes per key row
+  constexpr int RPI = 64 / LPR;  // rows per load instruction
+  constexpr int TPW = 32;        // tokens per wave
+  constexpr int WPP = BS / TPW;  // waves per pair
+  constexpr int NI = TPW / RPI;  // load instructions per wave
+  static_assert(BS % TPW == 0 && (LPR == 8 || LPR == 16), "shape");
+  const int wave = threadIdx.x / kWave, l = lane_id();
+  const uint32_t gw = blockIdx.x * 4u + static_cast<uint32_t>(wave);
+  const uint32_t pair = gw / WPP;
+  if (pair >= npairs) return;
+  const int c = block_idx[pair];
+  if (c < 0 || c >= nblk) return;  // empty slot: never a candidate
+  const int b = static_cast<int>(pair / (static_cast<uint32_t>(nq) * m));
+  const int qq = static_cast<int>((pair / m) % nq);
+  const int p = l % LPR, r = l / LPR;
+  const int w0 = static_cast<int>(gw % WPP) * TPW;  // first token of this wave in the block
+  const int tok0 = c * BS + w0;
+  const uint16_t* kb = kidx + b * ksb + 8 * p;
+  uint4 kv[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int j = min(tok0 + i * RPI + r, L - 1);
+    kv[i] = *reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(j) * kst);
+  }
+  const uint4 qv = *reinterpret_cast<const uint4*>(qidx + b * qsb + static_cast<int64_t>(qq) * qst +
+                                                   8 * p);
+  const float qf[8] = {bf16_lo(qv.x), bf16_hi(qv.x), bf16_lo(qv.y), bf16_hi(qv.y),
+                       bf16_lo(qv.z), bf16_hi(qv.z), bf16_lo(qv.w), bf16_hi(qv.w)};
+  float* out = scores + static_cast<int64_t>(pair) * BS + w0;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const uint32_t e[4] = {kv[i].x, kv[i].y, kv[i].z, kv[i].w};
+    float sv = 0.0f;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      sv = __builtin_fmaf(bf16_lo(e[h]), qf[2 * h], sv);
+      sv = __builtin_fmaf(bf16_hi(e[h]), qf[2 * h + 1], sv);
+    }
+    sv = row_lanes_sum<LPR>(sv);
+    if (p == 0) out[i * RPI + r] = sv;
   }
 }
 
@@ -1019,21 +1063,15 @@ hipError_t launch_token_select(const uint16_t* qidx, Str3 qs, const uint16_t* ki
   const uint32_t np32 = static_cast<uint32_t>(npairs);
 #define HISA_TS(D_, B_)                                                                       \
   do {                                                                                        \
-    if (direct && B_ == 64)                                                                   \
-      hipLaunchKernelGGL((token_score_kernel<D_, B_, true, true>),                            \
-                         dim3(static_cast<unsigned>((npairs + 3) / 4)), dim3(256), 0, s, qidx, \
-                         qs.b, qs.t, kidx, ks.b, ks.t, L, nq, m, nblk, w.tiles, w.total,      \
-                         w.tile_off, w.offs, w.cnt, w.pairs, block_idx, w.scores, np32);      \
-    else if (direct)                                                                          \
-      hipLaunchKernelGGL((token_score_kernel<D_, B_, true>), dim3(static_cast<unsigned>(npairs)), \
-                         dim3(256), 0, s, qidx, qs.b, qs.t, kidx, ks.b, ks.t, L, nq, m, nblk, \
-                         w.tiles, w.total, w.tile_off, w.offs, w.cnt, w.pairs, block_idx,     \
+    if (direct)                                                                               \
+      hipLaunchKernelGGL((token_score_direct_kernel<D_, B_>),                                 \
+                         dim3(static_cast<unsigned>((npairs * (B_ / 32) + 3) / 4)), dim3(256), \
+                         0, s, qidx, qs.b, qs.t, kidx, ks.b, ks.t, L, nq, m, nblk, block_idx,  \
                          w.scores, np32);                                                     \
     else                                                                                      \
-      hipLaunchKernelGGL((token_score_kernel<D_, B_, false>),                                 \
-                         dim3(static_cast<unsigned>(max_tiles)), dim3(256), 0, s, qidx, qs.b,  \
-                         qs.t, kidx, ks.b, ks.t, L, nq, m, nblk, w.tiles, w.total, w.tile_off, \
-                         w.offs, w.cnt, w.pairs, block_idx, w.scores, np32);                  \
+      hipLaunchKernelGGL((token_score_kernel<D_, B_>), dim3(static_cast<unsigned>(max_tiles)),  \
+                         dim3(256), 0, s, qidx, qs.b, qs.t, kidx, ks.b, ks.t, L, nq, m, nblk,  \
+                         w.tiles, w.total, w.tile_off, w.offs, w.cnt, w.pairs, w.scores);      \
   } while (0)
   if (d == 64) {
     if (B == 64) HISA_TS(64, 64); else if (B == 128) HISA_TS(64, 128); else HISA_TS(64, 256);
