@@ -16,9 +16,11 @@
 //
 // Per tile: S^T = K Q^T on 16x16x32 bf16 MFMA (K fragments from LDS, the
 // group's Q rows in registers). Its accumulator holds, in lane l, head l%16
-// and tokens 4(l/16)..+3, which is exactly the A operand of a 16x16x16 MFMA,
-// so the numerators P feed O += P V without passing through LDS; V^T
-// fragments come from the row-major V tile through ds_read_tr16_b64.
+// and tokens 4(l/16)..+3, the A operand layout of a 16x16x16 MFMA, so the
+// numerators P feed O += P V without passing through LDS; V^T fragments come
+// from the row-major V tile through ds_read_tr16_b64. The products of two
+// consecutive tiles run together as 16x16x32 MFMAs (each lane's 4 tokens of
+// both tiles as its 8 k values).
 //
 // Softmax reference: R per head is the maximum over the query's first tile's
 // valid tokens (base-2 logits, scale folded in); a later tile whose maximum
@@ -205,6 +207,8 @@ struct State {
   float R;           // reference of head l%16 (base 2)
   float lsum;        // partial row sum of head l%16 over this lane's tokens
   uint32_t m0, m1;   // valid masks of tiles t and t+1
+  v4s pp;             // bf16 numerators of a pair's even tile (this lane's 4 tokens)
+  v4s pv[8];          // its V^T fragments
 };
 
 // The fragments of tile t (slot I = t % 2) this lane needs: K fragments
@@ -265,7 +269,13 @@ __device__ __forceinline__ int4 read_frags_ids(Frags& f, const Item& it, int tid
 }
 
 // Tile t: S^T, the softmax update, O += P V, from fragments already read.
-__device__ __forceinline__ void tile(State& st, const Frags& f, int t, float scale_log2, int l) {
+// The numerators of an even tile wait for the odd tile after it: the pair's
+// P V products then run as 16x16x32 MFMAs over the pair's 32 tokens (lane
+// group g holding tokens 4g..4g+3 of each tile as its 8 k values, in P and
+// in V^T alike), half the instructions of two 16x16x16 rounds.
+template <int I>
+__device__ __forceinline__ void tile(State& st, const Frags& f, int t,
+                                     float scale_log2, int l) {
   const int g = l >> 4;
   // ---- S^T of the tile: lane l gets head l%16, tokens 4g + (0..3); two
   // accumulation chains over the k steps, added at the end
@@ -288,6 +298,12 @@ __device__ __forceinline__ void tile(State& st, const Frags& f, int t, float sca
   // ---- reference: set on the first tile, raised when exceeded by far
   const bool up = t == 0 || tmax > st.R + kRaise;
   if (__ballot(up) != 0ull) {
+    if constexpr (I % 2 == 1) {
+      // the even tile's products first, against the reference they used
+#pragma unroll
+      for (int dvb = 0; dvb < 8; ++dvb) st.o[dvb] = mfma16k16(st.pp, st.pv[dvb], st.o[dvb]);
+      st.pp = v4s{0, 0, 0, 0};
+    }
     const float rnew = up ? tmax : st.R;
     const float a = exp2_ratio(st.R, rnew);
     st.lsum *= t == 0 ? 0.0f : a;
@@ -307,9 +323,21 @@ __device__ __forceinline__ void tile(State& st, const Frags& f, int t, float sca
   st.lsum += (p[0] + p[1]) + (p[2] + p[3]);
   const uint2 pp = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
   const v4s pa = __builtin_bit_cast(v4s, pp);
-  // ---- O += P V
+  if constexpr (I % 2 == 0) {
+    st.pp = pa;
 #pragma unroll
-  for (int dvb = 0; dvb < 8; ++dvb) st.o[dvb] = mfma16k16(pa, f.v[dvb], st.o[dvb]);
+    for (int dvb = 0; dvb < 8; ++dvb) st.pv[dvb] = f.v[dvb];
+  } else {
+    // ---- O += P V over the pair: k values 0..3 from the even tile, 4..7
+    // from this one
+    const bf16x8 p8 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(st.pp, pa, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+    for (int dvb = 0; dvb < 8; ++dvb) {
+      const bf16x8 v8 = __builtin_bit_cast(
+          bf16x8, __builtin_shufflevector(st.pv[dvb], f.v[dvb], 0, 1, 2, 3, 4, 5, 6, 7));
+      st.o[dvb] = mfma16(p8, v8, st.o[dvb]);
+    }
+  }
 }
 
 // Iteration t (slot t % 2): the K and V fragments of tile t and the gather
@@ -319,12 +347,13 @@ __device__ __forceinline__ void tile(State& st, const Frags& f, int t, float sca
 // iteration: at most this iteration's 9 loads (8 gathers, 1 id load) remain,
 // so tile t+1 and the ids of tile t+3 have landed.
 template <int I, bool OFF32>
-__device__ __forceinline__ void iter(State& st, const Item& it, int t, float scale_log2, int l) {
+__device__ __forceinline__ void iter(State& st, const Item& it, int t,
+                                     float scale_log2, int l) {
   Frags f;
   const int4 ids = read_frags_ids<I>(f, it, t + 2, l);
   const uint32_t m2 = gather_ids<OFF32>(it, t + 2, kbuf<I>(it.w), vbuf<I>(it.w), ids, l);
   ids_issue(it, t + 5, l);
-  tile(st, f, t, scale_log2, l);
+  tile<I>(st, f, t, scale_log2, l);
   st.m0 = st.m1;
   st.m1 = m2;
   __builtin_amdgcn_sched_barrier(0);
