@@ -409,8 +409,8 @@ __global__ __launch_bounds__(256) void hils_local_keys_kernel(
 // per workgroup instead of once per wave, 64K 6.07 -> 5.78 ms); longer
 // chunks read K fragments from global per group. S^T = K Q^T on 16x16x32 bf16 MFMA leaves
 // in lane l the entry l%16 and the tokens 4(l/16)..+3 of each 16-token tile:
-// the A operand of the 16x16x16 P V product, with V^T fragments from
-// ds_read_tr16_b64. Online softmax over the chunk's 64-token groups. Each
+// with the next tile's, the A operand of a 16x16x32 P V product over two
+// tiles, with V^T fragments from ds_read_tr16_b64. Online softmax over the chunk's 64-token groups. Each
 // wave's 16 result rows are staged in LDS and written as whole rows.
 struct TileTabs {
   const uint32_t* cnt;
@@ -617,22 +617,33 @@ __global__ __launch_bounds__(256) void hils_pair_chunk_kernel(
       }
       mrun = mnew;
       const float moff = mnew == -INFINITY ? 0.0f : -mnew;
+      // P V for two 16-token tiles at a time: 16x16x32 products whose 8 k
+      // values per lane are its 4 tokens of each tile (in P and V^T alike)
 #pragma unroll
-      for (int tau = 0; tau < 4; ++tau) {
-        v4s_t pa;
+      for (int tp = 0; tp < 2; ++tp) {
+        v4s_t pa[2];
 #pragma unroll
-        for (int ee = 0; ee < 4; ++ee) {
-          const float p = __builtin_amdgcn_exp2f(sv[tau][ee] + moff);
-          lsum += p;
-          pa[ee] = static_cast<short>(f32_to_bf16(p));
+        for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+          for (int ee = 0; ee < 4; ++ee) {
+            const float p = __builtin_amdgcn_exp2f(sv[2 * tp + h2][ee] + moff);
+            lsum += p;
+            pa[h2][ee] = static_cast<short>(f32_to_bf16(p));
+          }
         }
-        const unsigned char* vrow =
-            vt + (64 * gi + 16 * tau + 4 * g + (r >> 2)) * RS + 8 * (r & 3);
+        const bf16x8 p8 =
+            __builtin_bit_cast(bf16x8, __builtin_shufflevector(pa[0], pa[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        const unsigned char* vrow0 =
+            vt + (64 * gi + 32 * tp + 4 * g + (r >> 2)) * RS + 8 * (r & 3);
+        const unsigned char* vrow1 = vrow0 + 16 * RS;
 #pragma unroll
         for (int x = 0; x < NDB; ++x) {
-          const v4s_t vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4s_t*)(vrow + 32 * x));
-          o[x] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vf, o[x], 0, 0, 0);
+          const v4s_t vf0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s_t*)(vrow0 + 32 * x));
+          const v4s_t vf1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s_t*)(vrow1 + 32 * x));
+          o[x] = mfma16(p8, __builtin_bit_cast(bf16x8, __builtin_shufflevector(vf0, vf1, 0, 1, 2, 3, 4, 5, 6, 7)),
+                        o[x]);
         }
       }
     }
