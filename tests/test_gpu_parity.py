@@ -386,6 +386,79 @@ def test_decode_graph_replays_match_eager():
         assert torch.equal(got_out, s.out), rep
 
 
+@pytest.mark.parametrize("shape", ["direct", "bucketed"])
+def test_prefill_step_graph_replays_match_eager(shape):
+    # the prefill step as one HIP graph (the calls the benchmark captures):
+    # each replay, on fresh queries, with eager work and a synchronisation in
+    # between, must equal the eager step on the same queries. "direct" scores
+    # pairs straight from block_idx, "bucketed" buckets them by key block
+    # (its tables cleared by fill kernels inside the graph).
+    if shape == "direct":
+        w = _mk("pgraph_direct", L=2048, B=64, m=8, k=128, d_idx=64, Hq=2, Hkv=1)
+    else:
+        w = _mk("pgraph_bucketed", L=8192, nq=1024, B=128, m=64, k=512, d_idx=64, Hq=2, Hkv=1)
+    log(f"case prefill graph {w}")
+    inp = make_inputs(w, DEV, seed=13)
+    p = HierPipeline(inp["kidx"], inp["qidx"], inp["q_pos"], inp["q"], inp["k"], inp["v"], w.B,
+                     w.m, w.k, w.scale)
+    calls = [
+        p.summarize,
+        lambda: H.hisa_block_score(p.qidx, p.q_pos, p.split, p.B, out=p.block_scores),
+        lambda: H.hisa_select_blocks(p.block_scores, p.q_pos, p.B, p.m, out=p.block_idx),
+        lambda: H.hisa_token_select(p.qidx, p.kidx, p.q_pos, p.block_idx, p.B, p.k_top,
+                                    token_idx=p.token_idx, want_scores=False, workspace=p.ws),
+        p.attend,
+    ]
+    for c in calls:  # warm-up outside the capture
+        c()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    gen = torch.Generator(device=DEV).manual_seed(14)
+    for rep in range(3):
+        p.qidx.copy_(torch.randint(-8, 9, p.qidx.shape, generator=gen, device=DEV)
+                     .to(torch.bfloat16))
+        p.q.copy_(torch.randn(p.q.shape, generator=gen, device=DEV).to(torch.bfloat16))
+        g.replay()
+        torch.cuda.synchronize()
+        got = (p.block_idx.clone(), p.token_idx.clone(), p.out.clone())
+        for c in calls:  # eager, on the same queries
+            c()
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], p.block_idx), rep
+        assert torch.equal(got[1], p.token_idx), rep
+        assert torch.equal(got[2], p.out), rep
+
+
+def test_hils_decode_graph_replays_match_eager():
+    # routing and two-level attention of the two-level decode as one HIP
+    # graph, as the benchmark times it; every replay equals the eager step
+    w = WORKLOADS["hils_decode_1m"].with_(name="hgraph", batch=2, L=9000, m=16, Hq=4, Hkv=4)
+    log(f"case hils decode graph {w}")
+    inp = make_inputs(w, DEV, seed=15)
+    sc = 1.0 / math.sqrt(w.Dk)
+    hd = HilsDecode(inp["q"], inp["k"], inp["v"], inp["w_proj"], w.B, w.m, sc, sc)
+    hd.run(build=True)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        hd.route()
+        hd.attend()
+    gen = torch.Generator(device=DEV).manual_seed(16)
+    for rep in range(3):
+        hd.q.copy_(torch.randn(hd.q.shape, generator=gen, device=DEV).to(torch.bfloat16))
+        g.replay()
+        torch.cuda.synchronize()
+        got_idx, got_out = hd.chunk_idx.clone(), hd.out.clone()
+        hd.route()
+        hd.attend()
+        torch.cuda.synchronize()
+        assert torch.equal(got_idx, hd.chunk_idx), rep
+        assert torch.equal(got_out, hd.out), rep
+
+
 def test_determinism_and_decode_matches_prefill_row():
     w = _mk("det", L=3072, B=128, m=6, k=200, d_idx=128, Hq=16, Hkv=1)
     log(f"case determinism {w}")
