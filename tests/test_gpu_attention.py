@@ -36,6 +36,15 @@ CASES = [
     ("mla_lazy_moves", 3000, 6, 600, 64, 1, 576, 512, True, 24 * 30, 1 / 24, "sorted"),
     ("mla_redo", 3000, 6, 600, 64, 1, 576, 512, True, 24 * 60, 1 / 24, "late_peak"),
     ("mla_empty", 512, 3, 64, 64, 1, 576, 512, True, 1.0, 1 / 24, "empty"),
+    # hundreds of queries, so that every XCD's range holds many and the
+    # rotated sweep starts the queries in flight at different list tiles;
+    # a redo-forcing list, holes, the shortest list of 8 tiles, and empty
+    # lists among full ones
+    ("mla_stream", 5000, 700, 600, 64, 1, 576, 512, True, 1 / 24, 1 / 24, "sorted"),
+    ("mla_stream_redo", 3000, 600, 600, 64, 1, 576, 512, True, 24 * 60, 1 / 24, "late_peak"),
+    ("mla_stream_n8_holes", 2000, 650, 250, 64, 1, 576, 512, True, 1.0, 1 / 24, "holes"),
+    ("mla_stream_some_empty", 1500, 620, 300, 64, 1, 576, 512, True, 1 / 24, 1 / 24,
+     "some_empty"),
     ("mqa_holes", 1000, 8, 100, 16, 1, 128, 128, False, 1.0, 1.0, "holes"),
     ("gqa_dups_oob", 800, 8, 45, 8, 2, 64, 64, False, 1.0, 1.0, "dups_oob"),
 ]
@@ -63,6 +72,8 @@ def _lists(pattern, L, nq, topk, g):
                 # every list ends with the 8 last tokens, whose keys are boosted
                 r = np.concatenate([np.sort(g.choice(L - 8, size=topk - 8, replace=False)),
                                     np.arange(L - 8, L)])
+            elif pattern == "some_empty" and len(rows) % 3 == 1:
+                r[:] = -1
             elif pattern == "holes":
                 r[g.random(topk) < 0.2] = -1
             elif pattern == "dups_oob":

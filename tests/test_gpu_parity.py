@@ -819,7 +819,14 @@ def _hils_prefill_check(w, exact, positions=None, heads=None, bucketed=True, sub
                     bound = 4 * 2.0 ** -24 * w.Dk * 2 * np.abs(khat[order[m - 3:m - 1]] * q).sum()
                     assert gap <= bound, f"b={b} h={h} t={t}: chunk sets differ, gap {gap}"
                     excluded += 1
-                    continue
+                    # the output is still checked: the oracle's two-level
+                    # combine over the chunk set the GPU chose (the local
+                    # chunk keyed by its tokens up to t)
+                    kl = Wp @ K[bt * C: t + 1].mean(axis=0)
+                    gi = got_idx[b, h, r]
+                    logits = [0.0 if c < 0 else
+                              s_chunk * float((kl if c == bt else khat[c]) @ q) for c in gi]
+                    ref_out = O.hils_combine(q, K, V, gi, logits, t, C, s_token)
                 keep.append(r)
                 refs.append(ref_out)
             if keep:
