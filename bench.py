@@ -63,6 +63,10 @@ def parse():
     ap.add_argument("--attn-ids", default="selected", choices=["selected", "hot"],
                     help="--attn-only: the selected ids, or every query reading the same "
                          "rows 0..k-1 (all served from L2: the kernel's own ceiling)")
+    ap.add_argument("--attn-kept", default="",
+                    help="--attn-only: comma-separated kept-token counts k' (each <= k); time "
+                         "the attention over the first k' ids of every list (or rows 0..k'-1 "
+                         "with --attn-ids hot) and fit time = fixed + per-token * k'")
     ap.add_argument("--gather-probe", action="store_true",
                     help="prefill: time the gather-rate probe (the attention's row gathers "
                          "alone) on the selected ids, on the same lists shifted to one hot "
@@ -465,6 +469,39 @@ def bench_attn_only(w, a, inp):
     return {"attn_only": w.name, "ids": a.attn_ids, "ms": ms, "tflops": tf,
             "frac_mfma": tf / PEAK_BF16_TFLOPS,
             "kept_tokens": n_sel, "steps": a.steps, "warmup": a.warmup}
+
+
+def bench_attn_kept(w, a, inp):
+    """The attention launch over all queries on the first k' ids of each
+    selected list (contiguous copies), for several k': the least-squares line
+    time = fixed + per_token * k' separates the cost that scales with the
+    kept tokens from the part that does not (the Q rows read and the output
+    rows written once per query)."""
+    import numpy as np
+    import torch
+    import long_context_indexer_block_amd as H
+    from long_context_indexer_block_amd.pipeline import HierPipeline
+    p = HierPipeline(inp["kidx"], inp["qidx"], inp["q_pos"], inp["q"], inp["k"], inp["v"], w.B,
+                     w.m, w.k, w.scale)
+    p.index()
+    nq = p.token_idx.shape[1]
+    ks = sorted(int(x) for x in a.attn_kept.split(","))
+    if ks[0] < 1 or ks[-1] > w.k:
+        raise SystemExit(f"--attn-kept values must lie in 1..{w.k}")
+    ms = []
+    for kk in ks:
+        if a.attn_ids == "hot":
+            ids = torch.arange(kk, dtype=torch.int32, device="cuda").expand(1, nq, kk).contiguous()
+        else:
+            ids = p.token_idx[:, :, :kk].contiguous()
+        ms.append(time_launch(lambda: H.sparse_attn_fwd(p.q, p.k, p.v, ids, w.scale, out=p.out,
+                                                        workspace=p.attn_ws), a.steps, a.warmup))
+        log(f"k'={kk}: {ms[-1]:.3f} ms")
+    slope, fixed = np.polyfit(np.array(ks, dtype=np.float64), np.array(ms), 1)
+    return {"attn_kept": w.name, "ids": a.attn_ids, "queries": nq, "kept": ks, "ms": ms,
+            "fixed_ms": fixed, "ms_per_1024_tokens": slope * 1024,
+            "fixed_us_per_query_per_cu": fixed * 1e3 / (nq / 256),
+            "steps": a.steps, "warmup": a.warmup}
 
 
 def bench_gather_probe(w, a, inp):
@@ -1025,7 +1062,8 @@ def main():
         bench_sweep(w, a, inp)
         return
     if a.attn_only:
-        print(json.dumps(bench_attn_only(w, a, inp)), flush=True)
+        res = bench_attn_kept(w, a, inp) if a.attn_kept else bench_attn_only(w, a, inp)
+        print(json.dumps(res), flush=True)
         return
     if a.gather_probe:
         print(json.dumps(bench_gather_probe(w, a, inp)), flush=True)
