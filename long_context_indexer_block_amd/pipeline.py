@@ -25,7 +25,8 @@ from . import (flat_indexer_topk, flat_indexer_topk_workspace_bytes, hils_two_le
 class HierPipeline:
     """The hierarchical step a1-a5. overlap_slabs > 1 (one sequence only) sets
     up run_overlapped(): the block scores, block and token selection of query
-    slab i+1 on one stream while slab i attends on another."""
+    slab i+1 on one stream while slab i attends on another (two attention
+    streams, taking the slabs in turn)."""
 
     def __init__(self, kidx, qidx, q_pos, q, k, v, B, m, k_top, scale, want_scores=False,
                  want_lse=False, overlap_slabs=0):
@@ -57,7 +58,14 @@ class HierPipeline:
             nbytes = hisa_token_select_workspace_bytes(1, sl, L, B, m, k_top)
             self.slab_ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
             self.slab_attn_ws = sparse_attn_workspace(q[:, :sl], k, v, self.token_idx[:, :sl])
-            self.streams = (torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev))
+            # one stream selects, two alternate the slabs' attention (so that
+            # the next slab fills the compute units the last workgroups of a
+            # slab leave idle: 64K 19.30-19.38 -> 19.04-19.19 ms and 19.57 ->
+            # 19.48 ms on two hosts; a third attention stream gained nothing),
+            # each with its own attention workspace
+            self.streams = tuple(torch.cuda.Stream(device=dev) for _ in range(3))
+            self.slab_attn_wss = [self.slab_attn_ws, sparse_attn_workspace(
+                q[:, :sl], k, v, self.token_idx[:, :sl])]
 
     def summarize(self):
         hisa_block_summary(self.kidx, self.B, summary=self.summary, split=self.split)
@@ -82,14 +90,15 @@ class HierPipeline:
 
     def run_overlapped(self, summarize=True):
         """The same step, the query slabs' block scores, block and token
-        selection (stream A) ahead of their attention (stream B); same results
-        as run()."""
+        selection (one stream) ahead of their attention (two streams taking
+        the slabs in turn); same results as run()."""
         if not self.slabs:
             return self.run(summarize)
-        sa, sb = self.streams
+        sa = self.streams[0]
+        attn = list(zip(self.streams[1:], self.slab_attn_wss))
         cur = torch.cuda.current_stream()
-        sa.wait_stream(cur)
-        sb.wait_stream(cur)
+        for st in self.streams:
+            st.wait_stream(cur)
         ts, lse = self.token_scores, self.lse
         with torch.cuda.stream(sa):
             if summarize:
@@ -104,15 +113,16 @@ class HierPipeline:
                                   token_scores=None if ts is None else ts[:, s0:s1],
                                   want_scores=ts is not None, workspace=self.slab_ws)
                 done.record(sa)
-        with torch.cuda.stream(sb):
-            for (s0, s1), done in zip(self.slabs, self.slab_done):
-                sb.wait_event(done)
+        for i, ((s0, s1), done) in enumerate(zip(self.slabs, self.slab_done)):
+            st, ws = attn[i % len(attn)]
+            with torch.cuda.stream(st):
+                st.wait_event(done)
                 sparse_attn_fwd(self.q[:, s0:s1], self.k, self.v, self.token_idx[:, s0:s1],
                                 self.scale, out=self.out[:, s0:s1],
                                 lse=None if lse is None else lse[:, s0:s1],
-                                want_lse=lse is not None, workspace=self.slab_attn_ws)
-        cur.wait_stream(sa)
-        cur.wait_stream(sb)
+                                want_lse=lse is not None, workspace=ws)
+        for st in self.streams:
+            cur.wait_stream(st)
         return self.out
 
 
