@@ -22,6 +22,22 @@ from . import (flat_indexer_topk, flat_indexer_topk_workspace_bytes, hils_two_le
                sparse_attn_workspace)
 
 
+def _attend_slabs(pipe, streams, workspaces):
+    """The query slabs' attention, each slab after its selection's event, the
+    slabs taken in turn by the attention streams (each with its own
+    workspace), so that the next slab fills the compute units the last
+    workgroups of a slab leave idle."""
+    lse = pipe.lse
+    for i, ((s0, s1), done) in enumerate(zip(pipe.slabs, pipe.slab_done)):
+        st, ws = streams[i % len(streams)], workspaces[i % len(streams)]
+        with torch.cuda.stream(st):
+            st.wait_event(done)
+            sparse_attn_fwd(pipe.q[:, s0:s1], pipe.k, pipe.v, pipe.token_idx[:, s0:s1],
+                            pipe.scale, out=pipe.out[:, s0:s1],
+                            lse=None if lse is None else lse[:, s0:s1],
+                            want_lse=lse is not None, workspace=ws)
+
+
 class HierPipeline:
     """The hierarchical step a1-a5. overlap_slabs > 1 (one sequence only) sets
     up run_overlapped(): the block scores, block and token selection of query
@@ -95,11 +111,10 @@ class HierPipeline:
         if not self.slabs:
             return self.run(summarize)
         sa = self.streams[0]
-        attn = list(zip(self.streams[1:], self.slab_attn_wss))
         cur = torch.cuda.current_stream()
         for st in self.streams:
             st.wait_stream(cur)
-        ts, lse = self.token_scores, self.lse
+        ts = self.token_scores
         with torch.cuda.stream(sa):
             if summarize:
                 self.summarize()
@@ -113,14 +128,7 @@ class HierPipeline:
                                   token_scores=None if ts is None else ts[:, s0:s1],
                                   want_scores=ts is not None, workspace=self.slab_ws)
                 done.record(sa)
-        for i, ((s0, s1), done) in enumerate(zip(self.slabs, self.slab_done)):
-            st, ws = attn[i % len(attn)]
-            with torch.cuda.stream(st):
-                st.wait_event(done)
-                sparse_attn_fwd(self.q[:, s0:s1], self.k, self.v, self.token_idx[:, s0:s1],
-                                self.scale, out=self.out[:, s0:s1],
-                                lse=None if lse is None else lse[:, s0:s1],
-                                want_lse=lse is not None, workspace=ws)
+        _attend_slabs(self, self.streams[1:], self.slab_attn_wss)
         for st in self.streams:
             cur.wait_stream(st)
         return self.out
@@ -155,8 +163,11 @@ class FlatPipeline:
             self.slab_done = [torch.cuda.Event() for _ in self.slabs]
             nbytes = flat_indexer_topk_workspace_bytes(1, sl, L, k_top)
             self.slab_ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
-            self.slab_attn_ws = sparse_attn_workspace(q[:, :sl], k, v, self.token_idx[:, :sl])
-            self.streams = (torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev))
+            # one stream selects, two take the slabs' attention in turn, as in
+            # the hierarchical step
+            self.slab_attn_wss = [sparse_attn_workspace(q[:, :sl], k, v, self.token_idx[:, :sl])
+                                  for _ in range(2)]
+            self.streams = tuple(torch.cuda.Stream(device=dev) for _ in range(3))
 
     def index(self):
         flat_indexer_topk(self.qidx, self.kidx, self.q_pos, self.k_top, token_idx=self.token_idx,
@@ -173,15 +184,16 @@ class FlatPipeline:
         return self.out
 
     def run_overlapped(self):
-        """The flat selection of query slab i+1 (stream A) while slab i
-        attends (stream B); same results as run()."""
+        """The flat selection of query slab i+1 (one stream) while slab i
+        attends (two streams taking the slabs in turn); same results as
+        run()."""
         if not self.slabs:
             return self.run()
-        sa, sb = self.streams
+        sa = self.streams[0]
         cur = torch.cuda.current_stream()
-        sa.wait_stream(cur)
-        sb.wait_stream(cur)
-        ts, lse = self.token_scores, self.lse
+        for st in self.streams:
+            st.wait_stream(cur)
+        ts = self.token_scores
         with torch.cuda.stream(sa):
             for (s0, s1), pos, done in zip(self.slabs, self.slab_pos, self.slab_done):
                 flat_indexer_topk(self.qidx[:, s0:s1], self.kidx, pos, self.k_top,
@@ -189,15 +201,9 @@ class FlatPipeline:
                                   token_scores=None if ts is None else ts[:, s0:s1],
                                   want_scores=ts is not None, workspace=self.slab_ws)
                 done.record(sa)
-        with torch.cuda.stream(sb):
-            for (s0, s1), done in zip(self.slabs, self.slab_done):
-                sb.wait_event(done)
-                sparse_attn_fwd(self.q[:, s0:s1], self.k, self.v, self.token_idx[:, s0:s1],
-                                self.scale, out=self.out[:, s0:s1],
-                                lse=None if lse is None else lse[:, s0:s1],
-                                want_lse=lse is not None, workspace=self.slab_attn_ws)
-        cur.wait_stream(sa)
-        cur.wait_stream(sb)
+        _attend_slabs(self, self.streams[1:], self.slab_attn_wss)
+        for st in self.streams:
+            cur.wait_stream(st)
         return self.out
 
 
