@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--overlap-slabs", type=int, default=-1,
                     help="prefill: query slabs whose token selection overlaps the attention of "
                          "the slab before (0: stages one after another; default: 16 from 32768 "
-                         "queries on)")
+                         "queries on, 4 from 8192)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--bw-probe", type=int, default=0,
                     help="time a plain fill of this many bytes and a copy of half of them "
@@ -338,7 +338,8 @@ def bench_prefill(w, a, inp):
 
     nq = w.batch * w.queries
     # query slabs whose token selection overlaps the attention of the slab before
-    slabs = a.overlap_slabs if a.overlap_slabs >= 0 else (16 if nq >= 32768 else 0)
+    slabs = a.overlap_slabs if a.overlap_slabs >= 0 else (
+        16 if nq >= 32768 else 4 if nq >= 8192 else 0)
     p = HierPipeline(inp["kidx"], inp["qidx"], inp["q_pos"], inp["q"], inp["k"], inp["v"], w.B,
                      w.m, w.k, w.scale, overlap_slabs=slabs)
     stages = ["summary", "block_score", "select_blocks", "token_select", "attention"]

@@ -493,6 +493,18 @@ def test_workload_prefill_16k_mqa():
     p = _run_hier(w, inp)
     rows = _rows(w, 40)
     _check_hier(w, inp, p, rows, what=w.name)
+    # the step as the benchmark times it at this size: 4 query slabs, the
+    # selection on one stream, the slabs' attention alternating on two; the
+    # same block and token ids, and the same output bits (this attention's
+    # summation order does not depend on the schedule)
+    o = HierPipeline(inp["kidx"], inp["qidx"], inp["q_pos"], inp["q"], inp["k"], inp["v"], w.B,
+                     w.m, w.k, w.scale, overlap_slabs=4)
+    assert len(o.slabs) == 4
+    o.run_overlapped()
+    o.run_overlapped()
+    torch.cuda.synchronize()
+    assert torch.equal(o.block_idx, p.block_idx) and torch.equal(o.token_idx, p.token_idx)
+    assert torch.equal(o.out, p.out)
 
 
 def _rows_64k(w, slabs, n_total=4096, seed=0):
